@@ -1,0 +1,366 @@
+"""Benchmark of the fused W4A16 decode GEMV (and the prefill GEMM) on one MI355X.
+
+A step is one decode layer's weight matmuls of Llama-3-8B at M=1: the four
+projections qkv [6144,4096], o [4096,4096], gate_up [28672,4096] and down
+[4096,14336], INT4 asymmetric, group 128, fp16 scale + zero, bf16 activations.
+Each step reads a different copy of the packed weights (copies rotate over at
+least 1 GiB, four times the 256 MB Infinity Cache), so the weights stream
+from HBM as they do in a real decode over 32 layers.
+
+value = algorithmic bytes of a step / step time (GB/s), where the algorithmic
+bytes per [N, K] projection are N*K/2 + 4*N*K/G + 2*K + 2*N (packed codes,
+fp16 scale and zero per group, bf16 x in, bf16 y out).  Before timing, every
+projection's output is checked against the CPU oracle on sampled rows.
+
+Also reported: the prefill GEMM (M=2048, same shapes) in TFLOP/s against the
+dense bf16 MFMA peak, the small-batch and super-block GEMVs, a bf16 GEMV
+comparator (torch linear, hipBLASLt) for the effective-bytes speedup, and the
+CPU oracle timed on a bounded sample on this host.
+
+Prints ONE JSON line.  python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "W4A16 dequant-GEMV HBM GB/s & % peak (M=1); MFMA TFLOP/s at M=2048"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gemv_bytes(n, k, g, m=1, sym=False):
+    meta = 2 if sym else 4
+    return n * k // 2 + n * (k // g) * meta + 2 * m * k + 2 * m * n
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--skip-extras", action="store_true",
+                    help="only the decode step (used for profiling)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the kernels shard by output rows with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from oracle import gq_oracle as O
+    from w4a16_dequant_gemm_group_amd import binding as B
+    from w4a16_dequant_gemm_group_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def bits16(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    G = 128
+    shapes = [(name,) + synth.LLAMA3_8B_SHAPES[name] for name in synth.SHAPE_ORDER]
+
+    # ---------------- inputs, quantized on the GPU, parity-gated -----------------
+    W, X = {}, {}
+    host = {}
+    for name, n, k in shapes:
+        w, x = synth.decode_case(name)
+        host[name] = (w, x)
+        codes, s, z = B.gq_quantize_groups(to_dev(w), 4, G, False)
+        W[name] = (B.gq_pack_int4(codes), s, z)
+        X[name] = to_dev(x)
+        del codes
+    torch.cuda.synchronize()
+    log("inputs ready; parity gate")
+    for name, n, k in shapes:
+        w, x = host[name]
+        qw, s, z = W[name]
+        y = B.gq_w4a16_gemv(X[name], qw, s, z, G, False)
+        rows = np.sort(np.random.default_rng(0).choice(n, 64, replace=False))
+        c_ref, s_ref, z_ref = O.quantize_to_storage(w[rows], 4, G, False)
+        qref = O.pack_int4(c_ref, False)
+        if not np.array_equal(qw.cpu().numpy()[rows], qref):
+            raise SystemExit(f"parity gate: packed weights of {name} differ from the oracle")
+        ref = O.w4a16_reference(x, qref, s_ref, z_ref, G, False)
+        yv = O.bf16_to_f64(bits16(y))[:, rows]
+        rel = O.rel_frobenius(yv, ref)
+        if rel > 2e-3:
+            raise SystemExit(f"parity gate: {name} relF {rel:.2e}")
+    log("parity gate passed")
+
+    # ---------------- rotation copies ------------------------------------------------
+    step_weight_bytes = sum(W[nm][0].numel() + 2 * W[nm][1].numel() + 2 * W[nm][2].numel()
+                            for nm, _, _ in shapes)
+    R = max(2, int(np.ceil(args.rotate_gib * 2 ** 30 / step_weight_bytes)))
+    copies = [W] + [{nm: tuple(t.clone() for t in W[nm]) for nm, _, _ in shapes} for _ in range(R - 1)]
+    Y = {nm: torch.empty((1, n), dtype=torch.bfloat16, device=dev) for nm, n, _ in shapes}
+    torch.cuda.synchronize()
+    log(f"{R} rotating weight copies of {step_weight_bytes / 1e6:.1f} MB")
+
+    step_bytes = sum(gemv_bytes(n, k, G) for _, n, k in shapes)
+
+    def run_step(i):
+        # launches go to the current stream (the capture stream inside a graph)
+        c = copies[i % R]
+        for nm, n, k in shapes:
+            qw, s, z = c[nm]
+            B.gq_w4a16_gemv(X[nm], qw, s, z, G, False, y=Y[nm])
+
+    for i in range(args.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+    # The timed region replays a HIP graph holding exactly `steps` steps (4 launches
+    # each, rotating weight copies), so host launch overhead does not leak into the
+    # measurement.  The graph holds only this library's kernels.
+    g = capture(torch, stream, lambda: [run_step(i) for i in range(args.steps)])
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"decode step {ms_per_step * 1e3:.2f} us, {value:.0f} GB/s")
+    # the graph's outputs match eager launches of the same step
+    yg = {nm: Y[nm].clone() for nm, _, _ in shapes}
+    run_step(args.steps - 1)
+    torch.cuda.synchronize()
+    for nm, _, _ in shapes:
+        if not torch.equal(yg[nm], Y[nm]):
+            raise SystemExit(f"graph replay of {nm} differs from the eager launch")
+    del g
+
+    # per-launch durations: one graph per projection, `nrep` launches over the copies
+    nrep = max(20, min(args.steps, 200))
+    per_us = {}
+    for nm, n, k in shapes:
+        def one(i, nm=nm):
+            qw, s, z = copies[i % R][nm]
+            B.gq_w4a16_gemv(X[nm], qw, s, z, G, False, y=Y[nm], stream=torch.cuda.current_stream())
+        per_us[nm] = graph_time(torch, stream, one, nrep)
+    per_gbps = {nm: gemv_bytes(n, k, G) / (per_us[nm] * 1e-6) / 1e9 for nm, n, k in shapes}
+    # dominant kernel: the K=4096 instantiation (qkv, o, gate_up launches)
+    k4096 = [(nm, n, k) for nm, n, k in shapes if k == 4096]
+    dom_bytes = float(np.mean([gemv_bytes(n, k, G) for _, n, k in k4096]))
+    dom_us = float(np.mean([per_us[nm] for nm, _, _ in k4096]))
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                "kernel": "w4a16_gemv_kernel<1,2,2,false> (K=4096: qkv, o, gate_up)",
+                "bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 3)}
+    log(f"per-shape us {per_us}")
+
+    extras = {}
+    if not args.skip_extras:
+        extras = run_extras(args, torch, B, O, synth, to_dev, bits16, dev, stream, shapes, W, X, G)
+
+    cpu = cpu_baseline(args, O, synth, host, shapes, G)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights with 0.1% input channels x20, N(0,1) bf16 activations)",
+        "config": {"workload": "Llama-3-8B decode layer GEMVs, M=1, INT4 asym g128 fp16 scale+zero: "
+                               "qkv[6144,4096] o[4096,4096] gate_up[28672,4096] down[4096,14336]",
+                   "M": 1, "group_size": G, "rotating_copies": R,
+                   "step_algorithmic_bytes": step_bytes,
+                   "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+                   "per_shape_us": {k: round(v, 3) for k, v in per_us.items()},
+                   "per_shape_GBps": {k: round(v, 1) for k, v in per_gbps.items()}},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    out.update(extras)
+    print(json.dumps(out), flush=True)
+
+
+def capture(torch, stream, body):
+    """Capture body() (launches on the current stream) into a HIP graph."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            body()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    return g
+
+
+def graph_time(torch, stream, fn, reps):
+    """Average microseconds per fn(i) launch, from one replay of a graph of
+    `reps` launches (after one untimed replay)."""
+    g = capture(torch, stream, lambda: [fn(i) for i in range(reps)])
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return t0.elapsed_time(t1) / reps * 1e3
+
+
+def time_launches(torch, stream, fn, reps):
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(reps):
+        fn(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / reps * 1e3  # us
+
+
+def run_extras(args, torch, B, O, synth, to_dev, bits16, dev, stream, shapes, W, X, G):
+    ex = {}
+    # ---- prefill GEMM, M = 2048 -------------------------------------------------
+    gemm = {}
+    tot_flop, tot_us = 0.0, 0.0
+    for name, n, k in shapes:
+        _, xb = synth.prefill_case(name)
+        xd = to_dev(xb)
+        qw, s, z = W[name]
+        y = torch.empty((2048, n), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            B.gq_w4a16_gemm(xd, qw, s, z, G, False, y=y, stream=stream)
+        us = time_launches(torch, stream, lambda i: B.gq_w4a16_gemm(xd, qw, s, z, G, False, y=y, stream=stream), 10)
+        fl = 2.0 * 2048 * n * k
+        gemm[name] = {"us": round(us, 2), "TFLOP/s": round(fl / (us * 1e-6) / 1e12, 1)}
+        tot_flop += fl
+        tot_us += us
+        del xd, y
+    agg = tot_flop / (tot_us * 1e-6) / 1e12
+    ex["gemm_m2048"] = {"per_shape": gemm, "aggregate_TFLOPs": round(agg, 1),
+                        "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS, "frac": round(agg / MFMA_BF16_PEAK_TFLOPS, 4)}
+    log(f"gemm M=2048: {agg:.0f} TFLOP/s")
+
+    # ---- bf16 GEMV comparator (hipBLASLt through torch), rotating copies ------------
+    import torch.nn.functional as F
+    wb = {}
+    for name, n, k in shapes:
+        wb[name] = torch.randn((n, k), dtype=torch.bfloat16, device=dev) * 0.02
+    bf16_bytes = sum(2 * n * k + 2 * k + 2 * n for _, n, k in shapes)
+    Rb = max(2, int(np.ceil(2 ** 30 / bf16_bytes)))
+    wcopies = [wb] + [{nm: t.clone() for nm, t in wb.items()} for _ in range(Rb - 1)]
+
+    def bf16_step(i):
+        c = wcopies[i % Rb]
+        for nm, _, _ in shapes:
+            F.linear(X[nm], c[nm])
+    for i in range(10):
+        bf16_step(i)
+    us_bf16 = time_launches(torch, stream, bf16_step, 50)
+    del wcopies, wb
+    torch.cuda.empty_cache()
+    step_bytes = sum(gemv_bytes(n, k, G) for _, n, k in shapes)
+    ex["bf16_gemv_comparator"] = {"us_per_step": round(us_bf16, 2),
+                                  "GB/s": round(bf16_bytes / (us_bf16 * 1e-6) / 1e9, 1),
+                                  "byte_ratio": round(bf16_bytes / step_bytes, 3)}
+    log(f"bf16 GEMV step {us_bf16:.1f} us")
+
+    # ---- small batch M in {4,8,16}, symmetric g32, rotating weight copies ------------
+    sym_w = {}
+    for name, n, k in shapes:
+        w, _ = synth.decode_case(name)
+        codes, s, _ = B.gq_quantize_groups(to_dev(w), 4, 32, True)
+        sym_w[name] = (B.gq_pack_int4(codes, True), s)
+        del codes
+    sym_bytes = sum(sym_w[nm][0].numel() + 2 * sym_w[nm][1].numel() for nm, _, _ in shapes)
+    Rs = max(2, int(np.ceil(2 ** 30 / sym_bytes)))
+    sym_copies = [sym_w] + [{nm: tuple(t.clone() for t in sym_w[nm]) for nm, _, _ in shapes}
+                            for _ in range(Rs - 1)]
+    sb = {}
+    for m in (1, 4, 8, 16):
+        xs = {nm: to_dev(synth.activations(m, k, seed=2000 + synth.SHAPE_ORDER.index(nm))[0])
+              for nm, _, k in shapes}
+        ys = {nm: torch.empty((m, n), dtype=torch.bfloat16, device=dev) for nm, n, _ in shapes}
+
+        def sb_step(i):
+            c = sym_copies[i % Rs]
+            for nm, _, _ in shapes:
+                B.gq_w4a16_gemv(xs[nm], c[nm][0], c[nm][1], None, 32, True, y=ys[nm])
+        sb_step(0)
+        us = graph_time(torch, stream, sb_step, 4 * Rs)
+        tot_b = sum(gemv_bytes(n, k, 32, m, True) for _, n, k in shapes)
+        sb[f"M={m}"] = {"us_per_step": round(us, 2), "GB/s": round(tot_b / (us * 1e-6) / 1e9, 1),
+                        "TFLOP/s": round(2.0 * m * sum(n * k for _, n, k in shapes) / (us * 1e-6) / 1e12, 2)}
+    del sym_copies, sym_w
+    ex["small_batch_sym_g32"] = sb
+    log(f"small batch {sb}")
+
+    # ---- super-block format GEMV, rotating copies -------------------------------------
+    q4 = {}
+    for name in ("down", "gate_up"):
+        n, k = synth.LLAMA3_8B_SHAPES[name]
+        w, x = synth.q4k_case(name)
+        blocks = B.gq_q4k_quantize(to_dev(w))
+        reps = max(2, int(np.ceil(2 ** 30 / blocks.numel())))
+        bl = [blocks] + [blocks.clone() for _ in range(reps - 1)]
+        xd = to_dev(x)
+        y = torch.empty((1, n), dtype=torch.bfloat16, device=dev)
+        B.gq_q4k_gemv(xd, bl[0], y=y)
+        us = graph_time(torch, stream, lambda i: B.gq_q4k_gemv(xd, bl[i % reps], y=y), 4 * reps)
+        byt = 144 * n * k // 256 + 2 * k + 2 * n
+        q4[name] = {"us": round(us, 3), "GB/s": round(byt / (us * 1e-6) / 1e9, 1)}
+        del bl, blocks
+    ex["q4k_gemv_m1"] = q4
+    return ex
+
+
+def cpu_baseline(args, O, synth, host, shapes, G):
+    """The oracle's W4A16 product (dequantize + float64 group-by-group matmul) on a
+    bounded sample of the decode workload: the first rows of each projection."""
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    rows = 256
+    done_bytes, t_total, passes = 0, 0.0, 0
+    while t_total < args.cpu_seconds and passes < 50:
+        for name, n, k in shapes:
+            w, x = host[name]
+            t = time.perf_counter()
+            codes, s, z = O.quantize_to_storage(w[:rows], 4, G, False)
+            qw = O.pack_int4(codes, False)
+            tq = time.perf_counter()
+            O.w4a16_reference(x, qw, s, z, G, False)
+            t_total += time.perf_counter() - tq
+            done_bytes += gemv_bytes(rows, k, G)
+        passes += 1
+    gbps = done_bytes / t_total / 1e9
+    return {"value": round(gbps, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {rows} rows of each of the 4 decode projections, {passes} passes, "
+                      f"{t_total:.1f} s of matmul (dequantize + float64 group-by-group product); "
+                      f"host has {os.cpu_count()} logical CPUs"}
+
+
+if __name__ == "__main__":
+    main()

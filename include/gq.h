@@ -1,0 +1,173 @@
+/*
+ * gq.h - C ABI of libgq: group-wise low-bit weight quantization and the fused
+ * W4A16 matmul for AMD MI355X (gfx950).
+ *
+ * The operations follow these pages (cited by title and section):
+ *   [P1] "vLLM 量化与推测解码：怎样减少容量、带宽与串行轮次", section 1
+ *        "从实数到有限编码" (affine map q = clamp(round(x/s)+z, qmin, qmax),
+ *        x^ = s(q-z); min-max scale and zero; per-group quantization whose
+ *        inputs are a float tensor, bits and a group size and whose outputs are
+ *        codes plus a (scale, zero) per group) and section 2 (Y = X W^T; weight
+ *        bytes = N b/8 + metadata; the fused W4A16 kernel that reads packed
+ *        INT4 and group scales, dequantizes on chip, multiplies bf16/fp16
+ *        activations with a wider accumulator and never stores the expanded
+ *        weight; checkpoints carry packed qweight + scales + zeros + group_size).
+ *   [P2] "量化" chapter S08, sections "核心思路" (symmetric group quantizer with
+ *        an fp16 scale), "工作原理" (figure: group scales, the 256-weight
+ *        super-block with 6-bit sub-block scales/mins, fused dequantization)
+ *        and "亲手实现" (group-by-group fused matmul).
+ *   [P3] "量化：为何加速推理与精度权衡", sections "直接答案" (affine map and the
+ *        bound |x - x^| <= scale/2) and "深入原理" (exact zero).
+ *
+ * Conventions for every entry point
+ *   - Pointers are device pointers (HIP global memory) unless marked "host".
+ *     The caller owns every buffer; libgq allocates no memory and keeps no
+ *     state beyond a per-device architecture check.
+ *   - All matrices are dense, row-major, contiguous.  W is [N, K] = out x in,
+ *     so Y = X W^T [P1 sec.2]; groups run along K (the reduction axis).
+ *   - fp16 / bf16 values are passed as uint16_t bit patterns.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Arguments are
+ *     validated on the host before anything is enqueued; on a validation error
+ *     nothing is launched and no output is written.  On success the work is
+ *     enqueued asynchronously and the call returns GQ_OK; kernel faults surface
+ *     on the stream as usual.  A failed launch returns GQ_ERR_HIP and leaves the
+ *     outputs undefined.
+ *   - Calls are thread-safe; calls on one stream run in order.
+ *   - Only gfx950 devices are accepted (GQ_ERR_UNSUPPORTED otherwise).
+ *
+ * Storage contract (the readings of the pages used throughout)
+ *   - round() is round-half-to-even.
+ *   - asymmetric b-bit: codes 0..2^b-1; per group lo = min(min(g), 0),
+ *     hi = max(max(g), 0); s = (hi - lo)/(2^b - 1), or 1.0 when hi == lo.
+ *   - symmetric b-bit: codes -2^(b-1)..2^(b-1)-1; s = max|g| / (2^(b-1)-1),
+ *     or 1.0 when the group is all zero.
+ *   - The scale is rounded to fp16 first (nearest-even, saturated to
+ *     [2^-24, 65504]); zero point z = clamp(round(-lo/S)) and codes
+ *     q = clamp(round(x/S) + z) are computed from that stored S, in binary64.
+ *   - zeros are the integer zero points stored as fp16 (exact).
+ *   - Packed INT4: qweight[N][K/2]; byte j of a row holds k=2j in bits 0-3
+ *     and k=2j+1 in bits 4-7.  Symmetric codes are stored as q+8.
+ *   - x^ = S (q - z); symmetric: x^ = S (nibble - 8).
+ */
+#ifndef GQ_H_
+#define GQ_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GQ_OK = 0,
+  GQ_ERR_INVALID_ARG = 1, /* shape/pointer/parameter violates the contract   */
+  GQ_ERR_UNSUPPORTED = 2, /* valid request this build does not implement, or
+                             a device that is not gfx950                      */
+  GQ_ERR_MISALIGNED = 3,  /* a pointer that must be 16-byte aligned is not   */
+  GQ_ERR_HIP = 4          /* the HIP runtime reported an error               */
+} gq_status;
+
+typedef enum { GQ_F32 = 0, GQ_F16 = 1, GQ_BF16 = 2 } gq_dtype;
+
+/* Quantization parameters [P1 sec.1: bits and group size; symmetric or
+ * asymmetric (zero point)].  group_size must divide K; GPU kernels need
+ * group_size % 32 == 0. */
+typedef struct {
+  int32_t bits;       /* 2..8 for quantize; 4 for everything packed */
+  int32_t group_size; /* elements per group along K                 */
+  int32_t symmetric;  /* 0: asymmetric (scale + zero), 1: symmetric */
+} gq_qparams;
+
+/* Human-readable name of a status code (static string). */
+const char* gq_status_str(gq_status s);
+
+/* Library ABI version (major*10000 + minor*100 + patch). */
+int32_t gq_version(void);
+
+/* Byte sizes of the stored form of an [N, K] weight [P1 sec.2: payload
+ * N*K*bits/8 plus a 2-byte scale and (asymmetric) a 2-byte zero per group].
+ * Host only; any output pointer may be NULL.  Errors: INVALID_ARG for
+ * N, K < 1, bits outside 2..8, or group_size < 1 or not dividing K. */
+gq_status gq_packed_sizes(int64_t N, int64_t K, gq_qparams p, int64_t* qweight_bytes,
+                          int64_t* scale_bytes, int64_t* zero_bytes);
+
+/* Group-wise affine quantization [P1 sec.1 equations and per-group listing;
+ * P2 "核心思路" symmetric quantizer; P3 "直接答案"].
+ *   w      [N, K] of w_dtype (GQ_BF16, GQ_F16 or GQ_F32), finite values
+ *   codes  [N, K] bytes: uint8 0..2^b-1 (asymmetric) or int8 (symmetric)
+ *   scales [N, K/group_size] fp16
+ *   zeros  [N, K/group_size] fp16, or NULL exactly when p.symmetric
+ * Bit-exact with the storage contract above.  Errors: INVALID_ARG (shape,
+ * bits outside 2..8, group_size % 32 != 0 or not dividing K, zeros NULL-ness
+ * not matching symmetric, NULL buffers), UNSUPPORTED (device). */
+gq_status gq_quantize_groups(const void* w, gq_dtype w_dtype, int64_t N, int64_t K, gq_qparams p,
+                             void* codes, uint16_t* scales, uint16_t* zeros, void* stream);
+
+/* INT4 nibble packing [P1 sec.1: two INT4 values per byte; sec.4 "packed
+ * qweight"].  codes [N, K] (uint8 0..15, or int8 -8..7 when symmetric) ->
+ * qweight [N, K/2].  Codes outside the range are masked to 4 bits.
+ * Errors: INVALID_ARG (N, K < 1, K odd, NULL), UNSUPPORTED (device). */
+gq_status gq_pack_int4(const void* codes, int64_t N, int64_t K, int32_t symmetric, uint8_t* qweight,
+                       void* stream);
+
+/* Dequantization x^ = S (q - z) [P1 sec.1; P2 "核心思路" dequantize_group]:
+ * the materialized weight that the fused kernels never write.  Used for tests
+ * and as the unfused comparison path [P2 "亲手实现", pitfall paragraph].
+ *   qweight [N, K/2], scales/zeros [N, K/group_size] (zeros NULL iff symmetric)
+ *   w_hat   [N, K] of out_dtype: GQ_F32 exact, GQ_BF16/GQ_F16 nearest-even.
+ * Errors: INVALID_ARG, UNSUPPORTED (bits != 4, device). */
+gq_status gq_dequantize(const uint8_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                        int64_t N, int64_t K, gq_qparams p, void* w_hat, gq_dtype out_dtype,
+                        void* stream);
+
+/* Fused W4A16 GEMV for decode, 1 <= M <= 16 [P1 sec.2 fused-kernel paragraph;
+ * P2 "工作原理" figure right panel and "亲手实现"; P3 "直接答案" (decode is
+ * memory-bound)]:
+ *   y[m, n] = bf16( sum_g S[n,g] * sum_{k in g} x[m,k] * (q[n,k] - z[n,g]) )
+ * with fp32 accumulation, output rounded to nearest-even bf16.
+ *   x [M, K] bf16, qweight [N, K/2], scales/zeros [N, K/group_size] fp16
+ *   (zeros NULL iff symmetric), y [M, N] bf16.
+ * x, qweight and y must be 16-byte aligned.  Errors: INVALID_ARG (M outside
+ * 1..16, shapes, group_size % 32, zeros NULL-ness), UNSUPPORTED (bits != 4,
+ * device), MISALIGNED. */
+gq_status gq_w4a16_gemv(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                        const uint16_t* scales, const uint16_t* zeros, int64_t N, gq_qparams p,
+                        uint16_t* y, void* stream);
+
+/* Fused W4A16 GEMM for prefill-sized M (any M >= 1, built for M >= 64) on
+ * bf16 MFMA [P1 sec.2; P3 "面试官追问" (weight-only quantization keeps the
+ * FLOPs; prefill is compute-bound)].  Same arithmetic, arguments, layout and
+ * errors as gq_w4a16_gemv except the M range. */
+gq_status gq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                        const uint16_t* scales, const uint16_t* zeros, int64_t N, gq_qparams p,
+                        uint16_t* y, void* stream);
+
+/* Nested 4-bit super-block format [P2 "工作原理" figure, middle panel: 256
+ * weights = 8 sub-blocks of 32, 6-bit scale and 6-bit min per sub-block, fp16
+ * scale-of-scales d and min-of-mins dmin per super-block, 4.5 bits/weight].
+ * Per sub-block j: lo = min(min,0), hi = max(max,0), s_j = (hi-lo)/15 (0 if
+ * equal), m_j = -lo; d = fp16(max_j s_j / 63), dmin = fp16(max_j m_j / 63);
+ * sc_j = clamp(round(s_j/d), 0, 63), mn_j = clamp(round(m_j/dmin), 0, 63)
+ * (0 when d or dmin is 0); q = clamp(round((x + dmin mn_j)/(d sc_j)), 0, 15)
+ * (0 when d sc_j = 0); x^ = d sc_j q - dmin mn_j.  All in binary64.
+ * Block bytes (144): [0] d fp16, [2] dmin fp16, [4] sc_0..7 as a 48-bit
+ * little-endian stream (6 bits each), [10] mn_0..7 likewise, [16] 128 bytes of
+ * nibbles, sub-block j at 16+16j, low nibble = even k.
+ *   w [N, K] (K % 256 == 0) -> blocks [N, K/256, 144].
+ * Errors: INVALID_ARG, UNSUPPORTED (device). */
+gq_status gq_q4k_quantize(const void* w, gq_dtype w_dtype, int64_t N, int64_t K, uint8_t* blocks,
+                          void* stream);
+
+/* Fused GEMV over the super-block format, 1 <= M <= 16:
+ *   y[m, n] = bf16( sum_j d sc_j sum_k x q - dmin mn_j sum_k x ), fp32 accumulation.
+ *   x [M, K] bf16, blocks [N, K/256, 144], y [M, N] bf16.
+ * x, blocks and y must be 16-byte aligned.  Errors: INVALID_ARG, MISALIGNED,
+ * UNSUPPORTED (device). */
+gq_status gq_q4k_gemv(const uint16_t* x, int64_t M, int64_t K, const uint8_t* blocks, int64_t N,
+                      uint16_t* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQ_H_ */

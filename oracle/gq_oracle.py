@@ -82,7 +82,7 @@ def scale_to_f16(v: np.ndarray) -> np.ndarray:
     h = f16_to_f64(f64_to_f16_bits(v))
     h = np.where(np.isinf(h), FP16_MAX, h)
     h = np.where((v > 0) & (h == 0), FP16_MIN_SUB, h)
-    return h
+    return np.where(v > 0, h, 0.0)                     # +0.0, never -0.0
 
 
 def f32_exact_to_bf16_bits(v: np.ndarray) -> np.ndarray:
@@ -255,7 +255,7 @@ def q4k_quantize(w: np.ndarray):
     lo = np.minimum(sub.min(axis=3), 0.0)
     hi = np.maximum(sub.max(axis=3), 0.0)
     s = np.where(hi != lo, (hi - lo) / 15.0, 0.0)      # sub-block step
-    m = -lo                                             # sub-block min (>= 0)
+    m = 0.0 - lo                                        # sub-block min (>= +0)
     d = scale_to_f16(s.max(axis=2) / 63.0)              # fp16 scale of scales
     dmin = scale_to_f16(m.max(axis=2) / 63.0)           # fp16 min of mins
     with np.errstate(divide="ignore", invalid="ignore"):

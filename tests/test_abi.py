@@ -1,0 +1,111 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/gq.h, and rejects invalid arguments on the host before any
+device call (the validation paths return without touching HIP)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT, read_golden
+from oracle import gq_oracle as O
+from w4a16_dequant_gemm_group_amd import binding as B
+
+HEADER = os.path.join(ROOT, "include", "gq.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gq_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert len(names) == 10
+    assert set(names) == set(B.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    for s in range(5):
+        assert lib.gq_status_str(s).decode().startswith("GQ_")
+    assert lib.gq_version() == 100
+
+
+def test_packed_sizes_page_byte_counts():
+    g = read_golden("p1_byte_counts.txt")
+    for n, G, payload, meta, total in (map(int, r) for r in g["_rows"]):
+        q, s, z = B.gq_packed_sizes(1, n, 4, G, False)
+        assert (q, s + z, q + s + z) == (payload, meta, total)
+    for N, K, G, sym in ((6144, 4096, 128, False), (4096, 14336, 32, True), (7, 96, 32, False)):
+        assert B.gq_packed_sizes(N, K, 4, G, sym) == O.packed_sizes(N, K, G, sym)
+
+
+FAKE = ctypes.c_void_p(4096)        # never dereferenced: every case below fails validation
+FAKE_MIS = ctypes.c_void_p(4096 + 4)
+
+
+def q(bits=4, g=128, sym=0):
+    return B.GqQParams(bits, g, sym)
+
+
+@pytest.mark.parametrize("args,expect", [
+    # K not a multiple of the group size
+    (dict(K=1000, p=q()), B.GQ_ERR_INVALID_ARG),
+    # group size not a multiple of 32
+    (dict(K=960, p=q(g=48)), B.GQ_ERR_INVALID_ARG),
+    # M above the GEMV range
+    (dict(M=17), B.GQ_ERR_INVALID_ARG),
+    # negative sizes
+    (dict(N=-1), B.GQ_ERR_INVALID_ARG),
+    # asymmetric without zeros
+    (dict(zeros=None), B.GQ_ERR_INVALID_ARG),
+    # symmetric with zeros
+    (dict(p=q(sym=1)), B.GQ_ERR_INVALID_ARG),
+    # bits other than 4 on a packed path
+    (dict(p=q(bits=8)), B.GQ_ERR_UNSUPPORTED),
+    (dict(p=q(bits=9)), B.GQ_ERR_INVALID_ARG),
+    # misaligned activation / output
+    (dict(x=FAKE_MIS), B.GQ_ERR_MISALIGNED),
+    (dict(y=FAKE_MIS), B.GQ_ERR_MISALIGNED),
+    # NULL buffers
+    (dict(qweight=None), B.GQ_ERR_INVALID_ARG),
+])
+def test_gemv_validation(lib, args, expect):
+    a = dict(x=FAKE, M=1, K=4096, qweight=FAKE, scales=FAKE, zeros=FAKE, N=4096, p=q(), y=FAKE)
+    a.update(args)
+    st = lib.gq_w4a16_gemv(a["x"], a["M"], a["K"], a["qweight"], a["scales"], a["zeros"], a["N"],
+                           a["p"], a["y"], None)
+    assert st == expect
+    if "M" not in args:
+        st = lib.gq_w4a16_gemm(a["x"], a["M"], a["K"], a["qweight"], a["scales"], a["zeros"],
+                               a["N"], a["p"], a["y"], None)
+        assert st == expect
+
+
+def test_empty_problems_are_noops(lib):
+    # nothing to compute: returns OK without touching pointers or the device
+    assert lib.gq_w4a16_gemv(None, 0, 4096, None, None, None, 4096, q(), None, None) == B.GQ_OK
+    assert lib.gq_w4a16_gemm(None, 5, 4096, None, None, None, 0, q(), None, None) == B.GQ_OK
+    assert lib.gq_quantize_groups(None, B.GQ_BF16, 0, 256, q(), None, None, None, None) == B.GQ_OK
+    assert lib.gq_q4k_gemv(None, 0, 256, None, 8, None, None) == B.GQ_OK
+
+
+def test_other_entry_point_validation(lib):
+    L = lib
+    assert L.gq_quantize_groups(FAKE, B.GQ_BF16, 4, 256, q(bits=1), FAKE, FAKE, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_quantize_groups(FAKE, 7, 4, 256, q(), FAKE, FAKE, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_quantize_groups(FAKE, B.GQ_BF16, 4, 256, q(sym=1), FAKE, FAKE, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_pack_int4(FAKE, 4, 255, 0, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_dequantize(FAKE, FAKE, FAKE, 4, 256, q(bits=3), FAKE, B.GQ_F32, None) == B.GQ_ERR_UNSUPPORTED
+    assert L.gq_dequantize(FAKE, FAKE, FAKE, 4, 256, q(), FAKE, 9, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_q4k_quantize(FAKE, B.GQ_BF16, 4, 300, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_q4k_gemv(FAKE, 1, 512, FAKE_MIS, 4, FAKE, None) == B.GQ_ERR_MISALIGNED
+    assert L.gq_q4k_gemv(FAKE, 17, 512, FAKE, 4, FAKE, None) == B.GQ_ERR_INVALID_ARG

@@ -1,0 +1,72 @@
+"""GPU parity of the fused W4A16 MFMA GEMM against the oracle's float64 product.
+
+Small cases span several 256x128 output tiles, ragged M/N/K tails and every
+group size path (32, 64, 96, 128, K); the Llama-3-8B prefill shapes
+(M = 2048, asym g128, activations with 4 channels x50) run at full size in the
+bench's launch configuration and are checked on sampled rows and columns.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import announce, assert_parity, bf16_dev, bits16, f16_dev, u8_dev
+from oracle import gq_oracle as O
+from w4a16_dequant_gemm_group_amd import binding as B
+from w4a16_dequant_gemm_group_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_weights(w_bits, G, sym):
+    codes, s_bits, z_bits = O.quantize_to_storage(w_bits, 4, G, sym)
+    return O.pack_int4(codes, sym), s_bits, z_bits
+
+
+@pytest.mark.parametrize("M,N,K,G,sym", [
+    (256, 128, 128, 128, False),     # exactly one tile
+    (300, 260, 640, 128, False),     # ragged M and N, 10 k tiles
+    (64, 384, 1024, 32, True),       # small M, group 32 (two groups per k tile)
+    (513, 200, 4096, 64, False),
+    (100, 128, 96, 96, False),       # K = 96 = one group, half a k tile
+    (2, 70, 864, 96, True),          # groups straddle k tiles
+    (257, 131, 512, 512, False),     # group = K
+    (1, 128, 256, 32, False),        # M = 1 through the GEMM
+])
+def test_small_shapes(M, N, K, G, sym):
+    w, _ = synth.weights(N, K, seed=N + K)
+    x, _ = synth.activations(M, K, seed=M + 1, n_outlier_channels=min(4, K // 32))
+    qw, s, z = _oracle_weights(w, G, sym)
+    y = B.gq_w4a16_gemm(bf16_dev(x), u8_dev(qw), f16_dev(s), None if sym else f16_dev(z), G, sym)
+    torch.cuda.synchronize()
+    ref = O.w4a16_reference(x, qw, s, z, G, sym)
+    wh = O.dequantize_packed(qw, s, z, G, sym)
+    assert_parity(bits16(y), ref, O.bf16_to_f64(x), wh, f"gemm [{M}x{N}x{K}] G={G} sym={sym}")
+
+
+def test_matches_gemv_on_small_m():
+    """For M <= 16 the GEMM and GEMV compute the same product."""
+    w, x = synth.small(256, 4096, 8, seed=12)
+    qw, s, z = _oracle_weights(w, 128, False)
+    args = (u8_dev(qw), f16_dev(s), f16_dev(z), 128, False)
+    yg = O.bf16_to_f64(bits16(B.gq_w4a16_gemm(bf16_dev(x), *args)))
+    yv = O.bf16_to_f64(bits16(B.gq_w4a16_gemv(bf16_dev(x), *args)))
+    assert O.rel_frobenius(yg, yv) < 3e-3
+
+
+@pytest.mark.parametrize("name", synth.SHAPE_ORDER)
+def test_prefill_shapes_full_size(name):
+    w, x = synth.prefill_case(name)
+    codes, scales, zeros = B.gq_quantize_groups(bf16_dev(w), 4, 128, False)
+    qw = B.gq_pack_int4(codes)
+    y = B.gq_w4a16_gemm(bf16_dev(x), qw, scales, zeros, 128, False)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    rows = np.sort(rng.choice(w.shape[0], 192, replace=False))
+    ms = np.sort(rng.choice(x.shape[0], 96, replace=False))
+    qw_ref, s_ref, z_ref = _oracle_weights(w[rows], 128, False)
+    assert np.array_equal(qw.cpu().numpy()[rows], qw_ref)
+    ref = O.w4a16_reference(x[ms], qw_ref, s_ref, z_ref, 128, False)
+    wh = O.dequantize_packed(qw_ref, s_ref, z_ref, 128, False)
+    yb = bits16(y)[np.ix_(ms, rows)]
+    # the max-error bound uses ||x||_inf of the whole activation
+    assert_parity(yb, ref, O.bf16_to_f64(x), wh, f"gemm {name} M=2048 full, sampled")

@@ -1,0 +1,65 @@
+"""GPU parity of the super-block format: quantize bit-exact (all 144 bytes of
+every block), fused GEMV within the parity bar."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import announce, assert_parity, bf16_dev, bits16, device, u8_dev
+from oracle import gq_oracle as O
+from w4a16_dequant_gemm_group_amd import binding as B
+from w4a16_dequant_gemm_group_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def test_quantize_bit_exact_with_edge_blocks():
+    w, _ = synth.weights(40, 1024, seed=21)
+    wf = O.bf16_to_f64(w)
+    wf[0, :256] = 0.0                       # all-zero block
+    wf[1, 32:64] = 0.0                      # all-zero sub-block
+    wf[2, :256] = np.abs(wf[2, :256])       # no negative values: dmin = 0
+    wf[3, :256] *= 1e-3                     # tiny block: d near fp16 subnormals
+    wb = synth.f32_to_bf16_bits(wf.astype(np.float32))
+    announce("q4k quantize [40,1024] edge blocks")
+    blocks = B.gq_q4k_quantize(bf16_dev(wb))
+    torch.cuda.synchronize()
+    ref = O.q4k_encode(O.q4k_quantize(O.bf16_to_f64(wb)))
+    got = blocks.cpu().numpy()
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"blocks differ at {bad[:5]}"
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
+def test_quantize_other_dtypes(dtype):
+    rng = np.random.default_rng(3)
+    w = rng.normal(0, 0.1, size=(9, 512)).astype(np.float32)
+    wd = torch.from_numpy(w).to(device()).to(dtype)
+    blocks = B.gq_q4k_quantize(wd)
+    ref = O.q4k_encode(O.q4k_quantize(wd.float().cpu().numpy().astype(np.float64)))
+    assert np.array_equal(blocks.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 16])
+@pytest.mark.parametrize("N,K", [(77, 2304), (64, 256), (33, 18432)])
+def test_gemv_small(M, N, K):
+    w, x = synth.small(N, K, M, seed=N + M)
+    blocks = O.q4k_encode(O.q4k_quantize(O.bf16_to_f64(w)))
+    y = B.gq_q4k_gemv(bf16_dev(x), u8_dev(blocks))
+    torch.cuda.synchronize()
+    ref = O.q4k_reference(x, blocks)
+    wh = O.q4k_dequantize_fields(O.q4k_decode(blocks))
+    assert_parity(bits16(y), ref, O.bf16_to_f64(x), wh, f"q4k gemv [{N},{K}] M={M}")
+
+
+@pytest.mark.parametrize("name", ["down", "gate_up"])
+def test_full_size(name):
+    w, x = synth.q4k_case(name)
+    rows = np.sort(np.random.default_rng(6).choice(w.shape[0], 256, replace=False))
+    blocks = B.gq_q4k_quantize(bf16_dev(w))
+    y = B.gq_q4k_gemv(bf16_dev(x), blocks)
+    torch.cuda.synchronize()
+    ref_blocks = O.q4k_encode(O.q4k_quantize(O.bf16_to_f64(w[rows])))
+    assert np.array_equal(blocks.cpu().numpy()[rows], ref_blocks)
+    ref = O.q4k_reference(x, ref_blocks)
+    wh = O.q4k_dequantize_fields(O.q4k_decode(ref_blocks))
+    assert_parity(bits16(y)[:, rows], ref, O.bf16_to_f64(x), wh, f"q4k {name} {w.shape} M=1 full, sampled")

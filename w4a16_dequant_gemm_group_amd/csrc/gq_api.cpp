@@ -1,0 +1,181 @@
+// C ABI of libgq: argument validation, device check and dispatch to the
+// kernels.  Validation runs entirely on the host before any HIP call, so an
+// invalid call never touches the device (and can be exercised without one).
+#include <atomic>
+#include <cstring>
+
+#include "gq_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other architecture
+std::atomic<int> g_arch_state[kMaxDevices];
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+gq_status check_device(hipStream_t stream) {
+  (void)stream;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GQ_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return GQ_ERR_UNSUPPORTED;
+  int st = g_arch_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GQ_ERR_HIP;
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch_state[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? GQ_OK : GQ_ERR_UNSUPPORTED;
+}
+
+gq_status from_hip(hipError_t e) { return e == hipSuccess ? GQ_OK : GQ_ERR_HIP; }
+
+bool valid_dtype(gq_dtype d) { return d == GQ_F32 || d == GQ_F16 || d == GQ_BF16; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+// Shape/group checks common to everything that reads or writes groups.
+gq_status check_groups(int64_t N, int64_t K, int32_t G) {
+  if (N < 0 || K < 1 || N > kMaxDim || K > kMaxDim) return GQ_ERR_INVALID_ARG;
+  if (G < 32 || G % 32 != 0 || K % G != 0) return GQ_ERR_INVALID_ARG;
+  if (N * (K / G) >= ((int64_t)1 << 31)) return GQ_ERR_INVALID_ARG;
+  return GQ_OK;
+}
+
+// Checks shared by the packed 4-bit matmuls.
+gq_status check_w4_matmul(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                          const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                          gq_qparams p, uint16_t* y) {
+  if (M < 0 || M > kMaxDim) return GQ_ERR_INVALID_ARG;
+  if (gq_status s = check_groups(N, K, p.group_size)) return s;
+  if (p.symmetric != 0 && p.symmetric != 1) return GQ_ERR_INVALID_ARG;
+  if (p.bits < 2 || p.bits > 8) return GQ_ERR_INVALID_ARG;
+  if (p.bits != 4) return GQ_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return GQ_OK;
+  if (!x || !qweight || !scales || !y) return GQ_ERR_INVALID_ARG;
+  if ((zeros == nullptr) != (p.symmetric == 1)) return GQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(qweight) || !aligned16(y)) return GQ_ERR_MISALIGNED;
+  return GQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gq_status_str(gq_status s) {
+  switch (s) {
+    case GQ_OK: return "GQ_OK";
+    case GQ_ERR_INVALID_ARG: return "GQ_ERR_INVALID_ARG: argument violates the contract";
+    case GQ_ERR_UNSUPPORTED: return "GQ_ERR_UNSUPPORTED: not implemented for these parameters or this device";
+    case GQ_ERR_MISALIGNED: return "GQ_ERR_MISALIGNED: pointer must be 16-byte aligned";
+    case GQ_ERR_HIP: return "GQ_ERR_HIP: HIP runtime error";
+  }
+  return "unknown gq_status";
+}
+
+int32_t gq_version(void) { return 100; }
+
+gq_status gq_packed_sizes(int64_t N, int64_t K, gq_qparams p, int64_t* qweight_bytes,
+                          int64_t* scale_bytes, int64_t* zero_bytes) {
+  if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return GQ_ERR_INVALID_ARG;
+  if (p.bits < 2 || p.bits > 8) return GQ_ERR_INVALID_ARG;
+  if (p.group_size < 1 || K % p.group_size != 0) return GQ_ERR_INVALID_ARG;
+  if (p.symmetric != 0 && p.symmetric != 1) return GQ_ERR_INVALID_ARG;
+  const int64_t groups = N * (K / p.group_size);
+  if (qweight_bytes) *qweight_bytes = (N * K * p.bits + 7) / 8;
+  if (scale_bytes) *scale_bytes = 2 * groups;
+  if (zero_bytes) *zero_bytes = p.symmetric ? 0 : 2 * groups;
+  return GQ_OK;
+}
+
+gq_status gq_quantize_groups(const void* w, gq_dtype w_dtype, int64_t N, int64_t K, gq_qparams p,
+                             void* codes, uint16_t* scales, uint16_t* zeros, void* stream) {
+  if (gq_status s = check_groups(N, K, p.group_size)) return s;
+  if (p.bits < 2 || p.bits > 8) return GQ_ERR_INVALID_ARG;
+  if (p.symmetric != 0 && p.symmetric != 1) return GQ_ERR_INVALID_ARG;
+  if (!valid_dtype(w_dtype)) return GQ_ERR_INVALID_ARG;
+  if (N == 0) return GQ_OK;
+  if (!w || !codes || !scales) return GQ_ERR_INVALID_ARG;
+  if ((zeros == nullptr) != (p.symmetric == 1)) return GQ_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (gq_status st = check_device(s)) return st;
+  return from_hip(gq::launch_quantize_groups(w, w_dtype, N, K, p.bits, p.group_size, p.symmetric,
+                                             codes, scales, zeros, s));
+}
+
+gq_status gq_pack_int4(const void* codes, int64_t N, int64_t K, int32_t symmetric,
+                       uint8_t* qweight, void* stream) {
+  if (N < 0 || K < 2 || N > kMaxDim || K > kMaxDim || (K & 1)) return GQ_ERR_INVALID_ARG;
+  if (symmetric != 0 && symmetric != 1) return GQ_ERR_INVALID_ARG;
+  if (N == 0) return GQ_OK;
+  if (!codes || !qweight) return GQ_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (gq_status st = check_device(s)) return st;
+  return from_hip(gq::launch_pack_int4(codes, N, K, symmetric, qweight, s));
+}
+
+gq_status gq_dequantize(const uint8_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                        int64_t N, int64_t K, gq_qparams p, void* w_hat, gq_dtype out_dtype,
+                        void* stream) {
+  if (gq_status s = check_groups(N, K, p.group_size)) return s;
+  if (p.symmetric != 0 && p.symmetric != 1) return GQ_ERR_INVALID_ARG;
+  if (p.bits < 2 || p.bits > 8) return GQ_ERR_INVALID_ARG;
+  if (!valid_dtype(out_dtype)) return GQ_ERR_INVALID_ARG;
+  if (p.bits != 4) return GQ_ERR_UNSUPPORTED;
+  if (N == 0) return GQ_OK;
+  if (!qweight || !scales || !w_hat) return GQ_ERR_INVALID_ARG;
+  if ((zeros == nullptr) != (p.symmetric == 1)) return GQ_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (gq_status st = check_device(s)) return st;
+  return from_hip(gq::launch_dequantize(qweight, scales, zeros, N, K, p.group_size, p.symmetric,
+                                        w_hat, out_dtype, s));
+}
+
+gq_status gq_w4a16_gemv(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                        const uint16_t* scales, const uint16_t* zeros, int64_t N, gq_qparams p,
+                        uint16_t* y, void* stream) {
+  if (M > 16) return GQ_ERR_INVALID_ARG;
+  if (gq_status s = check_w4_matmul(x, M, K, qweight, scales, zeros, N, p, y)) return s;
+  if (M == 0 || N == 0) return GQ_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (gq_status st = check_device(s)) return st;
+  return from_hip(gq::launch_w4a16_gemv(x, (int)M, K, qweight, scales, zeros, N, p.group_size,
+                                        p.symmetric, y, s));
+}
+
+gq_status gq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                        const uint16_t* scales, const uint16_t* zeros, int64_t N, gq_qparams p,
+                        uint16_t* y, void* stream) {
+  if (gq_status s = check_w4_matmul(x, M, K, qweight, scales, zeros, N, p, y)) return s;
+  if (M == 0 || N == 0) return GQ_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (gq_status st = check_device(s)) return st;
+  return from_hip(gq::launch_w4a16_gemm(x, M, K, qweight, scales, zeros, N, p.group_size,
+                                        p.symmetric, y, s));
+}
+
+gq_status gq_q4k_quantize(const void* w, gq_dtype w_dtype, int64_t N, int64_t K, uint8_t* blocks,
+                          void* stream) {
+  if (N < 0 || K < 256 || N > kMaxDim || K > kMaxDim || K % 256 != 0) return GQ_ERR_INVALID_ARG;
+  if (!valid_dtype(w_dtype)) return GQ_ERR_INVALID_ARG;
+  if (N == 0) return GQ_OK;
+  if (!w || !blocks) return GQ_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (gq_status st = check_device(s)) return st;
+  return from_hip(gq::launch_q4k_quantize(w, w_dtype, N, K, blocks, s));
+}
+
+gq_status gq_q4k_gemv(const uint16_t* x, int64_t M, int64_t K, const uint8_t* blocks, int64_t N,
+                      uint16_t* y, void* stream) {
+  if (M < 0 || M > 16) return GQ_ERR_INVALID_ARG;
+  if (N < 0 || K < 256 || N > kMaxDim || K > kMaxDim || K % 256 != 0) return GQ_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return GQ_OK;
+  if (!x || !blocks || !y) return GQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(blocks) || !aligned16(y)) return GQ_ERR_MISALIGNED;
+  hipStream_t s = (hipStream_t)stream;
+  if (gq_status st = check_device(s)) return st;
+  return from_hip(gq::launch_q4k_gemv(x, (int)M, K, blocks, N, y, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,136 @@
+// Group-wise affine quantization, INT4 packing and dequantization kernels.
+//
+// Quantization follows "vLLM 量化与推测解码" section 1 (q = clamp(round(x/s)+z),
+// x^ = s(q - z); min-max scale and zero over a zero-inclusive range; per-group
+// along the last axis) and the symmetric max-abs quantizer of the S08 "量化"
+// page ("核心思路").  The decisions are taken in binary64 with the stored fp16
+// scale, so every output is a deterministic function of the input bits.  None
+// of this runs on the decode path: it is the offline step that produces the
+// packed weight the fused kernels read.
+#include "gq_internal.h"
+
+namespace gq {
+namespace {
+
+constexpr int kThreads = 256;
+
+// One thread quantizes one (row, group).  Offline work: simple and exact.
+__global__ __launch_bounds__(kThreads) void quantize_groups_kernel(
+    const void* __restrict__ w, gq_dtype dt, int64_t N, int64_t K, int bits, int G,
+    int symmetric, uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
+    uint16_t* __restrict__ zeros) {
+#pragma clang fp contract(off)
+  const int64_t ng = K / G;
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (gid >= N * ng) return;
+  const int64_t row = gid / ng;
+  const int64_t g = gid - row * ng;
+  const int64_t base = row * K + g * G;
+
+  if (symmetric) {
+    const double qmax = (double)((1 << (bits - 1)) - 1);
+    const double qmin = -(double)(1 << (bits - 1));
+    double amax = 0.0;
+    for (int i = 0; i < G; ++i) amax = fmax(amax, fabs(load_elem_f64(w, base + i, dt)));
+    const double s = amax > 0.0 ? amax / qmax : 1.0;
+    const uint16_t sh = scale_to_f16(s);
+    const double S = f16_to_f64(sh);
+    for (int i = 0; i < G; ++i) {
+      const double q = fmin(fmax(rint(load_elem_f64(w, base + i, dt) / S), qmin), qmax);
+      codes[base + i] = (uint8_t)(int8_t)(int)q;
+    }
+    scales[gid] = sh;
+  } else {
+    const double qmax = (double)((1 << bits) - 1);
+    double lo = 0.0, hi = 0.0;  // the range always holds 0
+    for (int i = 0; i < G; ++i) {
+      const double v = load_elem_f64(w, base + i, dt);
+      lo = fmin(lo, v);
+      hi = fmax(hi, v);
+    }
+    const double s = (hi != lo) ? (hi - lo) / qmax : 1.0;
+    const uint16_t sh = scale_to_f16(s);
+    const double S = f16_to_f64(sh);
+    const double z = fmin(fmax(rint(0.0 - lo / S), 0.0), qmax);
+    for (int i = 0; i < G; ++i) {
+      const double q = fmin(fmax(rint(load_elem_f64(w, base + i, dt) / S) + z, 0.0), qmax);
+      codes[base + i] = (uint8_t)(int)q;
+    }
+    scales[gid] = sh;
+    zeros[gid] = f64_to_f16_rne(z);
+  }
+}
+
+// One thread writes one packed byte (two codes along K).
+__global__ __launch_bounds__(kThreads) void pack_int4_kernel(const uint8_t* __restrict__ codes,
+                                                           int64_t total_bytes, int symmetric,
+                                                           uint8_t* __restrict__ qweight) {
+  const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (j >= total_bytes) return;
+  const uint32_t off = symmetric ? 8u : 0u;
+  const uint32_t lo = ((uint32_t)codes[2 * j] + off) & 15u;
+  const uint32_t hi = ((uint32_t)codes[2 * j + 1] + off) & 15u;
+  qweight[j] = (uint8_t)(lo | (hi << 4));
+}
+
+// One thread expands one packed byte into two weights: S (nibble - z), exact
+// in float32 (11-bit scale times a 5-bit integer).
+__global__ __launch_bounds__(kThreads) void dequantize_kernel(
+    const uint8_t* __restrict__ qweight, const uint16_t* __restrict__ scales,
+    const uint16_t* __restrict__ zeros, int64_t N, int64_t K, int G, int symmetric,
+    void* __restrict__ out, gq_dtype odt) {
+  const int64_t half = K / 2;
+  const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (j >= N * half) return;
+  const int64_t row = j / half;
+  const int64_t k = 2 * (j - row * half);
+  const int64_t gi = row * (K / G) + k / G;
+  const float S = f16_to_f32(scales[gi]);
+  const float z = symmetric ? 8.0f : f16_to_f32(zeros[gi]);
+  const uint32_t b = qweight[j];
+  const float v0 = S * ((float)(b & 15u) - z);
+  const float v1 = S * ((float)(b >> 4) - z);
+  const int64_t o = row * K + k;
+  if (odt == GQ_F32) {
+    ((float*)out)[o] = v0;
+    ((float*)out)[o + 1] = v1;
+  } else if (odt == GQ_BF16) {
+    ((uint16_t*)out)[o] = f32_to_bf16_rne(v0);
+    ((uint16_t*)out)[o + 1] = f32_to_bf16_rne(v1);
+  } else {
+    ((_Float16*)out)[o] = (_Float16)v0;
+    ((_Float16*)out)[o + 1] = (_Float16)v1;
+  }
+}
+
+inline unsigned blocks_for(int64_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
+
+}  // namespace
+
+hipError_t launch_quantize_groups(const void* w, gq_dtype dt, int64_t N, int64_t K, int bits,
+                                  int G, int symmetric, void* codes, uint16_t* scales,
+                                  uint16_t* zeros, hipStream_t s) {
+  const int64_t groups = N * (K / G);
+  hipLaunchKernelGGL(quantize_groups_kernel, dim3(blocks_for(groups)), dim3(kThreads), 0, s, w,
+                     dt, N, K, bits, G, symmetric, (uint8_t*)codes, scales, zeros);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_int4(const void* codes, int64_t N, int64_t K, int symmetric,
+                            uint8_t* qweight, hipStream_t s) {
+  const int64_t total = N * (K / 2);
+  hipLaunchKernelGGL(pack_int4_kernel, dim3(blocks_for(total)), dim3(kThreads), 0, s,
+                     (const uint8_t*)codes, total, symmetric, qweight);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t* qweight, const uint16_t* scales,
+                             const uint16_t* zeros, int64_t N, int64_t K, int G, int symmetric,
+                             void* out, gq_dtype odt, hipStream_t s) {
+  const int64_t total = N * (K / 2);
+  hipLaunchKernelGGL(dequantize_kernel, dim3(blocks_for(total)), dim3(kThreads), 0, s, qweight,
+                     scales, zeros, N, K, G, symmetric, out, odt);
+  return hipGetLastError();
+}
+
+}  // namespace gq
