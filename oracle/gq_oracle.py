@@ -349,6 +349,28 @@ def max_err_bound(x64, w_hat64) -> float:
     return 1e-2 * float(np.abs(x64).max()) * float(np.abs(w_hat64).max()) * np.sqrt(K) / 64.0
 
 
+def bf16_half_ulp(v) -> np.ndarray:
+    """Half the spacing of bf16 values at |v| (the rounding error a bf16 output
+    can carry on its own); 2^-134 below the normal range."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -126.0)
+    return np.where(a > 0, 2.0 ** (e - 8), 2.0 ** -134)
+
+
+def within_parity(y, y_ref, x64, w_hat):
+    """The matmul parity bar: relative Frobenius error <= 2e-3 and, element-wise,
+    |y - y_ref| <= 1e-2 ||x||_inf ||w^||_inf sqrt(K)/64 plus half a bf16 ulp of
+    the output (the result is stored as bf16, whose rounding alone may exceed the
+    first term when K is small).  Returns (ok, rel_f, max_excess_ratio)."""
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    rel = rel_frobenius(y, y_ref)
+    allow = max_err_bound(x64, w_hat) + bf16_half_ulp(np.maximum(np.abs(y), np.abs(y_ref)))
+    ratio = float((np.abs(y - y_ref) / allow).max()) if y.size else 0.0
+    return (rel <= 2e-3 and ratio <= 1.0), rel, ratio
+
+
 def snr_db(w, w_hat) -> float:
     w = np.asarray(w, dtype=np.float64)
     e = np.asarray(w_hat, dtype=np.float64) - w

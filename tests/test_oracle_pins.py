@@ -324,10 +324,10 @@ def test_tolerance_bar_accepts_bf16_rounding_and_rejects_mistakes():
     ref = O.w4a16_reference(x, qw, sb, zb, G, False)
     wh = O.dequantize_packed(qw, sb, zb, G, False)
     x64 = O.bf16_to_f64(x)
-    bound = O.max_err_bound(x64, wh)
 
     def passes(y):
-        return O.rel_frobenius(y, ref) <= 2e-3 and np.abs(y - ref).max() <= bound
+        ok, _, _ = O.within_parity(y, ref, x64, wh)
+        return ok
 
     y_rne = O.bf16_to_f64(O.f32_exact_to_bf16_bits(ref.astype(np.float32).astype(np.float64)))
     assert passes(y_rne)
@@ -441,3 +441,15 @@ def test_q4k_reference_matches_dense_product():
     ref = O.bf16_to_f64(x) @ wh.T
     assert np.allclose(y, ref, rtol=1e-12, atol=1e-13)
     assert O.snr_db(O.bf16_to_f64(w), wh) > 15
+
+
+def test_bf16_half_ulp_closed_form():
+    # bf16 keeps 8 significant bits: spacing 2^(e-7) in [2^e, 2^(e+1))
+    for v, want in ((1.0, 2.0 ** -8), (1.99, 2.0 ** -8), (2.0, 2.0 ** -7), (10.0, 2.0 ** -5),
+                    (-0.3, 2.0 ** -10), (0.0, 2.0 ** -134)):
+        assert float(O.bf16_half_ulp(np.array([v]))[0]) == want
+    # a value and its bf16 rounding differ by at most half an ulp
+    rng = np.random.default_rng(2)
+    v = rng.normal(0, 10, 5000).astype(np.float32).astype(np.float64)
+    r = O.bf16_to_f64(O.f32_exact_to_bf16_bits(v))
+    assert np.all(np.abs(r - v) <= O.bf16_half_ulp(v))
