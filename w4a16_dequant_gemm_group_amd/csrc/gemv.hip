@@ -7,22 +7,31 @@
 // dequantized weight exists only in registers.
 //
 // Decode is bound by HBM bandwidth (S08 "为什么重要": latency = bytes /
-// bandwidth), so the kernel is shaped around the weight stream:
-//   * a wavefront owns RPW rows; lane l of the wave reads 16 contiguous bytes
-//     (32 nibbles) of a row at k = 2048 t + 32 l, so one wave load instruction
-//     covers 1 KiB of a row contiguously (global_load_dwordx4, fully coalesced);
-//     every weight load of the wave's rows is issued before any arithmetic;
-//   * x is staged once per workgroup into LDS, pre-permuted so that each
-//     dword holds the bf16 pair (x[k+p], x[k+p+4]) that matches the nibble pair
-//     (k+p, k+p+4) extracted below, plus the sum of every 32-element chunk;
-//   * a nibble pair becomes two exact bf16 values 128+q with one AND-OR
-//     (0x4300 is bf16 128.0; the nibble fills the low mantissa bits), and
-//     v_dot2c_f32_bf16 multiplies both by x and accumulates in fp32:
-//     11 VALU ops per 8 weights;
-//   * per 32-chunk the offset and zero point are removed with the chunk sum:
-//     sum x (q - z) = sum x (128 + q) - (128 + z) sum x, then scaled by S;
-//   * the fp32 partials are summed across the wave with cross-lane adds and
-//     rounded once to bf16 (nearest-even).
+// bandwidth), so both kernels are shaped around the weight stream.  Lane l of a
+// wavefront owns the 32 weights at k = 2048 t + 32 l of a row (one 16-byte
+// load; a wave load covers 1 KiB of a row contiguously).  A nibble becomes the
+// exact bf16 value 128 + q by placing it under the exponent byte 0x43 (bf16
+// 128.0, whose low mantissa bits the nibble fills), v_dot2_f32_bf16 multiplies
+// a pair of them by the matching activation pair with fp32 accumulation, and
+// per 32-element chunk the offset and zero point are removed with the chunk's
+// sum of x:  sum x (q - z) = sum x (128 + q) - (128 + z) sum x,  then scaled by
+// S.  The row's 64 lane partials are summed across the wave and rounded once
+// to bf16 (nearest-even).
+//
+// gemv_stream_kernel (M = 1): persistent workgroups; x is staged once per
+// workgroup into LDS (pre-permuted into the pairs the nibble extraction yields,
+// plus every chunk sum).  Each wave walks a sequence of work items (a pair of
+// rows x one 2048-wide k step) with three register buffers, so two items' loads
+// are in flight while one is multiplied.  Loads are raw buffer loads with the
+// nontemporal hint against whole-matrix descriptors; anything past the matrix
+// (rows beyond N, lanes beyond a ragged K) reads as zero from the hardware's
+// range check, so the loads are unconditional and the compiler's wait counts
+// stay exact.  Row sums are reduced with DPP (quad_perm, row_ror, row_bcast).
+//
+// gemv_chunked_kernel (M = 2..16, or K too long for x to sit in LDS): x staged
+// per K chunk for all M rows; one workgroup per 4*RPW rows.
+#include <algorithm>
+
 #include "gq_internal.h"
 
 namespace gq {
@@ -86,7 +95,7 @@ __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, int M, i
 // MT: activation rows handled together (M <= MT), RPW: weight rows per wave,
 // T: 2048-wide steps per LDS chunk.  Each workgroup owns 4*RPW rows.
 template <int MT, int RPW, int T, bool SYM>
-__global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(
+__global__ __launch_bounds__(kThreads) void gemv_chunked_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
     uint16_t* __restrict__ y) {
@@ -167,7 +176,7 @@ hipError_t launch_t(const uint16_t* x, int M, int K, const uint8_t* qw, const ui
                     const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
   const int rows_per_block = kWaves * RPW;
   const unsigned grid = (unsigned)((N + rows_per_block - 1) / rows_per_block);
-  hipLaunchKernelGGL((w4a16_gemv_kernel<MT, RPW, T, SYM>), dim3(grid), dim3(kThreads), 0, s, x,
+  hipLaunchKernelGGL((gemv_chunked_kernel<MT, RPW, T, SYM>), dim3(grid), dim3(kThreads), 0, s, x,
                      M, K, qw, sc, zr, N, G, y);
   return hipGetLastError();
 }
@@ -194,11 +203,278 @@ hipError_t dispatch(const uint16_t* x, int M, int K, const uint8_t* qw, const ui
   return launch_t<16, 2, 1, SYM>(x, M, K, qw, sc, zr, N, G, y, s);
 }
 
+
+// ---------------------------------------------------------------------------
+// M = 1 streaming kernel
+// ---------------------------------------------------------------------------
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kSRpw = 2;    // rows per work item
+constexpr int kSNbuf = 3;   // register buffers (items in flight + 1)
+constexpr int kSMaxT = 13;  // 2048-steps of x that fit the LDS budget
+constexpr uint32_t kOob = 0x80000000u;  // an offset past every buffer's range
+
+// Raw buffer descriptor over [base, base + bytes); every field wave-uniform.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, (int)n,
+                                           0x00020000);
+}
+
+// 8 nibbles (k = 0..7 at bits 4p) against activation pairs (x0,x2) (x4,x6)
+// (x1,x3) (x5,x7): the even and odd nibbles are split into bytes, and each
+// byte pair gets the exponent byte 0x43 from `magic` (0x43004300) by v_perm.
+__device__ __forceinline__ float dot8_perm(uint32_t d, const uint4& xp, float a, uint32_t magic) {
+  const uint32_t ev = d & 0x0F0F0F0Fu;
+  const uint32_t od = (d >> 4) & 0x0F0F0F0Fu;
+  a = dot2(__builtin_amdgcn_perm(ev, magic, 0x01050104u), xp.x, a);
+  a = dot2(__builtin_amdgcn_perm(ev, magic, 0x01070106u), xp.y, a);
+  a = dot2(__builtin_amdgcn_perm(od, magic, 0x01050104u), xp.z, a);
+  a = dot2(__builtin_amdgcn_perm(od, magic, 0x01070106u), xp.w, a);
+  return a;
+}
+
+// x0..x7 (bf16, natural order in v) -> pairs (x0,x2) (x4,x6) (x1,x3) (x5,x7).
+__device__ __forceinline__ uint4 perm_x_pairs(uint4 v) {
+  uint4 p;
+  p.x = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);
+  p.y = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);
+  p.z = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);
+  p.w = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);
+  return p;
+}
+
+__device__ __forceinline__ float sum_bf16x8(uint4 v) {
+  float s = bf16_to_f32(v.x & 0xFFFFu) + bf16_to_f32(v.x >> 16);
+  s += bf16_to_f32(v.y & 0xFFFFu) + bf16_to_f32(v.y >> 16);
+  s += bf16_to_f32(v.z & 0xFFFFu) + bf16_to_f32(v.z >> 16);
+  s += bf16_to_f32(v.w & 0xFFFFu) + bf16_to_f32(v.w >> 16);
+  return s;
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               ROW_MASK, 0xF, ROW_MASK == 0xF));
+}
+
+// Sum over the 64 lanes; the total lands in lane 63.
+__device__ __forceinline__ float wave_sum_to_lane63(float v) {
+  v += dpp_f32<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0x124, 0xF>(v);  // row_ror:4
+  v += dpp_f32<0x128, 0xF>(v);  // row_ror:8  (every lane holds its row's sum)
+  v += dpp_f32<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_f32<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+struct StreamBuf {
+  uint4 w[kSRpw];
+  uint32_t s[kSRpw], z[kSRpw];
+};
+
+struct Cursor {
+  int b, p;  // row pair, k step
+};
+
+__device__ __forceinline__ void advance(Cursor& c, int T, int W) {
+  if (++c.p == T) {
+    c.p = 0;
+    c.b += W;
+  }
+}
+
+// TAB: per-(step, lane) byte offsets come from LDS tables (ragged K or a group
+// size that does not divide 2048); otherwise they are lane constants plus a
+// uniform per-step term.
+template <bool SYM, bool TAB>
+__device__ __forceinline__ void stream_load(StreamBuf& B, Cursor c, int N, uint32_t rb, uint32_t ngb,
+                                            uint32_t sgs, uint32_t vw, uint32_t vs,
+                                            const uint32_t* wtab, const uint32_t* stab, int lane,
+                                            rsrc_t rw, rsrc_t rs, rsrc_t rz) {
+  uint32_t ow = vw, os = vs, uw = (uint32_t)c.p * 1024u, us = (uint32_t)c.p * sgs;
+  if (TAB) {
+    ow = wtab[c.p * 64 + lane];
+    os = stab[c.p * 64 + lane];
+    uw = 0;
+    us = 0;
+  }
+#pragma unroll
+  for (int r = 0; r < kSRpw; ++r) {
+    const uint32_t row = (uint32_t)min(c.b * kSRpw + r, N);  // row N reads out of range
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, ow, row * rb + uw, 2);
+    B.w[r] = make_uint4(v[0], v[1], v[2], v[3]);
+    B.s[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, os, row * ngb + us, 0);
+    if (!SYM) B.z[r] = __builtin_amdgcn_raw_buffer_load_b16(rz, os, row * ngb + us, 0);
+  }
+}
+
+template <bool SYM>
+__device__ __forceinline__ void stream_compute(const StreamBuf& B, Cursor c, int T, int N, int lane,
+                                               const uint4* xs, const float* sxs,
+                                               uint16_t* __restrict__ y, uint32_t magic,
+                                               float (&acc)[kSRpw]) {
+  if (c.p == 0) {
+#pragma unroll
+    for (int r = 0; r < kSRpw; ++r) acc[r] = 0.f;
+  }
+  const uint4* xp = xs + c.p * 256 + lane * 4;
+  const uint4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
+  const float sx = sxs[c.p * 64 + lane];
+  const float init = -128.f * sx;
+#pragma unroll
+  for (int r = 0; r < kSRpw; ++r) {
+    float a = dot8_perm(B.w[r].x, x0, init, magic);
+    a = dot8_perm(B.w[r].y, x1, a, magic);
+    a = dot8_perm(B.w[r].z, x2, a, magic);
+    a = dot8_perm(B.w[r].w, x3, a, magic);
+    const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)B.s[r]);
+    const float z = SYM ? 8.f : (float)__builtin_bit_cast(_Float16, (uint16_t)B.z[r]);
+    acc[r] = fmaf(sc, fmaf(-z, sx, a), acc[r]);
+  }
+  if (c.p == T - 1) {
+#pragma unroll
+    for (int r = 0; r < kSRpw; ++r) {
+      const float v = wave_sum_to_lane63(acc[r]);
+      const int row = c.b * kSRpw + r;
+      if (lane == 63 && row < N) y[row] = f32_to_bf16_rne(v);
+    }
+  }
+}
+
+// Requires N * K/2 < 2^32 and N * (K/G) * 2 < 2^32 (the launcher splits N).
+template <bool SYM, bool TAB>
+__global__ __launch_bounds__(kThreads) void gemv_stream_kernel(
+    const uint16_t* __restrict__ x, int K, const uint8_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
+    uint16_t* __restrict__ y) {
+  extern __shared__ uint4 lds[];
+  const int T = (K + kStepK - 1) / kStepK;
+  uint4* xs = lds;                                      // [T * 256] permuted x pairs
+  float* sxs = (float*)(xs + T * 256);                  // [T * 64] chunk sums
+  uint32_t* wtab = (uint32_t*)(sxs + T * 64);           // [T * 64] (TAB only)
+  uint32_t* stab = wtab + T * 64;                       // [T * 64] (TAB only)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nb = (N + kSRpw - 1) / kSRpw;
+  const int W = gridDim.x * kWaves;
+  const uint32_t rb = (uint32_t)K / 2;
+  const uint32_t ngb = (uint32_t)(K / G) * 2;
+  const uint32_t sgs = TAB ? 0u : (uint32_t)(kStepK / G) * 2;
+  const uint32_t vw = (uint32_t)lane * 16;
+  const uint32_t vs = TAB ? 0u : (uint32_t)((lane * 32) / G) * 2;
+  const uint32_t magic = 0x43004300u;
+  const rsrc_t rw = make_rsrc(qw, (uint32_t)N * rb);
+  const rsrc_t rs = make_rsrc(scales, (uint32_t)N * ngb);
+  const rsrc_t rz = make_rsrc(SYM ? (const void*)scales : (const void*)zeros, (uint32_t)N * ngb);
+
+  if (TAB) {  // byte offsets per (step, lane); lanes past K read out of range
+    for (int i = threadIdx.x; i < T * 64; i += kThreads) {
+      const int k = (i >> 6) * kStepK + (i & 63) * 32;
+      wtab[i] = k < K ? (uint32_t)k / 2 : kOob;
+      stab[i] = k < K ? (uint32_t)(k / G) * 2 : kOob;
+    }
+    __syncthreads();
+  }
+
+  // x: issue the first loads before the weight prefetch, stage after it.
+  constexpr int kXr = 8;
+  uint4 xv[kXr];
+#pragma unroll
+  for (int i = 0; i < kXr; ++i) {
+    const int c = threadIdx.x + kThreads * i;
+    xv[i] = make_uint4(0, 0, 0, 0);
+    if (i < T && c * 8 < K) xv[i] = *(const uint4*)(x + c * 8);
+  }
+
+  StreamBuf buf[kSNbuf];
+  float acc[kSRpw];
+#pragma unroll
+  for (int r = 0; r < kSRpw; ++r) acc[r] = 0.f;
+  Cursor lc{(int)blockIdx.x * kWaves + wave, 0};
+  Cursor cc = lc;
+#pragma unroll
+  for (int j = 0; j < kSNbuf - 1; ++j) {
+    stream_load<SYM, TAB>(buf[j], lc, N, rb, ngb, sgs, vw, vs, wtab, stab, lane, rw, rs, rz);
+    advance(lc, T, W);
+  }
+
+  for (int c0 = 0; c0 < T * 256; c0 += kXr * kThreads) {
+#pragma unroll
+    for (int i = 0; i < kXr; ++i) {
+      const int c = c0 + threadIdx.x + kThreads * i;
+      uint4 v = xv[i];
+      if (c0 > 0) {
+        v = make_uint4(0, 0, 0, 0);
+        if (c < T * 256 && c * 8 < K) v = *(const uint4*)(x + c * 8);
+      }
+      if (c0 + kThreads * i < T * 256) {  // uniform over the block
+        xs[c] = perm_x_pairs(v);
+        float sm = sum_bf16x8(v);
+        sm += __shfl_xor(sm, 1, 64);
+        sm += __shfl_xor(sm, 2, 64);
+        if ((c & 3) == 0) sxs[c >> 2] = sm;
+      }
+    }
+  }
+  __syncthreads();
+
+  while (cc.b < nb) {
+#pragma unroll
+    for (int j = 0; j < kSNbuf; ++j) {
+      if (cc.b >= nb) break;
+      stream_load<SYM, TAB>(buf[(j + kSNbuf - 1) % kSNbuf], lc, N, rb, ngb, sgs, vw, vs, wtab, stab,
+                            lane, rw, rs, rz);
+      advance(lc, T, W);
+      stream_compute<SYM>(buf[j], cc, T, N, lane, xs, sxs, y, magic, acc);
+      advance(cc, T, W);
+    }
+  }
+}
+
+template <bool SYM, bool TAB>
+hipError_t launch_stream(const uint16_t* x, int K, const uint8_t* qw, const uint16_t* sc,
+                         const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
+  const int T = (K + kStepK - 1) / kStepK;
+  const size_t lds = (size_t)T * (256 * 16 + 64 * 4) + (TAB ? (size_t)T * 64 * 8 : 0);
+  const int nb = (N + kSRpw - 1) / kSRpw;
+  const int grid = std::max(1, std::min((nb + kWaves - 1) / kWaves, 2 * num_cus()));
+  hipLaunchKernelGGL((gemv_stream_kernel<SYM, TAB>), dim3(grid), dim3(kThreads), lds, s, x, K, qw,
+                     sc, zr, N, G, y);
+  return hipGetLastError();
+}
+
+template <bool SYM>
+hipError_t stream_m1(const uint16_t* x, int K, const uint8_t* qw, const uint16_t* sc,
+                     const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
+  // Rows per launch so that every byte offset fits 32 bits.
+  const uint64_t rb = (uint64_t)K / 2, ngb = (uint64_t)(K / G) * 2;
+  const int64_t cap = (int64_t)std::min<uint64_t>(((uint64_t)1 << 31) / rb, ((uint64_t)1 << 31) / ngb);
+  const bool tab = (K % kStepK) != 0 || (kStepK % G) != 0;
+  for (int64_t n0 = 0; n0 < N; n0 += cap) {
+    const int n = (int)std::min<int64_t>(cap, N - n0);
+    const uint8_t* q = qw + n0 * rb;
+    const uint16_t* a = sc + n0 * (K / G);
+    const uint16_t* b = SYM ? zr : zr + n0 * (K / G);
+    hipError_t e = tab ? launch_stream<SYM, true>(x, K, q, a, b, n, G, y + n0, s)
+                       : launch_stream<SYM, false>(x, K, q, a, b, n, G, y + n0, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 }  // namespace
 
 hipError_t launch_w4a16_gemv(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
                              const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
                              int symmetric, uint16_t* y, hipStream_t s) {
+  if (M == 1 && (K + kStepK - 1) / kStepK <= kSMaxT) {
+    if (symmetric) return stream_m1<true>(x, (int)K, qweight, scales, zeros, (int)N, G, y, s);
+    return stream_m1<false>(x, (int)K, qweight, scales, zeros, (int)N, G, y, s);
+  }
   if (symmetric) return dispatch<true>(x, M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
   return dispatch<false>(x, M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
 }

@@ -11,6 +11,8 @@ namespace {
 constexpr int kMaxDevices = 64;
 // 0 = unknown, 1 = gfx950, 2 = other architecture
 std::atomic<int> g_arch_state[kMaxDevices];
+// compute-unit count per device (0 = unknown)
+std::atomic<int> g_num_cus[kMaxDevices];
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -24,6 +26,7 @@ gq_status check_device(hipStream_t stream) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GQ_ERR_HIP;
     st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_num_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
     g_arch_state[dev].store(st, std::memory_order_relaxed);
   }
   return st == 1 ? GQ_OK : GQ_ERR_UNSUPPORTED;
@@ -60,6 +63,17 @@ gq_status check_w4_matmul(const uint16_t* x, int64_t M, int64_t K, const uint8_t
 }
 
 }  // namespace
+
+namespace gq {
+
+int num_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  const int n = g_num_cus[dev].load(std::memory_order_relaxed);
+  return n > 0 ? n : 256;
+}
+
+}  // namespace gq
 
 extern "C" {
 

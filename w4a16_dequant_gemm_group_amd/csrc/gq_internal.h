@@ -88,6 +88,9 @@ __device__ __forceinline__ double load_elem_f64(const void* p, int64_t i, gq_dty
   return (double)((const float*)p)[i];
 }
 
+// Compute units of the current device (set by the C ABI's device check).
+int num_cus();
+
 // ---------------------------------------------------------------------------
 // Launchers (arguments already validated by the C ABI layer)
 // ---------------------------------------------------------------------------
