@@ -5,12 +5,21 @@ projections qkv [6144,4096], o [4096,4096], gate_up [28672,4096] and down
 [4096,14336], INT4 asymmetric, group 128, fp16 scale + zero, bf16 activations.
 Each step reads a different copy of the packed weights (copies rotate over at
 least 1 GiB, four times the 256 MB Infinity Cache), so the weights stream
-from HBM as they do in a real decode over 32 layers.
+from HBM as they do in a real decode over 32 layers.  Inputs are resident in
+HBM before the timed region starts.
 
 value = algorithmic bytes of a step / step time (GB/s), where the algorithmic
 bytes per [N, K] projection are N*K/2 + 4*N*K/G + 2*K + 2*N (packed codes,
 fp16 scale and zero per group, bf16 x in, bf16 y out).  Before timing, every
 projection's output is checked against the CPU oracle on sampled rows.
+
+The roofline object describes the step's only kernel (every projection runs
+the same streaming GEMV kernel): algorithmic bytes per launch over the
+average launch duration, both from the timed region, against 8 TB/s.  Its
+`traffic` comes from rocprofv3 FETCH_SIZE / WRITE_SIZE passes (see
+--profile-pass and --summarize-traffic), scaled by what the same counters
+read for a copy of known size; it is reported only while the GEMV source is
+the one the counters were taken on, else null.
 
 Also reported: the prefill GEMM (M=2048, same shapes) in TFLOP/s against the
 dense bf16 MFMA peak, the small-batch and super-block GEMVs, a bf16 GEMV
@@ -22,6 +31,8 @@ Prints ONE JSON line.  python bench.py [--steps K] [--warmup W] [--gpus 1]
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -35,6 +46,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "W4A16 dequant-GEMV HBM GB/s & % peak (M=1); MFMA TFLOP/s at M=2048"
+GEMV_SOURCE = os.path.join(ROOT, "w4a16_dequant_gemm_group_amd", "csrc", "gemv.hip")
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "w4a16_gemv_stream_traffic.json")
+GEMV_KERNEL = "gemv_stream_kernel"
+CALIB_BYTES = 256 << 20          # calibration copy: reads and writes this many bytes
+G = 128
 
 
 def log(msg):
@@ -46,6 +62,64 @@ def gemv_bytes(n, k, g, m=1, sym=False):
     return n * k // 2 + n * (k // g) * meta + 2 * m * k + 2 * m * n
 
 
+def source_digest() -> str:
+    with open(GEMV_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------
+# rocprofv3 counter passes -> per-launch HBM traffic
+# ----------------------------------------------------------------------------
+
+def _counter_rows(d):
+    for root, _, files in os.walk(d):
+        for fn in files:
+            if fn.endswith("counter_collection.csv"):
+                with open(os.path.join(root, fn)) as f:
+                    yield from csv.DictReader(f)
+
+
+def summarize_traffic(fetch_dir, write_dir):
+    """Reduce the FETCH_SIZE and WRITE_SIZE passes of `--profile-pass` to
+    per-launch HBM bytes of the GEMV, calibrated against the copy kernel."""
+    from w4a16_dequant_gemm_group_amd import synth
+    shapes = [(nm,) + synth.LLAMA3_8B_SHAPES[nm] for nm in synth.SHAPE_ORDER]
+    out = {"source_sha256_16": source_digest(), "kernel": GEMV_KERNEL, "calibration_bytes": CALIB_BYTES}
+    for cname, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _counter_rows(d) if r["Counter_Name"] == cname]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        calib = [float(r["Counter_Value"]) for r in rows if "neg" in r["Kernel_Name"]]
+        gemv = [float(r["Counter_Value"]) for r in rows if GEMV_KERNEL in r["Kernel_Name"]]
+        if not calib or not gemv or len(gemv) % len(shapes):
+            raise SystemExit(f"{cname}: expected calibration and {len(shapes)}*k GEMV dispatches, "
+                             f"found {len(calib)} / {len(gemv)}")
+        factor = CALIB_BYTES / (max(calib) * 1024.0)        # bytes per counted KiB
+        per = {}
+        for i, (nm, _, _) in enumerate(shapes):
+            vals = gemv[i::len(shapes)]
+            per[nm] = float(np.median(vals)) * 1024.0 * factor
+        out[cname] = {"scale_bytes_per_KiB": round(factor * 1024.0, 4), "per_launch_bytes": per}
+    tot = {nm: out["FETCH_SIZE"]["per_launch_bytes"][nm] + out["WRITE_SIZE"]["per_launch_bytes"][nm]
+           for nm, _, _ in shapes}
+    out["hbm_bytes_per_launch"] = tot
+    out["mean_hbm_bytes_per_launch"] = float(np.mean(list(tot.values())))
+    out["algorithmic_bytes_per_launch"] = {nm: gemv_bytes(n, k, G) for nm, n, k in shapes}
+    print(json.dumps(out, indent=1))
+
+
+def load_traffic():
+    try:
+        with open(TRAFFIC_JSON) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256_16") != source_digest():
+        return None
+    return t
+
+
+# ----------------------------------------------------------------------------
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -55,15 +129,21 @@ def main():
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the decode step (used for profiling)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="run a few decode steps and one calibration copy, for rocprofv3 --pmc")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="reduce two rocprofv3 --pmc passes of --profile-pass to per-launch bytes")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic)
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported here "
               "(the kernels shard by output rows with no exchange; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
 
     import torch
-    from oracle import gq_oracle as O
     from w4a16_dequant_gemm_group_amd import binding as B
     from w4a16_dequant_gemm_group_amd import synth
 
@@ -77,12 +157,10 @@ def main():
     def bits16(t):
         return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
-    G = 128
     shapes = [(name,) + synth.LLAMA3_8B_SHAPES[name] for name in synth.SHAPE_ORDER]
 
-    # ---------------- inputs, quantized on the GPU, parity-gated -----------------
-    W, X = {}, {}
-    host = {}
+    # ---------------- inputs, quantized on the GPU -------------------------------
+    W, X, host = {}, {}, {}
     for name, n, k in shapes:
         w, x = synth.decode_case(name)
         host[name] = (w, x)
@@ -91,6 +169,21 @@ def main():
         X[name] = to_dev(x)
         del codes
     torch.cuda.synchronize()
+    Y = {nm: torch.empty((1, n), dtype=torch.bfloat16, device=dev) for nm, n, _ in shapes}
+
+    if args.profile_pass:
+        for _ in range(3):
+            for nm, _, _ in shapes:
+                qw, s, z = W[nm]
+                B.gq_w4a16_gemv(X[nm], qw, s, z, G, False, y=Y[nm])
+        a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        log("profile pass done")
+        return
+
+    from oracle import gq_oracle as O
     log("inputs ready; parity gate")
     for name, n, k in shapes:
         w, x = host[name]
@@ -102,10 +195,10 @@ def main():
         if not np.array_equal(qw.cpu().numpy()[rows], qref):
             raise SystemExit(f"parity gate: packed weights of {name} differ from the oracle")
         ref = O.w4a16_reference(x, qref, s_ref, z_ref, G, False)
-        yv = O.bf16_to_f64(bits16(y))[:, rows]
-        rel = O.rel_frobenius(yv, ref)
-        if rel > 2e-3:
-            raise SystemExit(f"parity gate: {name} relF {rel:.2e}")
+        wh = O.dequantize_packed(qref, s_ref, z_ref, G, False)
+        ok, rel, ratio = O.within_parity(O.bf16_to_f64(bits16(y))[:, rows], ref, O.bf16_to_f64(x), wh)
+        if not ok:
+            raise SystemExit(f"parity gate: {name} relF {rel:.2e} max/allowed {ratio:.2f}")
     log("parity gate passed")
 
     # ---------------- rotation copies ------------------------------------------------
@@ -113,10 +206,8 @@ def main():
                             for nm, _, _ in shapes)
     R = max(2, int(np.ceil(args.rotate_gib * 2 ** 30 / step_weight_bytes)))
     copies = [W] + [{nm: tuple(t.clone() for t in W[nm]) for nm, _, _ in shapes} for _ in range(R - 1)]
-    Y = {nm: torch.empty((1, n), dtype=torch.bfloat16, device=dev) for nm, n, _ in shapes}
     torch.cuda.synchronize()
     log(f"{R} rotating weight copies of {step_weight_bytes / 1e6:.1f} MB")
-
     step_bytes = sum(gemv_bytes(n, k, G) for _, n, k in shapes)
 
     def run_step(i):
@@ -137,6 +228,7 @@ def main():
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0.record(stream)
     g.replay()
     t1.record(stream)
@@ -162,22 +254,27 @@ def main():
             B.gq_w4a16_gemv(X[nm], qw, s, z, G, False, y=Y[nm], stream=torch.cuda.current_stream())
         per_us[nm] = graph_time(torch, stream, one, nrep)
     per_gbps = {nm: gemv_bytes(n, k, G) / (per_us[nm] * 1e-6) / 1e9 for nm, n, k in shapes}
-    # dominant kernel: the K=4096 instantiation (qkv, o, gate_up launches)
-    k4096 = [(nm, n, k) for nm, n, k in shapes if k == 4096]
-    dom_bytes = float(np.mean([gemv_bytes(n, k, G) for _, n, k in k4096]))
-    dom_us = float(np.mean([per_us[nm] for nm, _, _ in k4096]))
-    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                "kernel": "w4a16_gemv_kernel<1,2,2,false> (K=4096: qkv, o, gate_up)",
-                "bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 3)}
     log(f"per-shape us {per_us}")
+
+    # Every launch of the step is the same streaming GEMV kernel: its algorithmic
+    # bytes per launch over its average launch duration in the timed region.
+    bytes_per_launch = step_bytes / len(shapes)
+    avg_launch_us = ms_per_step * 1e3 / len(shapes)
+    achieved = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
+    tr = load_traffic()
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": None if tr is None else round(tr["mean_hbm_bytes_per_launch"]),
+                "kernel": f"{GEMV_KERNEL}<false,false> (all four projections)",
+                "bytes_per_launch": bytes_per_launch, "avg_launch_us": round(avg_launch_us, 3)}
+    if tr is not None:
+        roofline["traffic_per_shape"] = {k: round(v) for k, v in tr["hbm_bytes_per_launch"].items()}
 
     extras = {}
     if not args.skip_extras:
-        extras = run_extras(args, torch, B, O, synth, to_dev, bits16, dev, stream, shapes, W, X, G)
+        extras = run_extras(torch, B, synth, to_dev, dev, stream, shapes, W, X)
 
-    cpu = cpu_baseline(args, O, synth, host, shapes, G)
+    cpu = cpu_baseline(args, O, host, shapes)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -238,7 +335,7 @@ def time_launches(torch, stream, fn, reps):
     return t0.elapsed_time(t1) / reps * 1e3  # us
 
 
-def run_extras(args, torch, B, O, synth, to_dev, bits16, dev, stream, shapes, W, X, G):
+def run_extras(torch, B, synth, to_dev, dev, stream, shapes, W, X):
     ex = {}
     # ---- prefill GEMM, M = 2048 -------------------------------------------------
     gemm = {}
@@ -285,7 +382,7 @@ def run_extras(args, torch, B, O, synth, to_dev, bits16, dev, stream, shapes, W,
                                   "byte_ratio": round(bf16_bytes / step_bytes, 3)}
     log(f"bf16 GEMV step {us_bf16:.1f} us")
 
-    # ---- small batch M in {4,8,16}, symmetric g32, rotating weight copies ------------
+    # ---- small batch M in {1,4,8,16}, symmetric g32, rotating weight copies ---------
     sym_w = {}
     for name, n, k in shapes:
         w, _ = synth.decode_case(name)
@@ -334,32 +431,35 @@ def run_extras(args, torch, B, O, synth, to_dev, bits16, dev, stream, shapes, W,
     return ex
 
 
-def cpu_baseline(args, O, synth, host, shapes, G):
-    """The oracle's W4A16 product (dequantize + float64 group-by-group matmul) on a
-    bounded sample of the decode workload: the first rows of each projection."""
+def cpu_baseline(args, O, host, shapes):
+    """The oracle's W4A16 product (dequantize + float64 group-by-group matmul, as
+    it stands) on a bounded sample of the decode workload: the first `rows`
+    output rows of each projection, repeated until about `cpu_seconds` of work."""
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    rows = 256
+    rows = 512
+    packed = {}
+    for name, n, k in shapes:
+        w, x = host[name]
+        codes, s, z = O.quantize_to_storage(w[:rows], 4, G, False)
+        packed[name] = (x, O.pack_int4(codes, False), s, z)
     done_bytes, t_total, passes = 0, 0.0, 0
-    while t_total < args.cpu_seconds and passes < 50:
+    while t_total < args.cpu_seconds:
         for name, n, k in shapes:
-            w, x = host[name]
+            x, qw, s, z = packed[name]
             t = time.perf_counter()
-            codes, s, z = O.quantize_to_storage(w[:rows], 4, G, False)
-            qw = O.pack_int4(codes, False)
-            tq = time.perf_counter()
             O.w4a16_reference(x, qw, s, z, G, False)
-            t_total += time.perf_counter() - tq
+            t_total += time.perf_counter() - t
             done_bytes += gemv_bytes(rows, k, G)
         passes += 1
     gbps = done_bytes / t_total / 1e9
-    return {"value": round(gbps, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {rows} rows of each of the 4 decode projections, {passes} passes, "
-                      f"{t_total:.1f} s of matmul (dequantize + float64 group-by-group product); "
-                      f"host has {os.cpu_count()} logical CPUs"}
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {rows} output rows of each of the 4 decode projections (M=1, asym g128), "
+                      f"{passes} passes, {t_total:.1f} s of oracle W4A16 product (dequantize + float64 "
+                      f"group-by-group matmul); host has {os.cpu_count()} logical CPUs"}
 
 
 if __name__ == "__main__":
