@@ -137,7 +137,9 @@ gq_status gq_w4a16_gemv(const uint16_t* x, int64_t M, int64_t K, const uint8_t* 
 /* Fused W4A16 GEMM for prefill-sized M (any M >= 1, built for M >= 64) on
  * bf16 MFMA [P1 sec.2; P3 "面试官追问" (weight-only quantization keeps the
  * FLOPs; prefill is compute-bound)].  Same arithmetic, arguments, layout and
- * errors as gq_w4a16_gemv except the M range. */
+ * errors as gq_w4a16_gemv except the M range; additionally UNSUPPORTED for
+ * K > 2^22.  The dequantized weight enters the bf16 MFMA as the exact integer
+ * q - z and the group scale is applied in fp32, so no weight is rounded. */
 gq_status gq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
                         const uint16_t* scales, const uint16_t* zeros, int64_t N, gq_qparams p,
                         uint16_t* y, void* stream);

@@ -70,3 +70,29 @@ def test_prefill_shapes_full_size(name):
     yb = bits16(y)[np.ix_(ms, rows)]
     # the max-error bound uses ||x||_inf of the whole activation
     assert_parity(yb, ref, O.bf16_to_f64(x), wh, f"gemm {name} M=2048 full, sampled")
+
+
+@pytest.mark.parametrize("G", [32, 128])
+def test_zero_scale_groups(G):
+    """Groups whose fp16 scale is 0 contribute nothing (x^ = 0 * (q - z) = 0),
+    including the first group of a column and runs of zero-scale groups; the
+    GEMM's running-scale accumulation must skip them exactly."""
+    M, N, K = 130, 260, 1024
+    w, _ = synth.weights(N, K, seed=31)
+    x, _ = synth.activations(M, K, seed=32, n_outlier_channels=4)
+    qw, s, z = _oracle_weights(w, G, False)
+    s = s.copy()
+    s[0, :] = 0                     # a whole column of zero scales
+    s[1, 0] = 0                     # the first group
+    s[2, 1:4] = 0                   # a run in the middle
+    s[3, -1] = 0                    # the last group
+    s[5::7, 2] = 0                  # scattered
+    y = B.gq_w4a16_gemm(bf16_dev(x), u8_dev(qw), f16_dev(s), f16_dev(z), G, False)
+    yv = B.gq_w4a16_gemv(bf16_dev(x[:3]), u8_dev(qw), f16_dev(s), f16_dev(z), G, False)
+    torch.cuda.synchronize()
+    ref = O.w4a16_reference(x, qw, s, z, G, False)
+    wh = O.dequantize_packed(qw, s, z, G, False)
+    assert np.all(ref[:, 0] == 0.0)
+    assert np.all(bits16(y)[:, 0] & 0x7FFF == 0)
+    assert_parity(bits16(y), ref, O.bf16_to_f64(x), wh, f"gemm zero-scale groups G={G}")
+    assert_parity(bits16(yv), ref[:3], O.bf16_to_f64(x[:3]), wh, f"gemv zero-scale groups G={G}")

@@ -5,196 +5,281 @@
 // ("量化：为何加速推理与精度权衡", follow-up questions: weight-only INT4 leaves the
 // matmul FLOPs unchanged; prefill is compute-bound).
 //
-// Precision: the dequantized weight S(q - z) is *not* rounded to bf16.  The
+// Precision: the dequantized weight S(q - z) is never rounded to bf16.  The
 // MFMA B operand is the exact small integer q - z (|q - z| <= 15 is exact in
-// bf16), products are exact in fp32, and each group's partial sum is scaled by
-// its fp16 scale in fp32: C += S[n,g] * (A_g . (q - z)_g).  The output is
+// bf16), so every product is exact in fp32, and the fp16 group scale is applied
+// in fp32.  To keep a single accumulator per output element, the accumulator
+// holds the running sum divided by the current group's scale,
+//   U_g = T_g / c_g,   T_g = sum_{g' <= g} S_g' P_g'   (P = unscaled group sum),
+// so the MFMAs of group g+1 accumulate P_{g+1} straight into it after one
+// rescale U <- U * (c_g / c_{g+1}) at the group boundary; at the end
+// T = U * c_last.  c_g is the group's scale, or the previous c when a scale is
+// 0 (that group's B operand is then zeroed).  Ratios of fp16 scales stay far
+// inside fp32 range, and each rescale adds one fp32 rounding.  The output is
 // rounded once to bf16 (nearest-even).
 //
-// Tiling: a 512-thread workgroup (8 wavefronts, 4 x 2) computes a 256 x 128
-// tile of Y; each wavefront a 64 x 64 block as 2 x 2 v_mfma_f32_32x32x16_bf16
-// tiles.  K advances in 64-wide tiles: the activation tile is copied to LDS,
-// the packed weight tile is expanded once per workgroup to exact bf16 (q - z)
-// in LDS (so 256 rows of X share each expansion), and global loads of the next
-// tile are in flight while the current one is multiplied.  With M = 2048 the 8
-// row tiles of a column of workgroups land on the 8 XCDs (workgroups are
-// dealt round-robin), so every XCD keeps one activation row-tile in its L2.
+// Tiling: a workgroup computes a (128 WM) x 256 tile of Y with WM x 4
+// wavefronts; each wavefront owns a 128 x 64 block as 4 x 2
+// v_mfma_f32_32x32x16_bf16 tiles.  K advances in 64-wide tiles through two LDS
+// stages: the activation tile is copied in (bf16, 144-byte padded rows), the
+// packed weight tile is expanded once per workgroup into exact bf16 (q - z), and
+// the tile's column scales are stored beside it.  Global loads run two tiles
+// ahead in registers; they are unconditional raw buffer loads (anything outside
+// the matrices reads as zero), so the compiler's wait counts stay exact.  With
+// workgroups dealt round-robin to the 8 XCDs and the M tile varying fastest,
+// each XCD keeps the same activation rows in its L2.
+#include <algorithm>
+
 #include "gq_internal.h"
 
 namespace gq {
 namespace {
 
-constexpr int kBM = 256, kBN = 128, kKT = 64;
-constexpr int kThreads = 512;
-constexpr int kLdsStride = kKT + 8;  // bf16 elements per LDS row (+16 B pad)
+constexpr int kBK = 64;
+constexpr int kLdsRow = kBK + 8;  // bf16 elements per LDS row (+16 B pad)
+constexpr int kBN = 256;
+constexpr uint32_t kOob = 0x80000000u;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-// 8 nibbles (k = 0..7 at bits 4p) -> 8 exact bf16 values (q - z) in k order,
-// as 4 dwords.  Bytes are biased by 128 so the per-byte subtraction never
-// borrows, flipped back to two's complement, widened to fp32 (exact), and the
-// upper halves of consecutive k are paired.
-__device__ __forceinline__ uint4 expand8(uint32_t d, uint32_t zb) {
-  uint32_t lo = ((d & 0x0F0F0F0Fu) | 0x80808080u) - zb;  // k = 0,2,4,6
-  uint32_t hi = (((d >> 4) & 0x0F0F0F0Fu) | 0x80808080u) - zb;  // k = 1,3,5,7
-  lo ^= 0x80808080u;
-  hi ^= 0x80808080u;
-  uint32_t f[8];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    f[2 * b] = __float_as_uint((float)(int8_t)(lo >> (8 * b)));
-    f[2 * b + 1] = __float_as_uint((float)(int8_t)(hi >> (8 * b)));
-  }
-  uint4 r;
-  r.x = __builtin_amdgcn_perm(f[1], f[0], 0x07060302u);
-  r.y = __builtin_amdgcn_perm(f[3], f[2], 0x07060302u);
-  r.z = __builtin_amdgcn_perm(f[5], f[4], 0x07060302u);
-  r.w = __builtin_amdgcn_perm(f[7], f[6], 0x07060302u);
-  return r;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane((uint32_t)std::min<uint64_t>(bytes, 0xFFFFFFFFull));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, (int)n,
+                                           0x00020000);
 }
 
-template <bool SYM>
-__global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint16_t bload2(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+__device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// two fp32 holding small integers -> packed bf16 pair (exact)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// 8 nibbles (k = 0..7 at bits 4p) -> 8 bf16 values q - z in k order (4 dwords).
+__device__ __forceinline__ uint4 expand8(uint32_t d, float z) {
+  const uint32_t e = d & 0x0F0F0F0Fu, o = (d >> 4) & 0x0F0F0F0Fu;
+  const float q0 = (float)(e & 0xFFu) - z, q2 = (float)((e >> 8) & 0xFFu) - z;
+  const float q4 = (float)((e >> 16) & 0xFFu) - z, q6 = (float)(e >> 24) - z;
+  const float q1 = (float)(o & 0xFFu) - z, q3 = (float)((o >> 8) & 0xFFu) - z;
+  const float q5 = (float)((o >> 16) & 0xFFu) - z, q7 = (float)(o >> 24) - z;
+  return make_uint4(pack_bf16(q0, q1), pack_bf16(q2, q3), pack_bf16(q4, q5), pack_bf16(q6, q7));
+}
+
+template <int WM, bool SYM>
+__global__ __launch_bounds__(256 * WM, 2) void w4a16_gemm_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
     uint16_t* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[kBM * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kBN * kLdsStride];
+  constexpr int BM = 128 * WM;
+  constexpr int NT = 256 * WM;
+  constexpr int A_CH = BM * kBK / 8 / NT;  // 16-byte activation chunks per thread (4)
+  constexpr int B_HALF = kBN * 2 / NT;     // 32-k column halves expanded per thread
+  extern __shared__ uint4 lds_raw[];
+  uint16_t* As = (uint16_t*)lds_raw;          // [2][BM][kLdsRow]
+  uint16_t* Bs = As + 2 * BM * kLdsRow;       // [2][kBN][kLdsRow]
+  float* Cs = (float*)(Bs + 2 * kBN * kLdsRow);  // [2][2][kBN] scales of the tile's groups
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 wavefronts
-  const int ntm = (M + kBM - 1) / kBM;
-  const int m0 = (blockIdx.x % ntm) * kBM;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
+  const int ntm = (M + BM - 1) / BM;
+  const int m0 = (blockIdx.x % ntm) * BM;
   const int n0 = (blockIdx.x / ntm) * kBN;
   const int ng = K / G;
-  const size_t row_bytes = (size_t)K / 2;
+  const uint32_t rb = (uint32_t)K / 2;
 
-  // --- global -> register prefetch of one K tile ---------------------------
-  // A: 256 rows x 128 B = 2048 chunks of 16 B, 4 per thread.
-  // B: 128 rows x 32 B packed, 8 B per thread (row tid/4, k-part tid%4).
-  uint4 ra[4];
-  uint2 rb;
-  uint32_t rz;
-  const int b_row = tid >> 2, b_part = tid & 3;
+  const rsrc_t rA = make_rsrc(x + (size_t)m0 * K, (uint64_t)(M - m0) * K * 2);
+  const rsrc_t rB = make_rsrc(qw + (size_t)n0 * rb, (uint64_t)(N - n0) * rb);
+  const rsrc_t rS = make_rsrc(scales + (size_t)n0 * ng, (uint64_t)(N - n0) * ng * 2);
+  const rsrc_t rZ = make_rsrc(SYM ? (const void*)scales : (const void*)(zeros + (size_t)n0 * ng),
+                              (uint64_t)(N - n0) * ng * 2);
 
-  auto load_tile = [&](int k0) {
+  const int lcol[2] = {wn * 64 + (lane & 31), wn * 64 + 32 + (lane & 31)};  // tile-local columns
+  struct Stage {
+    uint4 a[A_CH];
+    uint4 b[B_HALF];
+    uint16_t z[B_HALF], s[B_HALF];
+    uint16_t cs[2];  // scales of this lane's MFMA columns for the tile's first group
+  };
+  auto load_tile = [&](Stage& S, int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + i * kThreads;
+    for (int i = 0; i < A_CH; ++i) {
+      const int id = tid + i * NT;
       const int r = id >> 3, c = id & 7;
-      const int gm = m0 + r, gk = k0 + c * 8;
-      ra[i] = make_uint4(0, 0, 0, 0);
-      if (gm < M && gk < K) ra[i] = *(const uint4*)(x + (size_t)gm * K + gk);
+      const int gk = k0 + c * 8;
+      S.a[i] = bload16(rA, gk < K ? (uint32_t)(r * K + gk) * 2u : kOob);
     }
-    const int gn = n0 + b_row, gk = k0 + b_part * 16;
-    rb = make_uint2(0, 0);
-    rz = 0;
-    if (gn < N && gk < K) {
-      rb = *(const uint2*)(qw + gn * row_bytes + gk / 2);
-      const uint32_t z = SYM ? 8u : (uint32_t)f16_to_f32(zeros[(size_t)gn * ng + gk / G]);
-      rz = z * 0x01010101u;
+    const int g0 = __builtin_amdgcn_readfirstlane(k0 / G);
+    const int g1 = __builtin_amdgcn_readfirstlane((k0 + 32) / G);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) S.cs[j] = bload2(rS, k0 < K ? (uint32_t)(lcol[j] * ng + g0) * 2u : kOob);
+#pragma unroll
+    for (int h = 0; h < B_HALF; ++h) {
+      const int id = tid + h * NT;
+      const int col = id >> 1, half = id & 1;
+      const int gk = k0 + half * 32;
+      const bool kin = gk < K;
+      S.b[h] = bload16(rB, kin ? (uint32_t)col * rb + (uint32_t)gk / 2 : kOob);
+      const uint32_t go = kin ? (uint32_t)(col * ng + (half ? g1 : g0)) * 2u : kOob;
+      S.s[h] = bload2(rS, go);
+      if (!SYM) S.z[h] = bload2(rZ, go);
+    }
+  };
+  auto store_tile = [&](const Stage& S, int buf) {
+    uint16_t* as = As + buf * BM * kLdsRow;
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int id = tid + i * NT;
+      const int r = id >> 3, c = id & 7;
+      *(uint4*)&as[r * kLdsRow + c * 8] = S.a[i];
+    }
+#pragma unroll
+    for (int h = 0; h < B_HALF; ++h) {
+      const int id = tid + h * NT;
+      const int col = id >> 1, half = id & 1;
+      uint16_t* bs = Bs + (buf * kBN + col) * kLdsRow + half * 32;
+      const float zf = SYM ? 8.f : h2f(S.z[h]);
+      uint4 e0 = expand8(S.b[h].x, zf), e1 = expand8(S.b[h].y, zf);
+      uint4 e2 = expand8(S.b[h].z, zf), e3 = expand8(S.b[h].w, zf);
+      if ((S.s[h] & 0x7FFF) == 0) e0 = e1 = e2 = e3 = make_uint4(0, 0, 0, 0);  // S = 0: no contribution
+      *(uint4*)(bs + 0) = e0;
+      *(uint4*)(bs + 8) = e1;
+      *(uint4*)(bs + 16) = e2;
+      *(uint4*)(bs + 24) = e3;
+      Cs[(buf * 2 + half) * kBN + col] = h2f(S.s[h]);
     }
   };
 
-  auto store_tile = [&]() {
+  f32x16_t acc[4][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + i * kThreads;
-      const int r = id >> 3, c = id & 7;
-      *(uint4*)&As[r * kLdsStride + c * 8] = ra[i];
-    }
-    uint4 e0 = expand8(rb.x, rz);
-    uint4 e1 = expand8(rb.y, rz);
-    uint16_t* dst = &Bs[b_row * kLdsStride + b_part * 16];
-    *(uint4*)dst = e0;
-    *(uint4*)(dst + 8) = e1;
-  };
-
-  f32x16_t acc[2][2], part[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) { acc[i][j][v] = 0.f; part[i][j][v] = 0.f; }
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  float cref[2] = {1.f, 1.f};
 
-  const int ntiles = (K + kKT - 1) / kKT;
-  load_tile(0);
-  for (int t = 0; t < ntiles; ++t) {
-    const int k0 = t * kKT;
-    store_tile();
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(k0 + kKT);
-
-    // scales of the (at most two) groups this tile touches, per column block
-    float s_lo[2], s_hi[2];
+  // Rescale the running sum from the current group scale cref to scale s of
+  // the group that starts next (s = 0: that group is skipped, keep cref).
+  auto rescale = [&](const float (&s)[2]) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int gn = n0 + wn * 64 + j * 32 + (lane & 31);
-      const int g0 = k0 / G, g1 = (k0 + 32) / G;
-      s_lo[j] = 0.f;
-      s_hi[j] = 0.f;
-      if (gn < N) {
-        s_lo[j] = f16_to_f32(scales[(size_t)gn * ng + g0]);
-        if (k0 + 32 < K) s_hi[j] = f16_to_f32(scales[(size_t)gn * ng + g1]);
-      }
+      const float cn = s[j] != 0.f ? s[j] : cref[j];
+      const float r = cref[j] / cn;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] *= r;
+      cref[j] = cn;
     }
+  };
 
+  // nxt: the stage of tile t+1 (its first group's scales, for a boundary at the tile end)
+  auto compute_tile = [&](int t, const Stage& nxt) {
+    const int k0 = t * kBK;
+    const int cur = t & 1;
+    const uint16_t* as = As + (cur * BM + wm * 128 + (lane & 31)) * kLdsRow;
+    const uint16_t* bs = Bs + (cur * kBN + wn * 64 + (lane & 31)) * kLdsRow;
 #pragma unroll
-    for (int ks = 0; ks < kKT / 16; ++ks) {
+    for (int ks = 0; ks < kBK / 16; ++ks) {
       const int kk = ks * 16 + 8 * (lane >> 5);
-      bf16x8_t a[2], b[2];
+      bf16x8_t a[4], b[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint4 v = *(const uint4*)&As[(wm * 64 + i * 32 + (lane & 31)) * kLdsStride + kk];
-        a[i] = __builtin_bit_cast(bf16x8_t, v);
-      }
+      for (int i = 0; i < 4; ++i)
+        a[i] = __builtin_bit_cast(bf16x8_t, *(const uint4*)&as[i * 32 * kLdsRow + kk]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint4 v = *(const uint4*)&Bs[(wn * 64 + j * 32 + (lane & 31)) * kLdsStride + kk];
-        b[j] = __builtin_bit_cast(bf16x8_t, v);
-      }
+      for (int j = 0; j < 2; ++j)
+        b[j] = __builtin_bit_cast(bf16x8_t, *(const uint4*)&bs[j * 32 * kLdsRow + kk]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], part[i][j], 0, 0, 0);
-
-      // end of a group (or of K): fold the group's partial into the output
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
       const int kend = k0 + (ks + 1) * 16;
-      if ((kend % G) == 0 || kend >= K) {
-        const bool upper = (ks >= 2);
+      if ((ks == 1 || ks == 3) && kend % G == 0 && kend < K) {
+        float s[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const float s = upper ? s_hi[j] : s_lo[j];
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              acc[i][j][v] = fmaf(s, part[i][j][v], acc[i][j][v]);
-              part[i][j][v] = 0.f;
-            }
-        }
+        for (int j = 0; j < 2; ++j)
+          s[j] = ks == 1 ? Cs[(cur * 2 + 1) * kBN + lcol[j]] : h2f(nxt.cs[j]);
+        rescale(s);
       }
     }
+  };
+
+  const int ntiles = (K + kBK - 1) / kBK;
+  Stage s0, s1;
+  load_tile(s0, 0);
+  load_tile(s1, kBK);
+  store_tile(s0, 0);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float c0 = Cs[lcol[j]];
+    cref[j] = c0 != 0.f ? c0 : 1.f;
+  }
+  // Tile t sits in LDS; the stage holding tile t+1 is in flight; tile t+2 is
+  // issued into the stage just drained.  Loads past the end read zeros.
+  for (int t = 0; t < ntiles; t += 2) {
+    load_tile(s0, (t + 2) * kBK);
+    compute_tile(t, s1);
+    if (t + 1 < ntiles) store_tile(s1, 1);
+    __syncthreads();
+    if (t + 1 >= ntiles) break;
+    load_tile(s1, (t + 3) * kBK);
+    compute_tile(t + 1, s0);
+    if (t + 2 < ntiles) store_tile(s0, 0);
     __syncthreads();
   }
 
   // epilogue: lane holds column (lane & 31) and rows 8*(v/4) + 4*(lane/32) + v%4
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int gn = n0 + wn * 64 + j * 32 + (lane & 31);
+      const int gn = n0 + lcol[j];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int gm = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (gm < M && gn < N) y[(size_t)gm * N + gn] = f32_to_bf16_rne(acc[i][j][v]);
+        const int gm = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (gm < M && gn < N) y[(size_t)gm * N + gn] = f32_to_bf16_rne(acc[i][j][v] * cref[j]);
       }
     }
+}
+
+template <int WM, bool SYM>
+hipError_t launch_t(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
+                    const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
+  constexpr int BM = 128 * WM;
+  const int64_t grid = (int64_t)((M + BM - 1) / BM) * ((N + kBN - 1) / kBN);
+  const size_t lds = (size_t)2 * (BM + kBN) * kLdsRow * 2 + (size_t)2 * 2 * kBN * 4;
+  hipLaunchKernelGGL((w4a16_gemm_kernel<WM, SYM>), dim3((unsigned)grid), dim3(256 * WM), lds, s, x, M,
+                     K, qw, sc, zr, N, G, y);
+  return hipGetLastError();
+}
+
+template <bool SYM>
+hipError_t dispatch(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
+                    const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
+  // 256-row tiles run two waves per SIMD; the 128-row tile (one wave per SIMD)
+  // only pays off when the larger tile would leave most compute units idle.
+  const int64_t tiles256 = (int64_t)((M + 255) / 256) * ((N + kBN - 1) / kBN);
+  if (2 * tiles256 >= num_cus()) return launch_t<2, SYM>(x, M, K, qw, sc, zr, N, G, y, s);
+  return launch_t<1, SYM>(x, M, K, qw, sc, zr, N, G, y, s);
 }
 
 }  // namespace
@@ -202,15 +287,9 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(
 hipError_t launch_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
                              const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
                              int symmetric, uint16_t* y, hipStream_t s) {
-  const int64_t ntm = (M + kBM - 1) / kBM, ntn = (N + kBN - 1) / kBN;
-  const dim3 grid((unsigned)(ntm * ntn));
   if (symmetric)
-    hipLaunchKernelGGL(w4a16_gemm_kernel<true>, grid, dim3(kThreads), 0, s, x, (int)M, (int)K,
-                       qweight, scales, zeros, (int)N, G, y);
-  else
-    hipLaunchKernelGGL(w4a16_gemm_kernel<false>, grid, dim3(kThreads), 0, s, x, (int)M, (int)K,
-                       qweight, scales, zeros, (int)N, G, y);
-  return hipGetLastError();
+    return dispatch<true>(x, (int)M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
+  return dispatch<false>(x, (int)M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
 }
 
 }  // namespace gq

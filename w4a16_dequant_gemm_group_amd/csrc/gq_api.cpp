@@ -37,6 +37,8 @@ gq_status from_hip(hipError_t e) { return e == hipSuccess ? GQ_OK : GQ_ERR_HIP; 
 bool valid_dtype(gq_dtype d) { return d == GQ_F32 || d == GQ_F16 || d == GQ_BF16; }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
+// The GEMM addresses a 256-row activation tile with 32-bit byte offsets.
+constexpr int64_t kMaxGemmK = (int64_t)1 << 22;
 
 // Shape/group checks common to everything that reads or writes groups.
 gq_status check_groups(int64_t N, int64_t K, int32_t G) {
@@ -162,6 +164,7 @@ gq_status gq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* 
                         const uint16_t* scales, const uint16_t* zeros, int64_t N, gq_qparams p,
                         uint16_t* y, void* stream) {
   if (gq_status s = check_w4_matmul(x, M, K, qweight, scales, zeros, N, p, y)) return s;
+  if (K > kMaxGemmK || M > kMaxDim / 2) return GQ_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return GQ_OK;
   hipStream_t s = (hipStream_t)stream;
   if (gq_status st = check_device(s)) return st;
