@@ -176,6 +176,10 @@ def main():
             for nm, _, _ in shapes:
                 qw, s, z = W[nm]
                 B.gq_w4a16_gemv(X[nm], qw, s, z, G, False, y=Y[nm])
+        for nm, n, k in shapes:   # one prefill GEMM per projection (M = 2048)
+            _, xb = synth.prefill_case(nm)
+            qw, s, z = W[nm]
+            B.gq_w4a16_gemm(to_dev(xb), qw, s, z, G, False)
         a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
         torch.neg(a, out=b)
