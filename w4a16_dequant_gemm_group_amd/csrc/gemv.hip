@@ -272,9 +272,11 @@ __device__ __forceinline__ float wave_sum_to_lane63(float v) {
   return v;
 }
 
+// Scale and zero stay 16-bit in registers: widening them where the loop
+// carries them would force a wait on every outstanding load.
 struct StreamBuf {
   uint4 w[kSRpw];
-  uint32_t s[kSRpw], z[kSRpw];
+  uint16_t s[kSRpw], z[kSRpw];
 };
 
 struct Cursor {
@@ -308,8 +310,8 @@ __device__ __forceinline__ void stream_load(StreamBuf& B, Cursor c, int N, uint3
     const uint32_t row = (uint32_t)min(c.b * kSRpw + r, N);  // row N reads out of range
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, ow, row * rb + uw, 2);
     B.w[r] = make_uint4(v[0], v[1], v[2], v[3]);
-    B.s[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, os, row * ngb + us, 0);
-    if (!SYM) B.z[r] = __builtin_amdgcn_raw_buffer_load_b16(rz, os, row * ngb + us, 0);
+    B.s[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, os, row * ngb + us, 2);
+    if (!SYM) B.z[r] = __builtin_amdgcn_raw_buffer_load_b16(rz, os, row * ngb + us, 2);
   }
 }
 
@@ -322,8 +324,8 @@ __device__ __forceinline__ void stream_compute(const StreamBuf& B, Cursor c, int
 #pragma unroll
     for (int r = 0; r < kSRpw; ++r) acc[r] = 0.f;
   }
-  const uint4* xp = xs + c.p * 256 + lane * 4;
-  const uint4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
+  const uint4* xp = xs + c.p * 256 + lane;
+  const uint4 x0 = xp[0], x1 = xp[64], x2 = xp[128], x3 = xp[192];
   const float sx = sxs[c.p * 64 + lane];
   const float init = -128.f * sx;
 #pragma unroll
@@ -354,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(
     uint16_t* __restrict__ y) {
   extern __shared__ uint4 lds[];
   const int T = (K + kStepK - 1) / kStepK;
-  uint4* xs = lds;                                      // [T * 256] permuted x pairs
+  uint4* xs = lds;                                      // [T][4][64] permuted x pairs
   float* sxs = (float*)(xs + T * 256);                  // [T * 64] chunk sums
   uint32_t* wtab = (uint32_t*)(sxs + T * 64);           // [T * 64] (TAB only)
   uint32_t* stab = wtab + T * 64;                       // [T * 64] (TAB only)
@@ -413,7 +415,10 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(
         if (c < T * 256 && c * 8 < K) v = *(const uint4*)(x + c * 8);
       }
       if (c0 + kThreads * i < T * 256) {  // uniform over the block
-        xs[c] = perm_x_pairs(v);
+        // chunk c = 8 x values; lane l of step p reads its four chunks at
+        // p*256 + j*64 + l (j = 0..3), so the 16-byte LDS reads of a wave are
+        // consecutive and free of bank conflicts
+        xs[(c & ~255) | ((c & 3) << 6) | ((c >> 2) & 63)] = perm_x_pairs(v);
         float sm = sum_bf16x8(v);
         sm += __shfl_xor(sm, 1, 64);
         sm += __shfl_xor(sm, 2, 64);
