@@ -134,6 +134,29 @@ gq_status gq_w4a16_gemv(const uint16_t* x, int64_t M, int64_t K, const uint8_t* 
                         const uint16_t* scales, const uint16_t* zeros, int64_t N, gq_qparams p,
                         uint16_t* y, void* stream);
 
+/* Scratch (bytes) that gq_w4a16_gemv_ws needs for these arguments, 0 when the
+ * call runs without any.  With 4 <= M <= 16 (group_size 32, 64 or a multiple of
+ * 128, K % 256 == 0) the GEMV runs on the matrix cores
+ * split along K into 1024-wide slices and keeps fp32 partial sums per slice:
+ * ceil(K / 1024) * M * N * 4 bytes.  Errors: those of gq_w4a16_gemv's argument
+ * checks; INVALID_ARG for a NULL `bytes`. */
+gq_status gq_w4a16_gemv_workspace_size(int64_t M, int64_t K, int64_t N, gq_qparams p,
+                                       size_t* bytes);
+
+/* gq_w4a16_gemv with caller-provided scratch, for callers that manage device
+ * memory themselves (e.g. under stream capture).  workspace: device memory of
+ * at least gq_w4a16_gemv_workspace_size() bytes, 16-byte aligned (NULL allowed
+ * when that size is 0); it is written by this call's kernels on `stream` and
+ * must not be touched by other work until they complete.  The plain
+ * gq_w4a16_gemv keeps such scratch per (device, stream) inside the library and,
+ * while its stream is being captured and none is available, runs the
+ * dot-product kernel instead.  Errors: those of gq_w4a16_gemv, and
+ * INVALID_ARG when a needed workspace is NULL or smaller than required. */
+gq_status gq_w4a16_gemv_ws(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                           const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                           gq_qparams p, uint16_t* y, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* Fused W4A16 GEMM for prefill-sized M (any M >= 1, built for M >= 64) on
  * bf16 MFMA [P1 sec.2; P3 "面试官追问" (weight-only quantization keeps the
  * FLOPs; prefill is compute-bound)].  Same arithmetic, arguments, layout and

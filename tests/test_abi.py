@@ -27,7 +27,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     assert set(names) == set(B.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -109,3 +109,27 @@ def test_other_entry_point_validation(lib):
     assert L.gq_q4k_quantize(FAKE, B.GQ_BF16, 4, 300, FAKE, None) == B.GQ_ERR_INVALID_ARG
     assert L.gq_q4k_gemv(FAKE, 1, 512, FAKE_MIS, 4, FAKE, None) == B.GQ_ERR_MISALIGNED
     assert L.gq_q4k_gemv(FAKE, 17, 512, FAKE, 4, FAKE, None) == B.GQ_ERR_INVALID_ARG
+
+
+def test_gemv_workspace_size_and_validation(lib):
+    # the matrix-core path (4 <= M <= 16, G in {32, 64, 128k}, K % 256 == 0)
+    # keeps ceil(K / 1024) * M * N fp32 partial sums; other calls need none
+    assert B.gq_w4a16_gemv_workspace_size(16, 14336, 4096, 32, True) == 14 * 16 * 4096 * 4
+    assert B.gq_w4a16_gemv_workspace_size(8, 6400, 203, 128) == 7 * 8 * 203 * 4
+    assert B.gq_w4a16_gemv_workspace_size(4, 4096, 4096, 128) == 4 * 4 * 4096 * 4
+    assert B.gq_w4a16_gemv_workspace_size(3, 4096, 4096, 128) == 0
+    assert B.gq_w4a16_gemv_workspace_size(1, 4096, 4096, 128) == 0
+    assert B.gq_w4a16_gemv_workspace_size(8, 6528, 203, 128) == 0   # K % 256 != 0
+    assert B.gq_w4a16_gemv_workspace_size(8, 6528, 203, 96) == 0    # G outside 32, 64, 128k
+    nbytes = ctypes.c_size_t()
+    assert lib.gq_w4a16_gemv_workspace_size(17, 4096, 64, q(), ctypes.byref(nbytes)) == B.GQ_ERR_INVALID_ARG
+    assert lib.gq_w4a16_gemv_workspace_size(8, 4096, 64, q(g=48), ctypes.byref(nbytes)) == B.GQ_ERR_INVALID_ARG
+    assert lib.gq_w4a16_gemv_workspace_size(8, 4096, 64, q(), None) == B.GQ_ERR_INVALID_ARG
+    # a needed workspace that is missing, too small or misaligned is rejected before any device call
+    need = B.gq_w4a16_gemv_workspace_size(8, 4096, 4096, 128)
+    args = (FAKE, 8, 4096, FAKE, FAKE, FAKE, 4096, q(), FAKE)
+    assert lib.gq_w4a16_gemv_ws(*args, None, need, None) == B.GQ_ERR_INVALID_ARG
+    assert lib.gq_w4a16_gemv_ws(*args, FAKE, need - 4, None) == B.GQ_ERR_INVALID_ARG
+    assert lib.gq_w4a16_gemv_ws(*args, FAKE_MIS, need, None) == B.GQ_ERR_MISALIGNED
+    # the plain GEMV checks still apply
+    assert lib.gq_w4a16_gemv_ws(FAKE, 17, 4096, FAKE, FAKE, FAKE, 4096, q(), FAKE, FAKE, need, None) == B.GQ_ERR_INVALID_ARG

@@ -53,6 +53,17 @@ def test_small_shapes(M, sym, G):
     _run(x, qw, s, z, G, sym, f"[203,{K}] M={M} sym={sym} G={G}")
 
 
+@pytest.mark.parametrize("M", [4, 5, 8, 9, 16])
+@pytest.mark.parametrize("sym,G", [(True, 32), (False, 64), (False, 128), (False, 256), (True, 512)])
+def test_small_batch_matrix_core_shapes(M, sym, G):
+    # the split-K matrix-core path (4 <= M <= 16, K % 256 == 0): K ends inside
+    # a 1024-wide slice and N = 203 leaves a partial 64-row group
+    K = 6656 if G == 512 else 6400
+    w, x = synth.small(203, K, M, seed=M * 13 + G)
+    qw, s, z = _oracle_weights(w, G, sym)
+    _run(x, qw, s, z, G, sym, f"[203,{K}] M={M} sym={sym} G={G} (matrix cores)")
+
+
 @pytest.mark.parametrize("K", [32, 96, 2048, 2080, 16384, 18432])
 def test_k_extents(K):
     # one lane's worth of k up to more than one LDS chunk (8 steps) of k
@@ -94,7 +105,7 @@ def test_decode_shapes_full_size(name):
     assert_parity(bits16(y)[:, rows], ref, O.bf16_to_f64(x), wh, f"{name} {w.shape} M=1 full, sampled")
 
 
-@pytest.mark.parametrize("M", [4, 16])
+@pytest.mark.parametrize("M", [4, 8, 16])
 def test_small_batch_full_size_sym_g32(M):
     w, _ = synth.decode_case("down")
     x, _ = synth.activations(M, w.shape[1], seed=2003)
@@ -132,3 +143,42 @@ def test_misaligned_pointer_rejected():
     with pytest.raises(B.GqError) as e:
         B.gq_w4a16_gemv(xd, u8_dev(qw), f16_dev(s), f16_dev(z), 128, False)
     assert e.value.status == B.GQ_ERR_MISALIGNED
+
+
+def test_workspace_entry_point_and_graph_replays():
+    # gq_w4a16_gemv_ws (caller scratch) and gq_w4a16_gemv (library scratch) run
+    # the same kernels: identical bits.  Captured into a graph, the call gets its
+    # scratch from torch's allocator and every replay must reproduce the eager
+    # result, with other eager work on the stream between replays.
+    M, K, N, G = 12, 4096, 1000, 32
+    w, x = synth.small(N, K, M, seed=77)
+    qw, s, _ = _oracle_weights(w, G, True)
+    xd, qd, sd = bf16_dev(x), u8_dev(qw), f16_dev(s)
+    need = B.gq_w4a16_gemv_workspace_size(M, K, N, G, True)
+    assert need == 4 * M * N * 4
+    y_lib = B.gq_w4a16_gemv(xd, qd, sd, None, G, True)
+    ws = torch.zeros(need + 64, dtype=torch.uint8, device=xd.device)
+    y_ws = B.gq_w4a16_gemv(xd, qd, sd, None, G, True, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y_lib, y_ws)
+    ref = O.w4a16_reference(x, qw, s, None, G, True)
+    wh = O.dequantize_packed(qw, s, None, G, True)
+    assert_parity(bits16(y_ws), ref, O.bf16_to_f64(x), wh, f"[{N},{K}] M={M} sym g32 via workspace")
+
+    y_g = torch.empty_like(y_lib)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        B.gq_w4a16_gemv(xd, qd, sd, None, G, True, y=y_g)  # warm-up on the capture stream
+        with torch.cuda.graph(g, stream=stream):
+            B.gq_w4a16_gemv(xd, qd, sd, None, G, True, y=y_g)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        y_g.zero_()
+        g.replay()
+        other = B.gq_w4a16_gemv(xd[:5], qd, sd, None, G, True)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_lib), f"replay {rep}"
+        assert other.shape == (5, N)

@@ -23,7 +23,8 @@ GQ_F32, GQ_F16, GQ_BF16 = 0, 1, 2
 # Every entry point declared in include/gq.h.
 EXPORTS = (
     "gq_status_str", "gq_version", "gq_packed_sizes", "gq_quantize_groups", "gq_pack_int4",
-    "gq_dequantize", "gq_w4a16_gemv", "gq_w4a16_gemm", "gq_q4k_quantize", "gq_q4k_gemv",
+    "gq_dequantize", "gq_w4a16_gemv", "gq_w4a16_gemv_workspace_size", "gq_w4a16_gemv_ws",
+    "gq_w4a16_gemm", "gq_q4k_quantize", "gq_q4k_gemv",
 )
 
 
@@ -61,6 +62,8 @@ def lib() -> ctypes.CDLL:
         "gq_pack_int4": [p, i64, i64, i32, p, p],
         "gq_dequantize": [p, p, p, i64, i64, Q, p, c, p],
         "gq_w4a16_gemv": [p, i64, i64, p, p, p, i64, Q, p, p],
+        "gq_w4a16_gemv_workspace_size": [i64, i64, i64, Q, ctypes.POINTER(ctypes.c_size_t)],
+        "gq_w4a16_gemv_ws": [p, i64, i64, p, p, p, i64, Q, p, p, ctypes.c_size_t, p],
         "gq_w4a16_gemm": [p, i64, i64, p, p, p, i64, Q, p, p],
         "gq_q4k_quantize": [p, c, i64, i64, p, p],
         "gq_q4k_gemv": [p, i64, i64, p, i64, p, p],
@@ -182,11 +185,45 @@ def _matmul(fn, name, x, qweight, scales, zeros, group_size, symmetric, y, strea
     return y
 
 
+def gq_w4a16_gemv_workspace_size(M: int, K: int, N: int, group_size: int = 128,
+                                 symmetric: bool = False) -> int:
+    """Bytes of scratch gq_w4a16_gemv_ws needs (0: none)."""
+    b = ctypes.c_size_t()
+    _check(lib().gq_w4a16_gemv_workspace_size(M, K, N, qparams(4, group_size, symmetric),
+                                              ctypes.byref(b)), "gq_w4a16_gemv_workspace_size")
+    return int(b.value)
+
+
 def gq_w4a16_gemv(x, qweight, scales, zeros, group_size: int = 128, symmetric: bool = False,
-                  y=None, stream=None):
-    """Fused W4A16 GEMV, x bf16 [M<=16, K] -> y bf16 [M, N]."""
-    return _matmul(lib().gq_w4a16_gemv, "gq_w4a16_gemv", x, qweight, scales, zeros,
-                   group_size, symmetric, y, stream)
+                  y=None, stream=None, workspace=None):
+    """Fused W4A16 GEMV, x bf16 [M<=16, K] -> y bf16 [M, N].
+
+    When the call needs scratch (gq_w4a16_gemv_workspace_size > 0) it is taken
+    from torch's allocator on the call's stream (or `workspace`, a uint8 GPU
+    tensor) and passed to gq_w4a16_gemv_ws, so the call is also safe under
+    stream capture."""
+    _need(x, "x", (torch.bfloat16,))
+    M, K = x.shape
+    N = qweight.shape[0]
+    need = gq_w4a16_gemv_workspace_size(M, K, N, group_size, symmetric) if M <= 16 else 0
+    if need == 0 and workspace is None:
+        return _matmul(lib().gq_w4a16_gemv, "gq_w4a16_gemv", x, qweight, scales, zeros,
+                       group_size, symmetric, y, stream)
+    if workspace is None:
+        # allocated on the call's stream, so the allocator hands this memory to
+        # other work only after the call's kernels on that stream
+        if stream is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        else:
+            with torch.cuda.stream(stream):
+                workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _need(workspace, "workspace", (torch.uint8,), x.device)
+    ws, nbytes = workspace, workspace.numel()
+
+    def fn(*a):
+        return lib().gq_w4a16_gemv_ws(*a[:9], _ptr(ws), nbytes, a[9])
+    return _matmul(fn, "gq_w4a16_gemv_ws", x, qweight, scales, zeros, group_size, symmetric,
+                   y, stream)
 
 
 def gq_w4a16_gemm(x, qweight, scales, zeros, group_size: int = 128, symmetric: bool = False,

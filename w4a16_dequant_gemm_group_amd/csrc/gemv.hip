@@ -475,10 +475,18 @@ hipError_t stream_m1(const uint16_t* x, int K, const uint8_t* qw, const uint16_t
 
 hipError_t launch_w4a16_gemv(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
                              const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
-                             int symmetric, uint16_t* y, hipStream_t s) {
+                             int symmetric, uint16_t* y, void* workspace, size_t ws_bytes,
+                             hipStream_t s) {
   if (M == 1 && (K + kStepK - 1) / kStepK <= kSMaxT) {
     if (symmetric) return stream_m1<true>(x, (int)K, qweight, scales, zeros, (int)N, G, y, s);
     return stream_m1<false>(x, (int)K, qweight, scales, zeros, (int)N, G, y, s);
+  }
+  if (gemv_mfma_supported(M, K, N, G)) {
+    (void)ws_bytes;  // checked against gemv_workspace_bytes by the caller
+    bool launched = false;
+    const hipError_t e = launch_w4a16_gemv_mfma(x, M, K, qweight, scales, zeros, N, G, symmetric,
+                                                y, workspace, s, &launched);
+    if (e != hipSuccess || launched) return e;
   }
   if (symmetric) return dispatch<true>(x, M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
   return dispatch<false>(x, M, (int)K, qweight, scales, zeros, (int)N, G, y, s);

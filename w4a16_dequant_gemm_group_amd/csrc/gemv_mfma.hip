@@ -1,0 +1,358 @@
+// Small-batch W4A16 GEMV (4 <= M <= 16) on bf16 MFMA, split along K.
+//
+// Same product as the streaming GEMV ("vLLM 量化与推测解码" section 2, fused
+// W4A16 paragraph; "量化" page, "工作原理" figure right panel):
+//   y[m, n] = bf16( sum_g S[n,g] * sum_{k in g} x[m,k] * (q[n,k] - z[n,g]) ).
+// With M activation rows the dot-product form costs M times the vector ALU work
+// per weight, so here the weights become the B operand of
+// v_mfma_f32_16x16x32_bf16 and the activations its A operand: the matrix core
+// multiplies all M rows at the cost of one.
+//
+// Operand construction (per 16-row block of W and 128-wide step of K):
+//  * lane (n, g) = (lane & 15, lane >> 4) loads 16 bytes of weight row n at
+//    k = k0 + 32 g, i.e. the four 8-nibble dwords of one 32-wide chunk;
+//  * a 4 x 4 transpose across the lane rows (v_permlane16/32_swap) gives lane
+//    (n, g) dword g of every chunk c, so MFMA c covers exactly the 32-wide
+//    chunk c, which lies in one quantization group for any group size that is
+//    a multiple of 32;
+//  * each dword becomes four bf16 pairs 128 + q (the nibble under exponent
+//    byte 0x43, exact) in the order (0,2)(4,6)(1,3)(5,7); the activations are
+//    staged in LDS permuted the same way;
+//  * per group segment, the offset and zero point are removed with the chunk
+//    sums of x and the scale applied in fp32:
+//      acc[m][n] += S * (D[m][n] - (128 + z) * sum_{k in segment} x[m][k]).
+// A workgroup (4 waves, 64 rows) covers a 1024-wide slice of K and writes fp32
+// partial sums; a second kernel adds the slices in a fixed order (so the result
+// does not depend on scheduling) and rounds once to bf16 (nearest-even).
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "gq_internal.h"
+
+namespace gq {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr int kKC = 1024;            // K covered by one workgroup
+constexpr int kXRow = kKC / 8 + 1;   // 16-byte chunks per staged x row (+1 pad: no bank conflicts)
+constexpr uint32_t kOob = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, (int)n,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// x0..x7 (bf16) -> pairs (x0,x2) (x4,x6) (x1,x3) (x5,x7)
+__device__ __forceinline__ uint4 perm_x(uint4 v) {
+  return make_uint4(__builtin_amdgcn_perm(v.y, v.x, 0x05040100u),
+                    __builtin_amdgcn_perm(v.w, v.z, 0x05040100u),
+                    __builtin_amdgcn_perm(v.y, v.x, 0x07060302u),
+                    __builtin_amdgcn_perm(v.w, v.z, 0x07060302u));
+}
+
+// 8 nibbles -> bf16 128 + q in the same pair order
+__device__ __forceinline__ uint4 unpack8(uint32_t e, uint32_t magic) {
+  const uint32_t ev = e & 0x0F0F0F0Fu, od = (e >> 4) & 0x0F0F0F0Fu;
+  return make_uint4(__builtin_amdgcn_perm(ev, magic, 0x01050104u),
+                    __builtin_amdgcn_perm(ev, magic, 0x01070106u),
+                    __builtin_amdgcn_perm(od, magic, 0x01050104u),
+                    __builtin_amdgcn_perm(od, magic, 0x01070106u));
+}
+
+// out[c] at lane row g = in[g] at lane row c (rows of 16 lanes)
+__device__ __forceinline__ void transpose4(uint32_t& d0, uint32_t& d1, uint32_t& d2, uint32_t& d3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(d0, d2, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(d1, d3, false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  d0 = c[0];
+  d1 = c[1];
+  d2 = d[0];
+  d3 = d[1];
+}
+
+// CPG: 32-wide chunks per correction segment (1: G = 32, 2: G = 64, 4: G a
+// multiple of 128).  MR: activation rows staged (>= M; 4, 8 or 16).  Requires
+// N * K / 2 and M * K * 2 below 2^31 (byte offsets of the buffer loads).
+// G = 32 needs about 400 registers per lane without spilling: one wave per SIMD.
+template <int CPG, bool SYM, int MR>
+__global__ __launch_bounds__(256, CPG == 1 ? 1 : 2) void gemv_mfma_tile_kernel(
+    const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
+    float* __restrict__ part) {
+  __shared__ uint4 xs[MR * kXRow];     // x[m][k0 .. k0 + 1024) as permuted 8-chunks
+  __shared__ float sxs[kKC / 32][16];  // per 32-chunk and row m: sum of x (0 for m >= MR)
+  // G = 32: per wave, scale | zero << 16 of its 16 rows x 32 groups (registers would spill)
+  __shared__ uint32_t meta[CPG == 1 ? 4 : 1][16][32];
+  constexpr int GPS = 4 / CPG;         // groups per 128-wide step
+  constexpr int XJ = MR * 128 / 256;   // x chunks staged per thread
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int split = blockIdx.y;
+  const int k0 = split * kKC;
+  const int row = blockIdx.x * 64 + w * 16 + n;  // this lane's weight row
+  const bool rin = row < N;
+  const int NG = K / G;
+  const uint32_t rb = (uint32_t)K / 2;
+  const rsrc_t rx = make_rsrc(x, (uint32_t)M * K * 2);
+  const rsrc_t rw = make_rsrc(qw, (uint32_t)N * rb);
+  const rsrc_t rs = make_rsrc(scales, (uint32_t)N * NG * 2);
+  const rsrc_t rz = make_rsrc(SYM ? (const void*)scales : (const void*)zeros, (uint32_t)N * NG * 2);
+
+  // 1. activations (rows >= M and k >= K read zero)
+  uint4 xv[XJ];
+#pragma unroll
+  for (int j = 0; j < XJ; ++j) {
+    const int id = threadIdx.x + 256 * j;
+    const int m = id >> 7, c = id & 127;
+    const int k = k0 + c * 8;
+    const uint32_t off = (m < M && k < K) ? (uint32_t)(m * K + k) * 2u : kOob;
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+    xv[j] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+  // 2. scales and zeros of row `row` for the 8 steps (GPS consecutive groups
+  //    each); for G = 32 one 16-byte load per lane covers the wave's 16 rows x 32
+  //    groups (lane l: row l / 4, groups 8 (l % 4) ..) and goes through LDS
+  uint32_t ms[8], mz[8];
+  uint4 gs4 = make_uint4(0, 0, 0, 0), gz4 = make_uint4(0, 0, 0, 0);
+  if (GPS == 4) {
+    const int mrow = blockIdx.x * 64 + w * 16 + (lane >> 2);
+    const int gq = k0 / 32 + 8 * (lane & 3);
+    const uint32_t off = (mrow < N && gq < NG) ? ((uint32_t)mrow * NG + gq) * 2u : kOob;
+    const auto a = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    gs4 = make_uint4(a[0], a[1], a[2], a[3]);
+    if (!SYM) {
+      const auto b = __builtin_amdgcn_raw_buffer_load_b128(rz, off, 0, 0);
+      gz4 = make_uint4(b[0], b[1], b[2], b[3]);
+    }
+  } else {
+#pragma unroll
+    for (int L = 0; L < 8; ++L) {
+      const int k = k0 + 128 * L;
+      const uint32_t off = (rin && k < K) ? ((uint32_t)row * NG + k / G) * 2u : kOob;
+      mz[L] = 0u;
+      if (GPS == 1) {
+        ms[L] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
+        if (!SYM) mz[L] = __builtin_amdgcn_raw_buffer_load_b16(rz, off, 0, 0);
+      } else {
+        ms[L] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+        if (!SYM) mz[L] = __builtin_amdgcn_raw_buffer_load_b32(rz, off, 0, 0);
+      }
+    }
+  }
+  // 3. weights: lane (n, g) reads 16 bytes of row `row` at k = k0 + 128 L + 32 g
+  uint4 wv[8];
+  const uint32_t wrow = (uint32_t)row * rb + (uint32_t)(k0 + 32 * g) / 2;
+#pragma unroll
+  for (int L = 0; L < 8; ++L) {
+    const bool ok = rin && k0 + 128 * L + 32 * g < K;
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? wrow + 64 * L : kOob, 0, 2);
+    wv[L] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+  // 4. stage x and its 32-chunk sums (the 4 chunks of a 32-chunk sit in
+  //    consecutive lanes: two quad-permute adds)
+#pragma unroll
+  for (int j = 0; j < XJ; ++j) {
+    const int id = threadIdx.x + 256 * j;
+    const int m = id >> 7, c = id & 127;
+    const uint4 v = xv[j];
+    xs[m * kXRow + c] = perm_x(v);
+    float s = dot2(v.x, 0x3F803F80u, 0.f);  // bf16 1.0 pairs
+    s = dot2(v.y, 0x3F803F80u, s);
+    s = dot2(v.z, 0x3F803F80u, s);
+    s = dot2(v.w, 0x3F803F80u, s);
+    s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0xB1,
+                                                               0xF, 0xF, true));
+    s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x4E,
+                                                               0xF, 0xF, true));
+    if ((c & 3) == 0) sxs[c >> 2][m] = s;
+  }
+  if (MR < 16) {
+    for (int i = threadIdx.x; i < (kKC / 32) * (16 - MR); i += 256)
+      sxs[i / (16 - MR)][MR + i % (16 - MR)] = 0.f;
+  }
+  if (GPS == 4) {
+    const uint32_t sv[4] = {gs4.x, gs4.y, gs4.z, gs4.w}, zv[4] = {gz4.x, gz4.y, gz4.z, gz4.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[2 * j] = __builtin_amdgcn_perm(zv[j], sv[j], 0x05040100u);      // (s, z) of group 2j
+      o[2 * j + 1] = __builtin_amdgcn_perm(zv[j], sv[j], 0x07060302u);  // (s, z) of group 2j + 1
+    }
+    uint32_t* dst = &meta[GPS == 4 ? w : 0][lane >> 2][8 * (lane & 3)];
+    *(uint4*)dst = make_uint4(o[0], o[1], o[2], o[3]);
+    *(uint4*)(dst + 4) = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+  __syncthreads();
+
+  // 5. MFMAs and per-segment corrections; lane (n, g) accumulates rows m = 4g + r
+  const uint32_t magic = 0x43004300u;
+  const int xrow = (n % MR) * kXRow;  // A row of this lane (rows >= M are dropped at the end)
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t D = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int L = 0; L < 8; ++L) {
+    uint32_t e0 = wv[L].x, e1 = wv[L].y, e2 = wv[L].z, e3 = wv[L].w;
+    transpose4(e0, e1, e2, e3);
+    const uint32_t ev[4] = {e0, e1, e2, e3};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 A = xs[xrow + 16 * L + 4 * c + g];
+      const uint4 B = unpack8(ev[c], magic);
+      const f32x4_t Cin = (c % CPG == 0) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : D;
+      D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A),
+                                                  __builtin_bit_cast(bf16x8_t, B), Cin, 0, 0, 0);
+      if (c % CPG == CPG - 1) {
+        uint32_t sb, zb;
+        if (GPS == 1) {
+          sb = ms[L];
+          zb = mz[L];
+        } else if (GPS == 2) {
+          sb = ms[L] >> (16 * (c / 2));
+          zb = mz[L] >> (16 * (c / 2));
+        } else {
+          sb = meta[GPS == 4 ? w : 0][n][4 * L + c];
+          zb = sb >> 16;
+        }
+        const float s = f16_to_f32((uint16_t)sb);
+        const float zc = 128.f + (SYM ? 8.f : f16_to_f32((uint16_t)zb));
+        const int ch = 4 * L + c;  // last 32-chunk of the segment
+        float4 sx = *(const float4*)&sxs[ch][4 * g];
+#pragma unroll
+        for (int q = 1; q < CPG; ++q) {
+          const float4 t = *(const float4*)&sxs[ch - q][4 * g];
+          sx.x += t.x;
+          sx.y += t.y;
+          sx.z += t.z;
+          sx.w += t.w;
+        }
+        acc[0] = fmaf(s, fmaf(-zc, sx.x, D[0]), acc[0]);
+        acc[1] = fmaf(s, fmaf(-zc, sx.y, D[1]), acc[1]);
+        acc[2] = fmaf(s, fmaf(-zc, sx.z, D[2]), acc[2]);
+        acc[3] = fmaf(s, fmaf(-zc, sx.w, D[3]), acc[3]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep each step's fragments short-lived
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * g + r;
+    if (m < M && rin) part[((size_t)split * M + m) * N + row] = acc[r];
+  }
+}
+
+// y = bf16(sum of the K slices, in slice order)
+__global__ __launch_bounds__(256) void gemv_split_finalize_kernel(const float* __restrict__ part,
+                                                                  int splits, int64_t MN,
+                                                                  uint16_t* __restrict__ y) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= MN) return;
+  float s = 0.f;
+  for (int j = 0; j < splits; ++j) s += part[(size_t)j * MN + i];
+  y[i] = f32_to_bf16_rne(s);
+}
+
+// Split-K partial sums live in one buffer per (device, stream), grown on demand
+// and kept for the life of the process.  Calls on one stream are ordered;
+// different streams get different buffers.  While the stream is being
+// captured into a graph no allocation is made (nullptr: the caller takes
+// another path).
+void* split_workspace(size_t bytes, hipStream_t s) {
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> bufs;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  auto& b = bufs[{dev, s}];
+  if (b.second >= bytes) return b.first;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+  if (b.first) {
+    // the old buffer may still be read by work queued on s
+    if (hipStreamSynchronize(s) != hipSuccess) return nullptr;
+    hipFree(b.first);
+    b = {nullptr, 0};
+  }
+  void* p = nullptr;
+  if (hipMalloc(&p, bytes) != hipSuccess) return nullptr;
+  b = {p, bytes};
+  return p;
+}
+
+template <int CPG, bool SYM>
+hipError_t launch_cpg(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
+                      const uint16_t* zr, int N, int G, float* part, int splits, hipStream_t s) {
+  const dim3 grid((unsigned)((N + 63) / 64), (unsigned)splits);
+  if (M <= 4)
+    hipLaunchKernelGGL((gemv_mfma_tile_kernel<CPG, SYM, 4>), grid, dim3(256), 0, s, x, M, K, qw, sc,
+                       zr, N, G, part);
+  else if (M <= 8)
+    hipLaunchKernelGGL((gemv_mfma_tile_kernel<CPG, SYM, 8>), grid, dim3(256), 0, s, x, M, K, qw, sc,
+                       zr, N, G, part);
+  else
+    hipLaunchKernelGGL((gemv_mfma_tile_kernel<CPG, SYM, 16>), grid, dim3(256), 0, s, x, M, K, qw, sc,
+                       zr, N, G, part);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemv_mfma_supported(int M, int64_t K, int64_t N, int G) {
+  if (M < 4 || M > 16) return false;
+  if (G != 32 && G != 64 && G % 128 != 0) return false;
+  if (K % 256 != 0) return false;  // keeps the 4-, 8- and 16-byte scale loads aligned
+  if (N * (K / 2) >= ((int64_t)1 << 31) || (int64_t)M * K * 2 >= ((int64_t)1 << 31)) return false;
+  if (N > ((int64_t)1 << 30) / 64) return false;
+  return true;
+}
+
+size_t gemv_workspace_bytes(int M, int64_t K, int64_t N, int G) {
+  if (!gemv_mfma_supported(M, K, N, G)) return 0;
+  return (size_t)((K + kKC - 1) / kKC) * (size_t)M * (size_t)N * sizeof(float);
+}
+
+hipError_t launch_w4a16_gemv_mfma(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
+                                  const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
+                                  int symmetric, uint16_t* y, void* workspace, hipStream_t s,
+                                  bool* launched) {
+  *launched = false;
+  const int splits = (int)((K + kKC - 1) / kKC);
+  float* part = workspace ? (float*)workspace
+                          : (float*)split_workspace(gemv_workspace_bytes(M, K, N, G), s);
+  if (!part) return hipSuccess;  // no workspace (graph capture): the caller falls back
+  hipError_t e;
+  const int k = (int)K, n = (int)N;
+  if (symmetric) {
+    if (G == 32) e = launch_cpg<1, true>(x, M, k, qweight, scales, zeros, n, G, part, splits, s);
+    else if (G == 64) e = launch_cpg<2, true>(x, M, k, qweight, scales, zeros, n, G, part, splits, s);
+    else e = launch_cpg<4, true>(x, M, k, qweight, scales, zeros, n, G, part, splits, s);
+  } else {
+    if (G == 32) e = launch_cpg<1, false>(x, M, k, qweight, scales, zeros, n, G, part, splits, s);
+    else if (G == 64) e = launch_cpg<2, false>(x, M, k, qweight, scales, zeros, n, G, part, splits, s);
+    else e = launch_cpg<4, false>(x, M, k, qweight, scales, zeros, n, G, part, splits, s);
+  }
+  if (e != hipSuccess) return e;
+  const int64_t mn = (int64_t)M * N;
+  hipLaunchKernelGGL(gemv_split_finalize_kernel, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, s,
+                     (const float*)part, splits, mn, y);
+  e = hipGetLastError();
+  if (e == hipSuccess) *launched = true;
+  return e;
+}
+
+}  // namespace gq

@@ -157,7 +157,36 @@ gq_status gq_w4a16_gemv(const uint16_t* x, int64_t M, int64_t K, const uint8_t* 
   hipStream_t s = (hipStream_t)stream;
   if (gq_status st = check_device(s)) return st;
   return from_hip(gq::launch_w4a16_gemv(x, (int)M, K, qweight, scales, zeros, N, p.group_size,
-                                        p.symmetric, y, s));
+                                        p.symmetric, y, nullptr, 0, s));
+}
+
+gq_status gq_w4a16_gemv_workspace_size(int64_t M, int64_t K, int64_t N, gq_qparams p,
+                                       size_t* bytes) {
+  if (!bytes) return GQ_ERR_INVALID_ARG;
+  *bytes = 0;
+  if (M < 0 || M > 16) return GQ_ERR_INVALID_ARG;
+  if (gq_status s = check_groups(N, K, p.group_size)) return s;
+  if (p.symmetric != 0 && p.symmetric != 1) return GQ_ERR_INVALID_ARG;
+  if (p.bits < 2 || p.bits > 8) return GQ_ERR_INVALID_ARG;
+  if (p.bits != 4) return GQ_ERR_UNSUPPORTED;
+  *bytes = gq::gemv_workspace_bytes((int)M, K, N, p.group_size);
+  return GQ_OK;
+}
+
+gq_status gq_w4a16_gemv_ws(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                           const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                           gq_qparams p, uint16_t* y, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (M > 16) return GQ_ERR_INVALID_ARG;
+  if (gq_status s = check_w4_matmul(x, M, K, qweight, scales, zeros, N, p, y)) return s;
+  if (M == 0 || N == 0) return GQ_OK;
+  const size_t need = gq::gemv_workspace_bytes((int)M, K, N, p.group_size);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GQ_ERR_INVALID_ARG;
+  if (workspace && !aligned16(workspace)) return GQ_ERR_MISALIGNED;
+  hipStream_t s = (hipStream_t)stream;
+  if (gq_status st = check_device(s)) return st;
+  return from_hip(gq::launch_w4a16_gemv(x, (int)M, K, qweight, scales, zeros, N, p.group_size,
+                                        p.symmetric, y, need ? workspace : nullptr, need, s));
 }
 
 gq_status gq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,

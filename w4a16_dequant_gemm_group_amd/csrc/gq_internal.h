@@ -103,9 +103,23 @@ hipError_t launch_pack_int4(const void* codes, int64_t N, int64_t K, int symmetr
 hipError_t launch_dequantize(const uint8_t* qweight, const uint16_t* scales,
                              const uint16_t* zeros, int64_t N, int64_t K, int G, int symmetric,
                              void* out, gq_dtype odt, hipStream_t s);
+// workspace: caller scratch of ws_bytes (>= gemv_workspace_bytes), or NULL to
+// use the library's per-stream scratch for the matrix-core path.
 hipError_t launch_w4a16_gemv(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
                              const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
-                             int symmetric, uint16_t* y, hipStream_t s);
+                             int symmetric, uint16_t* y, void* workspace, size_t ws_bytes,
+                             hipStream_t s);
+// Small-batch GEMV on the matrix cores (4 <= M <= 16, split along K).  Sets
+// *launched = false without launching when it cannot run this call (no split
+// workspace while the stream is being captured); the caller then uses the
+// dot-product kernel.
+bool gemv_mfma_supported(int M, int64_t K, int64_t N, int G);
+// Scratch the GEMV needs for these arguments (0 unless the matrix-core path runs).
+size_t gemv_workspace_bytes(int M, int64_t K, int64_t N, int G);
+hipError_t launch_w4a16_gemv_mfma(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
+                                  const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
+                                  int symmetric, uint16_t* y, void* workspace, hipStream_t s,
+                                  bool* launched);
 hipError_t launch_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
                              const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
                              int symmetric, uint16_t* y, hipStream_t s);
