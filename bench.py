@@ -126,6 +126,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--reps", type=int, default=7,
+                    help="timed replays of the step graph; the median is reported")
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the decode step (used for profiling)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -188,21 +190,27 @@ def main():
         return
 
     from oracle import gq_oracle as O
-    log("inputs ready; parity gate")
-    for name, n, k in shapes:
-        w, x = host[name]
-        qw, s, z = W[name]
-        y = B.gq_w4a16_gemv(X[name], qw, s, z, G, False)
-        rows = np.sort(np.random.default_rng(0).choice(n, 64, replace=False))
-        c_ref, s_ref, z_ref = O.quantize_to_storage(w[rows], 4, G, False)
-        qref = O.pack_int4(c_ref, False)
+
+    def gate(name, w, x, qw, s, z, g, sym):
+        """Correctness before timing: 64 sampled rows of the packed weights equal
+        the oracle's bytes and the GEMV output on them meets the parity bar."""
+        n = qw.shape[0]
+        y = B.gq_w4a16_gemv(to_dev(x), qw, s, z, g, sym)
+        rows = np.sort(np.random.default_rng(0).choice(n, min(64, n), replace=False))
+        c_ref, s_ref, z_ref = O.quantize_to_storage(w[rows], 4, g, sym)
+        qref = O.pack_int4(c_ref, sym)
         if not np.array_equal(qw.cpu().numpy()[rows], qref):
             raise SystemExit(f"parity gate: packed weights of {name} differ from the oracle")
-        ref = O.w4a16_reference(x, qref, s_ref, z_ref, G, False)
-        wh = O.dequantize_packed(qref, s_ref, z_ref, G, False)
+        ref = O.w4a16_reference(x, qref, s_ref, z_ref, g, sym)
+        wh = O.dequantize_packed(qref, s_ref, z_ref, g, sym)
         ok, rel, ratio = O.within_parity(O.bf16_to_f64(bits16(y))[:, rows], ref, O.bf16_to_f64(x), wh)
         if not ok:
             raise SystemExit(f"parity gate: {name} relF {rel:.2e} max/allowed {ratio:.2f}")
+
+    log("inputs ready; parity gate")
+    for name, n, k in shapes:
+        w, x = host[name]
+        gate(name, w, x, *W[name], G, False)
     log("parity gate passed")
 
     # ---------------- rotation copies ------------------------------------------------
@@ -227,19 +235,24 @@ def main():
     # The timed region replays a HIP graph holding exactly `steps` steps (4 launches
     # each, rotating weight copies), so host launch overhead does not leak into the
     # measurement.  The graph holds only this library's kernels.
+    # Each repetition replays the whole graph (exactly `steps` steps) between two
+    # events; the reported step time is the median over the repetitions.
     g = capture(torch, stream, lambda: [run_step(i) for i in range(args.steps)])
     g.replay()
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    g.replay()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
+    rep_ms = []
+    for _ in range(args.reps):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        g.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        rep_ms.append(t0.elapsed_time(t1) / args.steps)
+    ms_per_step = float(np.median(rep_ms))
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    log(f"decode step {ms_per_step * 1e3:.2f} us, {value:.0f} GB/s")
+    log(f"decode step {ms_per_step * 1e3:.2f} us, {value:.0f} GB/s (median of {args.reps})")
     # the graph's outputs match eager launches of the same step
     yg = {nm: Y[nm].clone() for nm, _, _ in shapes}
     run_step(args.steps - 1)
@@ -257,8 +270,11 @@ def main():
             qw, s, z = copies[i % R][nm]
             B.gq_w4a16_gemv(X[nm], qw, s, z, G, False, y=Y[nm], stream=torch.cuda.current_stream())
         per_us[nm] = graph_time(torch, stream, one, nrep)
+        # (graph_time is the median over repeated replays)
     per_gbps = {nm: gemv_bytes(n, k, G) / (per_us[nm] * 1e-6) / 1e9 for nm, n, k in shapes}
     log(f"per-shape us {per_us}")
+    ceiling = stream_ceiling(torch, B, dev, stream, {nm: gemv_bytes(n, k, G) for nm, n, k in shapes})
+    log(f"stream read ceiling {ceiling['GB/s']:.0f} GB/s; same-size pure reads {ceiling['per_shape_us']}")
 
     # Every launch of the step is the same streaming GEMV kernel: its algorithmic
     # bytes per launch over its average launch duration in the timed region.
@@ -270,13 +286,18 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": None if tr is None else round(tr["mean_hbm_bytes_per_launch"]),
                 "kernel": f"{GEMV_KERNEL}<false,false> (all four projections)",
-                "bytes_per_launch": bytes_per_launch, "avg_launch_us": round(avg_launch_us, 3)}
+                "bytes_per_launch": bytes_per_launch, "avg_launch_us": round(avg_launch_us, 3),
+                "frac_of_measured_read_ceiling": round(achieved / ceiling["GB/s"], 4),
+                # time of pure reads of the same byte counts over the time of the GEMVs
+                "frac_of_same_size_reads": round(sum(ceiling["per_shape_us"].values())
+                                                 / (ms_per_step * 1e3), 4)}
     if tr is not None:
         roofline["traffic_per_shape"] = {k: round(v) for k, v in tr["hbm_bytes_per_launch"].items()}
 
     extras = {}
     if not args.skip_extras:
-        extras = run_extras(torch, B, synth, to_dev, dev, stream, shapes, W, X)
+        extras = run_extras(torch, B, synth, to_dev, dev, stream, shapes, W, X, gate,
+                            ms_per_step * 1e3, ceiling, copies)
 
     cpu = cpu_baseline(args, O, host, shapes)
 
@@ -294,6 +315,10 @@ def main():
                    "per_shape_GBps": {k: round(v, 1) for k, v in per_gbps.items()}},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "timing": {"us_per_step": spread([v * 1e3 for v in rep_ms]),
+                   "method": f"median of {args.reps} replays of one HIP graph of {args.steps} steps, "
+                             "HIP events on the launch stream"},
+        "stream_read_ceiling": ceiling,
     }
     out.update(extras)
     print(json.dumps(out), flush=True)
@@ -312,20 +337,35 @@ def capture(torch, stream, body):
     return g
 
 
-def graph_time(torch, stream, fn, reps):
-    """Average microseconds per fn(i) launch, from one replay of a graph of
-    `reps` launches (after one untimed replay)."""
-    g = capture(torch, stream, lambda: [fn(i) for i in range(reps)])
+def graph_times(torch, stream, fn, launches, reps=5):
+    """Microseconds per fn(i) call in each of `reps` timed replays of one graph
+    holding fn(0) .. fn(launches - 1), after one untimed replay."""
+    g = capture(torch, stream, lambda: [fn(i) for i in range(launches)])
     g.replay()
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    g.replay()
-    t1.record(stream)
-    torch.cuda.synchronize()
+    out = []
+    for _ in range(reps):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        g.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        out.append(t0.elapsed_time(t1) / launches * 1e3)
     del g
-    return t0.elapsed_time(t1) / reps * 1e3
+    return out
+
+
+def graph_time(torch, stream, fn, launches, reps=5):
+    """Median of graph_times."""
+    return float(np.median(graph_times(torch, stream, fn, launches, reps)))
+
+
+def spread(v):
+    """median, p10, p90 of a list of times."""
+    v = np.asarray(v, dtype=np.float64)
+    return {"median": round(float(np.median(v)), 3), "p10": round(float(np.percentile(v, 10)), 3),
+            "p90": round(float(np.percentile(v, 90)), 3), "n": int(v.size)}
 
 
 def time_launches(torch, stream, fn, reps):
@@ -339,7 +379,33 @@ def time_launches(torch, stream, fn, reps):
     return t0.elapsed_time(t1) / reps * 1e3  # us
 
 
-def run_extras(torch, B, synth, to_dev, dev, stream, shapes, W, X):
+def stream_ceiling(torch, B, dev, stream, sizes):
+    """Read bandwidth one kernel reaches: gq_stream_read over a 2 GiB buffer (8x
+    the Infinity Cache), and the time of a pure read of each size in `sizes`,
+    rotating through the same buffer so every read comes from HBM."""
+    total = 1 << 31
+    buf = torch.zeros(total // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    B.gq_stream_read(buf, sink)
+    t = graph_times(torch, stream, lambda i: B.gq_stream_read(buf, sink), 4)
+    gbps = total / (np.median(t) * 1e-6) / 1e9
+    raw = buf.view(torch.uint8)
+    per_us = {}
+    for nm, nb in sizes.items():
+        nb = nb // 16 * 16
+        chunks = total // nb
+        per_us[nm] = round(graph_time(torch, stream, lambda i, nb=nb, c=chunks:
+                                      B.gq_stream_read(raw[(i % c) * nb:(i % c + 1) * nb], sink),
+                                      2 * chunks), 3)
+    del buf, raw
+    torch.cuda.empty_cache()
+    return {"GB/s": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "us_2GiB": spread(t), "per_shape_us": per_us,
+            "kernel": "stream_read_kernel (16-byte nontemporal loads, 2048 per workgroup)"}
+
+
+def run_extras(torch, B, synth, to_dev, dev, stream, shapes, W, X, gate, fused_step_us, ceiling,
+               W_copies):
     ex = {}
     # ---- prefill GEMM, M = 2048 -------------------------------------------------
     gemm = {}
@@ -362,7 +428,7 @@ def run_extras(torch, B, synth, to_dev, dev, stream, shapes, W, X):
                         "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS, "frac": round(agg / MFMA_BF16_PEAK_TFLOPS, 4)}
     log(f"gemm M=2048: {agg:.0f} TFLOP/s")
 
-    # ---- bf16 GEMV comparator (hipBLASLt through torch), rotating copies ------------
+    # ---- bf16 GEMV comparator: the faster of hipBLASLt (torch) and gq_bf16_gemv --------
     import torch.nn.functional as F
     wb = {}
     for name, n, k in shapes:
@@ -370,21 +436,137 @@ def run_extras(torch, B, synth, to_dev, dev, stream, shapes, W, X):
     bf16_bytes = sum(2 * n * k + 2 * k + 2 * n for _, n, k in shapes)
     Rb = max(2, int(np.ceil(2 ** 30 / bf16_bytes)))
     wcopies = [wb] + [{nm: t.clone() for nm, t in wb.items()} for _ in range(Rb - 1)]
+    Yb = {nm: torch.empty((1, n), dtype=torch.bfloat16, device=dev) for nm, n, _ in shapes}
 
-    def bf16_step(i):
+    def bf16_step_torch(i):
         c = wcopies[i % Rb]
         for nm, _, _ in shapes:
-            F.linear(X[nm], c[nm])
-    for i in range(10):
-        bf16_step(i)
-    us_bf16 = time_launches(torch, stream, bf16_step, 50)
+            torch.matmul(X[nm], c[nm].t(), out=Yb[nm])
+
+    def bf16_step_own(i):
+        c = wcopies[i % Rb]
+        for nm, _, _ in shapes:
+            B.gq_bf16_gemv(X[nm], c[nm], y=Yb[nm])
+
+    for i in range(3):
+        bf16_step_torch(i)
+        bf16_step_own(i)
+    torch.cuda.synchronize()
+    t_own = graph_times(torch, stream, bf16_step_own, 2 * Rb)
+    try:
+        t_torch = graph_times(torch, stream, bf16_step_torch, 2 * Rb)
+        torch_how = "HIP graph"
+    except Exception as e:  # a library call that cannot be captured is timed eagerly
+        log(f"hipBLASLt GEMV not capturable ({type(e).__name__}); timing eager launches")
+        torch.cuda.synchronize()
+        t_torch = [time_launches(torch, stream, bf16_step_torch, 2 * Rb) for _ in range(5)]
+        torch_how = "eager launches"
+    u_own, u_torch = float(np.median(t_own)), float(np.median(t_torch))
+    t_bf16 = min(u_own, u_torch)
+    bf16_per_shape = {}
+    for nm, n, k in shapes:
+        def one_own(i, nm=nm):
+            B.gq_bf16_gemv(X[nm], wcopies[i % Rb][nm], y=Yb[nm])
+        bf16_per_shape[nm] = round(graph_time(torch, stream, one_own, 2 * Rb), 3)
+    ex["bf16_gemv_comparator"] = {
+        "us_per_step": round(t_bf16, 2), "GB/s": round(bf16_bytes / (t_bf16 * 1e-6) / 1e9, 1),
+        "hipblaslt_us_per_step": spread(t_torch), "hipblaslt_timing": torch_how,
+        "gq_bf16_gemv_us_per_step": spread(t_own), "gq_bf16_gemv_per_shape_us": bf16_per_shape,
+        "faster": "gq_bf16_gemv" if u_own <= u_torch else "hipBLASLt",
+        "byte_ratio": round(bf16_bytes / sum(gemv_bytes(n, k, G) for _, n, k in shapes), 3),
+        "speedup_w4a16_vs_bf16": round(t_bf16 / fused_step_us, 3)}
+    log(f"bf16 GEMV step: own {u_own:.1f} us, hipBLASLt {u_torch:.1f} us; "
+        f"W4A16 speedup {t_bf16 / fused_step_us:.2f}x")
+
+    # ---- unfused comparator: gq_dequantize -> bf16 W^ in HBM -> bf16 product ----------
+    # M = 1: the decode step with every weight first expanded into a bf16 buffer.
+    Rq = len(W_copies)
+    wh = {nm: torch.empty((n, k), dtype=torch.bfloat16, device=dev) for nm, n, k in shapes}
+
+    def unfused_step(i):
+        c = W_copies[i % Rq]
+        for nm, _, _ in shapes:
+            qw, s_, z_ = c[nm]
+            B.gq_dequantize(qw, s_, z_, G, False, out=wh[nm])
+            B.gq_bf16_gemv(X[nm], wh[nm], y=Yb[nm])
+    unfused_step(0)
+    t_unf = graph_times(torch, stream, unfused_step, Rq)
+    unf_bytes = sum(gemv_bytes(n, k, G) + 4 * n * k for _, n, k in shapes)
+    u_unf = float(np.median(t_unf))
+    ex["unfused_m1"] = {
+        "us_per_step": spread(t_unf), "bytes_per_step": unf_bytes,
+        "bytes_vs_fused": round(unf_bytes / sum(gemv_bytes(n, k, G) for _, n, k in shapes), 3),
+        "bytes_vs_bf16": round(unf_bytes / bf16_bytes, 3),
+        "time_vs_fused": round(u_unf / fused_step_us, 3), "time_vs_bf16": round(u_unf / t_bf16, 3),
+        "path": "gq_dequantize (bf16 out) then gq_bf16_gemv, per projection, rotating weight copies"}
+    log(f"unfused decode step {u_unf:.1f} us ({u_unf / fused_step_us:.2f}x fused, "
+        f"{u_unf / t_bf16:.2f}x bf16)")
     del wcopies, wb
     torch.cuda.empty_cache()
-    step_bytes = sum(gemv_bytes(n, k, G) for _, n, k in shapes)
-    ex["bf16_gemv_comparator"] = {"us_per_step": round(us_bf16, 2),
-                                  "GB/s": round(bf16_bytes / (us_bf16 * 1e-6) / 1e9, 1),
-                                  "byte_ratio": round(bf16_bytes / step_bytes, 3)}
-    log(f"bf16 GEMV step {us_bf16:.1f} us")
+
+    # M = 2048: dequantize then hipBLASLt, against the fused GEMM and a plain bf16 GEMM.
+    unf_pf = {}
+    for name, n, k in shapes:
+        _, xb = synth.prefill_case(name)
+        xd = to_dev(xb)
+        qw, s_, z_ = W[name]
+        wb1 = torch.randn((n, k), dtype=torch.bfloat16, device=dev) * 0.02
+        yp = torch.empty((2048, n), dtype=torch.bfloat16, device=dev)
+
+        def unf(i):
+            B.gq_dequantize(qw, s_, z_, G, False, out=wh[name])
+            torch.matmul(xd, wh[name].t(), out=yp)
+
+        def plain(i):
+            torch.matmul(xd, wb1.t(), out=yp)
+        for i in range(3):
+            unf(i)
+            plain(i)
+        torch.cuda.synchronize()
+        t_u = float(np.median([time_launches(torch, stream, unf, 5) for _ in range(3)]))
+        t_p = float(np.median([time_launches(torch, stream, plain, 5) for _ in range(3)]))
+        fl = 2.0 * 2048 * n * k
+        unf_pf[name] = {"unfused_us": round(t_u, 2), "bf16_gemm_us": round(t_p, 2),
+                        "fused_us": gemm[name]["us"],
+                        "bf16_gemm_TFLOP/s": round(fl / (t_p * 1e-6) / 1e12, 1)}
+        del xd, wb1, yp
+    ex["unfused_and_bf16_m2048"] = unf_pf
+    log(f"M=2048 unfused / bf16 / fused: {unf_pf}")
+    del wh
+    torch.cuda.empty_cache()
+
+    # ---- group-size sweep on down [4096, 14336], M = 1, symmetric and asymmetric --------
+    name = "down"
+    n, k = synth.LLAMA3_8B_SHAPES[name]
+    w, x = synth.decode_case(name)
+    wd, xd = to_dev(w), to_dev(x)
+    yd = torch.empty((1, n), dtype=torch.bfloat16, device=dev)
+    sweep = {}
+    for sym in (True, False):
+        for g in (32, 64, 128):
+            codes, s_, z_ = B.gq_quantize_groups(wd, 4, g, sym)
+            qw = B.gq_pack_int4(codes, sym)
+            del codes
+            gate(f"{name} g{g} {'sym' if sym else 'asym'}", w, x, qw, s_, z_, g, sym)
+            one = (qw, s_, z_)
+            byt = gemv_bytes(n, k, g, 1, sym)
+            R = max(2, int(np.ceil(2 ** 30 / byt)))
+            cp = [one] + [tuple(None if t is None else t.clone() for t in one) for _ in range(R - 1)]
+
+            def fn(i, cp=cp, g=g, sym=sym):
+                a, b, c = cp[i % len(cp)]
+                B.gq_w4a16_gemv(xd, a, b, c, g, sym, y=yd)
+            t = graph_times(torch, stream, fn, 2 * R)
+            us = float(np.median(t))
+            gbps = byt / (us * 1e-6) / 1e9
+            sweep[f"{'sym' if sym else 'asym'}_g{g}"] = {
+                "us": spread(t), "bytes": byt, "GB/s": round(gbps, 1),
+                "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                "frac_of_read_ceiling": round(gbps / ceiling["GB/s"], 4)}
+            del cp, one, qw, s_, z_
+    ex["group_sweep_down_m1"] = sweep
+    log(f"group sweep down M=1: { {k_: v['us']['median'] for k_, v in sweep.items()} }")
+    del wd, xd, yd
 
     # ---- small batch M in {1,4,8,16}, symmetric g32, rotating weight copies ---------
     sym_w = {}

@@ -21,8 +21,11 @@
  *
  * Conventions for every entry point
  *   - Pointers are device pointers (HIP global memory) unless marked "host".
- *     The caller owns every buffer; libgq allocates no memory and keeps no
- *     state beyond a per-device architecture check.
+ *     The caller owns every buffer.  libgq keeps a per-device architecture
+ *     check and allocates nothing, with one exception: gq_w4a16_gemv for
+ *     4 <= M <= 16 keeps a split-K scratch buffer per (device, stream), grown on
+ *     demand and held until the process ends (gq_w4a16_gemv_ws takes it from
+ *     the caller instead).
  *   - All matrices are dense, row-major, contiguous.  W is [N, K] = out x in,
  *     so Y = X W^T [P1 sec.2]; groups run along K (the reduction axis).
  *   - fp16 / bf16 values are passed as uint16_t bit patterns.

@@ -12,10 +12,11 @@ from oracle import gq_oracle as O
 from w4a16_dequant_gemm_group_amd import binding as B
 
 HEADER = os.path.join(ROOT, "include", "gq.h")
+BENCH_HEADER = os.path.join(ROOT, "include", "gq_bench.h")
 
 
-def header_functions():
-    src = open(HEADER).read()
+def header_functions(path=HEADER):
+    src = open(path).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(gq_[a-z0-9_]+)\s*\(", src)))
 
@@ -30,6 +31,10 @@ def test_exports_every_declared_symbol(lib):
     assert len(names) == 12
     assert set(names) == set(B.EXPORTS)
     for n in names:
+        assert hasattr(lib, n), n
+    bench = header_functions(BENCH_HEADER)
+    assert set(bench) == set(B.BENCH_EXPORTS) and len(bench) == 2
+    for n in bench:
         assert hasattr(lib, n), n
 
 
@@ -133,3 +138,28 @@ def test_gemv_workspace_size_and_validation(lib):
     assert lib.gq_w4a16_gemv_ws(*args, FAKE_MIS, need, None) == B.GQ_ERR_MISALIGNED
     # the plain GEMV checks still apply
     assert lib.gq_w4a16_gemv_ws(FAKE, 17, 4096, FAKE, FAKE, FAKE, 4096, q(), FAKE, FAKE, need, None) == B.GQ_ERR_INVALID_ARG
+
+
+def test_bench_entry_point_validation(lib):
+    L = lib
+    # bf16 GEMV: M in 0..4, K a multiple of 8, byte limits, alignment
+    assert L.gq_bf16_gemv(FAKE, 5, 4096, FAKE, 64, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_bf16_gemv(FAKE, 1, 4092, FAKE, 64, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_bf16_gemv(FAKE, 1, 4096, FAKE, -1, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_bf16_gemv(FAKE, 1, 4096, FAKE, 1 << 18, FAKE, None) == B.GQ_ERR_UNSUPPORTED
+    # x staged in LDS: M * round_up(K, 2048) activations must fit 32768
+    assert L.gq_bf16_gemv(FAKE, 3, 14336, FAKE, 64, FAKE, None) == B.GQ_ERR_UNSUPPORTED
+    assert L.gq_bf16_gemv(FAKE, 1, 32776, FAKE, 64, FAKE, None) == B.GQ_ERR_UNSUPPORTED
+    assert L.gq_bf16_gemv(FAKE_MIS, 1, 4096, FAKE, 64, FAKE, None) == B.GQ_ERR_MISALIGNED
+    assert L.gq_bf16_gemv(FAKE, 1, 4096, FAKE_MIS, 64, FAKE, None) == B.GQ_ERR_MISALIGNED
+    assert L.gq_bf16_gemv(FAKE, 1, 4096, FAKE, 64, ctypes.c_void_p(4097), None) == B.GQ_ERR_MISALIGNED
+    assert L.gq_bf16_gemv(None, 1, 4096, FAKE, 64, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_bf16_gemv(None, 0, 4096, None, 64, None, None) == B.GQ_OK
+    # stream read: whole 16-byte words, bounded size, alignment
+    assert L.gq_stream_read(FAKE, 24, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_stream_read(FAKE, -16, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_stream_read(FAKE, (1 << 38) + 16, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_stream_read(FAKE_MIS, 64, FAKE, None) == B.GQ_ERR_MISALIGNED
+    assert L.gq_stream_read(FAKE, 64, ctypes.c_void_p(4098), None) == B.GQ_ERR_MISALIGNED
+    assert L.gq_stream_read(FAKE, 64, None, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_stream_read(None, 0, None, None) == B.GQ_OK

@@ -26,6 +26,8 @@ EXPORTS = (
     "gq_dequantize", "gq_w4a16_gemv", "gq_w4a16_gemv_workspace_size", "gq_w4a16_gemv_ws",
     "gq_w4a16_gemm", "gq_q4k_quantize", "gq_q4k_gemv",
 )
+# comparators and probes (include/gq_bench.h)
+BENCH_EXPORTS = ("gq_bf16_gemv", "gq_stream_read")
 
 
 class GqQParams(ctypes.Structure):
@@ -67,6 +69,8 @@ def lib() -> ctypes.CDLL:
         "gq_w4a16_gemm": [p, i64, i64, p, p, p, i64, Q, p, p],
         "gq_q4k_quantize": [p, c, i64, i64, p, p],
         "gq_q4k_gemv": [p, i64, i64, p, i64, p, p],
+        "gq_bf16_gemv": [p, i64, i64, p, i64, p, p],
+        "gq_stream_read": [p, i64, p, p],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -255,3 +259,27 @@ def gq_q4k_gemv(x: torch.Tensor, blocks: torch.Tensor, y=None, stream=None):
     _check(lib().gq_q4k_gemv(_ptr(x), M, K, _ptr(blocks), N, _ptr(y), _stream(stream)),
            "gq_q4k_gemv")
     return y
+
+
+def gq_bf16_gemv(x: torch.Tensor, w: torch.Tensor, y=None, stream=None):
+    """Plain bf16 GEMV (the 16-bit comparator), x bf16 [M<=4, K], w bf16 [N, K] -> y bf16 [M, N]."""
+    _need(x, "x", (torch.bfloat16,))
+    _need(w, "w", (torch.bfloat16,), x.device)
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError(f"w is {tuple(w.shape)}, expected [N, {K}]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(lib().gq_bf16_gemv(_ptr(x), M, K, _ptr(w), N, _ptr(y), _stream(stream)), "gq_bf16_gemv")
+    return y
+
+
+def gq_stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Read every byte of the contiguous GPU tensor buf once (bandwidth probe);
+    sink is a GPU int32/uint32 tensor of at least one element that the kernel may write."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    _need(sink, "sink", (torch.int32, torch.uint32), buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().gq_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "gq_stream_read")

@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgq.so")
 
-SOURCES = ["gq_api.cpp", "quant.hip", "gemv.hip", "gemv_mfma.hip", "gemm.hip", "q4k.hip"]
+SOURCES = ["gq_api.cpp", "quant.hip", "gemv.hip", "gemv_mfma.hip", "gemm.hip", "q4k.hip",
+           "bench_kernels.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

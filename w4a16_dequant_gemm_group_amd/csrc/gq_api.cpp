@@ -224,4 +224,28 @@ gq_status gq_q4k_gemv(const uint16_t* x, int64_t M, int64_t K, const uint8_t* bl
   return from_hip(gq::launch_q4k_gemv(x, (int)M, K, blocks, N, y, s));
 }
 
+gq_status gq_bf16_gemv(const uint16_t* x, int64_t M, int64_t K, const uint16_t* w, int64_t N,
+                       uint16_t* y, void* stream) {
+  if (M < 0 || M > 4) return GQ_ERR_INVALID_ARG;
+  if (N < 0 || K < 8 || N > kMaxDim || K > kMaxDim || K % 8 != 0) return GQ_ERR_INVALID_ARG;
+  if (N * K * 2 >= ((int64_t)1 << 31)) return GQ_ERR_UNSUPPORTED;
+  if (M * (int64_t)gq::bf16_gemv_kpad(K) * 2 > 65536) return GQ_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return GQ_OK;
+  if (!x || !w || !y) return GQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w) || ((uintptr_t)y & 1u)) return GQ_ERR_MISALIGNED;
+  hipStream_t s = (hipStream_t)stream;
+  if (gq_status st = check_device(s)) return st;
+  return from_hip(gq::launch_bf16_gemv(x, (int)M, K, w, N, y, s));
+}
+
+gq_status gq_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0 || bytes > ((int64_t)1 << 38)) return GQ_ERR_INVALID_ARG;
+  if (bytes == 0) return GQ_OK;
+  if (!buf || !sink) return GQ_ERR_INVALID_ARG;
+  if (!aligned16(buf) || ((uintptr_t)sink & 3u)) return GQ_ERR_MISALIGNED;
+  hipStream_t s = (hipStream_t)stream;
+  if (gq_status st = check_device(s)) return st;
+  return from_hip(gq::launch_stream_read(buf, bytes, sink, s));
+}
+
 }  // extern "C"

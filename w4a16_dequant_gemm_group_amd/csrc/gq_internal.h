@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "gq.h"
+#include "gq_bench.h"
 
 namespace gq {
 
@@ -127,5 +128,12 @@ hipError_t launch_q4k_quantize(const void* w, gq_dtype dt, int64_t N, int64_t K,
                                hipStream_t s);
 hipError_t launch_q4k_gemv(const uint16_t* x, int M, int64_t K, const uint8_t* blocks, int64_t N,
                            uint16_t* y, hipStream_t s);
+
+// Comparators and probes (no quantization): plain bf16 GEMV, 1 <= M <= 4, with
+// x staged in M * bf16_gemv_kpad(K) * 2 bytes of LDS; HBM stream read.
+int bf16_gemv_kpad(int64_t K);
+hipError_t launch_bf16_gemv(const uint16_t* x, int M, int64_t K, const uint16_t* w, int64_t N,
+                            uint16_t* y, hipStream_t s);
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
 
 }  // namespace gq
