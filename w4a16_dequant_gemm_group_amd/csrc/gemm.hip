@@ -155,10 +155,12 @@ __global__ __launch_bounds__(256 * WM, 2) void w4a16_gemm_kernel(
     const int g0 = __builtin_amdgcn_readfirstlane(k0 / G);
     const int g1 = __builtin_amdgcn_readfirstlane((k0 + 32) / G);
     if (!TAIL) {
+      // readfirstlane keeps the offsets in scalar registers: a buffer load whose
+      // soffset the compiler cannot prove uniform becomes a loop over lanes
       const bool kin = k0 < K;
-      const uint32_t sa = kin ? (uint32_t)k0 * 2u : kOob;
-      const uint32_t sb = kin ? (uint32_t)k0 / 2u : kOob;
-      const uint32_t sg = kin ? (uint32_t)g0 * 2u : kOob;
+      const uint32_t sa = __builtin_amdgcn_readfirstlane(kin ? (uint32_t)k0 * 2u : kOob);
+      const uint32_t sb = __builtin_amdgcn_readfirstlane(kin ? (uint32_t)k0 / 2u : kOob);
+      const uint32_t sg = __builtin_amdgcn_readfirstlane(kin ? (uint32_t)g0 * 2u : kOob);
 #pragma unroll
       for (int i = 0; i < A_CH; ++i) S.a[i] = bload16(rA, voa[i], sa);
 #pragma unroll
