@@ -31,6 +31,12 @@ def _oracle_weights(w_bits, G, sym):
     (2, 70, 864, 96, True),          # groups straddle k tiles
     (257, 131, 512, 512, False),     # group = K
     (1, 128, 256, 32, False),        # M = 1 through the GEMM
+    # 256 x 256 tile kernel (K % 64 == 0, G in 64, 128, 256k)
+    (260, 300, 832, 64, True),       # symmetric, odd number of k tiles
+    (640, 64, 1216, 64, False),      # 19 k tiles, N below one tile
+    (384, 520, 2560, 256, False),    # ten 256-groups, ragged N
+    (512, 256, 1792, 256, True),     # symmetric, seven 256-groups
+    (300, 1000, 1536, 128, True),    # symmetric g128, ragged M and N
 ])
 def test_small_shapes(M, N, K, G, sym):
     w, _ = synth.weights(N, K, seed=N + K)
@@ -72,7 +78,7 @@ def test_prefill_shapes_full_size(name):
     assert_parity(yb, ref, O.bf16_to_f64(x), wh, f"gemm {name} M=2048 full, sampled")
 
 
-@pytest.mark.parametrize("G", [32, 128])
+@pytest.mark.parametrize("G", [32, 64, 128, 256])
 def test_zero_scale_groups(G):
     """Groups whose fp16 scale is 0 contribute nothing (x^ = 0 * (q - z) = 0),
     including the first group of a column and runs of zero-scale groups; the

@@ -18,21 +18,39 @@
 // inside fp32 range, and each rescale adds one fp32 rounding.  The output is
 // rounded once to bf16 (nearest-even).
 //
-// Tiling: a workgroup computes a (128 WM) x 256 tile of Y with WM x 4
-// wavefronts; each wavefront owns a 128 x 64 block as 4 x 2
+// Two kernels share this arithmetic.
+//
+// w4a16_gemm_lds_kernel (K % 64 == 0 and group size 32, 64, 128 or a multiple
+// of 256): a workgroup of 8 wavefronts computes a 256 x 256 tile of Y; wavefront
+// (wm, wn) owns rows 128 wm .. +128 and columns 64 wn .. +64 as 4 x 2
 // v_mfma_f32_32x32x16_bf16 tiles.  K advances in 64-wide tiles through two LDS
-// stages: the activation tile is copied in (bf16, 144-byte padded rows), the
-// packed weight tile is expanded once per workgroup into exact bf16 (q - z), and
-// the tile's column scales are stored beside it.  Global loads run two tiles
-// ahead in registers; they are unconditional raw buffer loads (anything outside
-// the matrices reads as zero), so the compiler's wait counts stay exact.  When
-// K is a multiple of 64 the per-lane offsets are fixed and the k step (or the
-// past-the-end marker) is a wave-uniform scalar offset, which the hardware
-// range check includes; this keeps address arithmetic off the vector ALU,
-// which on this GPU barely overlaps with MFMA execution.  With
-// workgroups dealt round-robin to the 8 XCDs and the M tile varying fastest,
-// each XCD keeps the same activation rows in its L2.
+// stages.  The activation tile goes from memory straight into LDS (16-byte
+// buffer loads with the LDS destination), 16-byte chunks XOR-swizzled by row so
+// the MFMA operand reads are free of bank conflicts with 32 or 64 banks.  The
+// packed weights are loaded into registers one tile ahead and expanded into
+// exact bf16 (q - z) in the other LDS stage while the current tile's MFMAs run:
+// one 8-nibble word per 16-k step, scheduled between the MFMAs, and the group
+// rescale of each accumulator tile is placed right before its first MFMA of the
+// new group.  Vector work and MFMAs then overlap instead of alternating, which
+// matters because on this GPU only a few vector instructions per MFMA hide
+// behind its execution.  Group boundaries fall on fixed k steps for the
+// supported group sizes, so the boundary pattern is a template argument.
+//
+// w4a16_gemm_kernel (any other shape): a workgroup computes a (128 WM) x 256
+// tile with WM x 4 wavefronts, each owning a 128 x 64 block as 4 x 2 MFMA tiles.
+// K advances in 64-wide tiles through two LDS stages: the activation tile is
+// copied in (bf16, 144-byte padded rows), the packed weight tile is expanded
+// once per workgroup into exact bf16 (q - z), and the tile's column scales are
+// stored beside it.  Global loads run two tiles ahead in registers; they are
+// unconditional raw buffer loads (anything outside the matrices reads as zero),
+// so the compiler's wait counts stay exact.  When K is a multiple of 64 the
+// per-lane offsets are fixed and the k step (or the past-the-end marker) is a
+// wave-uniform scalar offset, which the hardware range check includes.
+//
+// In both, workgroups are dealt round-robin to the 8 XCDs with the M tile
+// varying fastest, so each XCD keeps the same activation rows in its L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "gq_internal.h"
 
@@ -314,6 +332,277 @@ __global__ __launch_bounds__(256 * WM, 2) void w4a16_gemm_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// 256 x 256 tile kernel with direct-to-LDS activations (K % 64 == 0)
+// ---------------------------------------------------------------------------
+
+constexpr int kLM = 256, kLN = 256, kLT = 512;  // tile rows, columns, threads
+constexpr int kLBRow = kBK + 8;                  // bf16 per expanded weight column (+16 B)
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt that bounds only the outstanding vector-memory operations
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// 8 nibbles (k = 0..7 at bits 4p) -> 8 exact bf16 values m (q - z) in k order,
+// with nz = -z m and m = 1, or m = 0 for a group whose scale is 0.
+__device__ __forceinline__ uint4 expand8m(uint32_t d, float m, float nz) {
+  const uint32_t e = d & 0x0F0F0F0Fu, o = (d >> 4) & 0x0F0F0F0Fu;
+  const float q0 = fmaf(ubyte_f32<0>(e), m, nz), q2 = fmaf(ubyte_f32<1>(e), m, nz);
+  const float q4 = fmaf(ubyte_f32<2>(e), m, nz), q6 = fmaf(ubyte_f32<3>(e), m, nz);
+  const float q1 = fmaf(ubyte_f32<0>(o), m, nz), q3 = fmaf(ubyte_f32<1>(o), m, nz);
+  const float q5 = fmaf(ubyte_f32<2>(o), m, nz), q7 = fmaf(ubyte_f32<3>(o), m, nz);
+  return make_uint4(pack_bf16(q0, q1), pack_bf16(q2, q3), pack_bf16(q4, q5), pack_bf16(q6, q7));
+}
+
+// Activation LDS tile: 16-byte chunk c of row r sits at position c ^ swz(r) of
+// the row's 128 bytes.  Sixteen consecutive rows read at one chunk touch 16
+// distinct 16-byte bank groups, eight consecutive rows 8 distinct ones.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+struct WStage {
+  uint4 b;        // 32 nibbles: one column, one 32-k half of a tile
+  uint16_t s, z;  // its group's scale and zero (fp16 bits)
+};
+
+// MODE: where groups start.  0: G = 32 (k steps 0 and 2 of every tile);
+// 1: G = 64 (every tile); 2: G = 128 (even tiles); 3: G a multiple of 256
+// (even tiles whose k0 is a multiple of G).
+template <bool SYM, int MODE>
+__global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
+    const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
+    uint16_t* __restrict__ y) {
+  __shared__ uint4 sA0[kLM * 8], sA1[kLM * 8];                        // 2 x 32 KiB
+  __shared__ uint4 sB0[kLN * kLBRow / 8], sB1[kLN * kLBRow / 8];      // 2 x 36 KiB
+  __shared__ float sC0[2 * kLN], sC1[2 * kLN];                        // scales per column half
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int ntm = (M + kLM - 1) / kLM;
+  const int m0 = (blockIdx.x % ntm) * kLM;
+  const int n0 = (blockIdx.x / ntm) * kLN;
+  const int ng = K / G;
+  const uint32_t rb = (uint32_t)K / 2;
+  const int T = K / kBK;
+
+  const rsrc_t rA = make_rsrc(x + (size_t)m0 * K, (uint64_t)(M - m0) * K * 2);
+  const rsrc_t rB = make_rsrc(qw + (size_t)n0 * rb, (uint64_t)(N - n0) * rb);
+  const rsrc_t rS = make_rsrc(scales + (size_t)n0 * ng, (uint64_t)(N - n0) * ng * 2);
+  const rsrc_t rZ = make_rsrc(SYM ? (const void*)scales : (const void*)(zeros + (size_t)n0 * ng),
+                              (uint64_t)(N - n0) * ng * 2);
+
+  // Activation DMA: LDS slot i*512 + tid (16 bytes) holds row slot/8 at
+  // position slot%8; a wavefront's load fills 1 KiB (8 rows) contiguously.
+  uint32_t voA[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int slot = i * kLT + tid;
+    const int r = slot >> 3, p = slot & 7;
+    voA[i] = (uint32_t)r * (uint32_t)K * 2u + (uint32_t)((p ^ swz(r)) * 16);
+  }
+  // Weights: a thread expands column tid/2, k half tid%2 of each tile.
+  const int bcol = tid >> 1, bhalf = tid & 1;
+  const uint32_t voB = (uint32_t)bcol * rb + (uint32_t)bhalf * 16u;
+  const uint32_t voS = (uint32_t)(bcol * ng) * 2u + (MODE == 0 && bhalf ? 2u : 0u);
+
+  auto issueA = [&](uint4* sA, int k0) {
+    // scalar offsets stay in SGPRs (a non-uniform soffset turns into a lane loop)
+    const uint32_t so = __builtin_amdgcn_readfirstlane(k0 < K ? (uint32_t)k0 * 2u : kOob);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)(sA + i * kLT + wave * 64), 16, voA[i],
+                                               so, 0, 0);
+  };
+  auto loadW = [&](WStage& S, int k0) {
+    const bool kin = k0 < K;
+    const uint32_t sb = __builtin_amdgcn_readfirstlane(kin ? (uint32_t)k0 / 2u : kOob);
+    const uint32_t sg = __builtin_amdgcn_readfirstlane(kin ? (uint32_t)(k0 / G) * 2u : kOob);
+    S.b = bload16(rB, voB, sb);
+    S.s = bload2(rS, voS, sg);
+    if (!SYM) S.z = bload2(rZ, voS, sg);
+  };
+  auto mult = [&](const WStage& S) { return (S.s & 0x7FFF) ? 1.f : 0.f; };
+  auto negz = [&](const WStage& S, float m) { return -(SYM ? 8.f : h2f(S.z)) * m; };
+  auto expand_all = [&](const WStage& S, uint4* sB, float* sC) {
+    const float m = mult(S), nz = negz(S, m);
+    uint4* d = sB + (bcol * kLBRow + bhalf * 32) / 8;
+    d[0] = expand8m(S.b.x, m, nz);
+    d[1] = expand8m(S.b.y, m, nz);
+    d[2] = expand8m(S.b.z, m, nz);
+    d[3] = expand8m(S.b.w, m, nz);
+    sC[bhalf * kLN + bcol] = h2f(S.s);
+  };
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  float cref[2];
+  const int lcol0 = wn * 64 + (lane & 31);
+
+  // factors moving the running sum from scale cref to the next group's scale
+  // (exactly 1 when no group starts here: use = false)
+  auto factors = [&](const float* sC, int half, float (&r)[2], bool use) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float sn = use ? sC[half * kLN + lcol0 + 32 * j] : cref[j];
+      const float cn = sn != 0.f ? sn : cref[j];
+      r[j] = cref[j] * __builtin_amdgcn_rcpf(cn);  // within 1 ulp of the quotient
+      cref[j] = cn;
+    }
+  };
+
+  // per-lane LDS offsets (uint4 units) of the MFMA operands
+  const int fl = swz(lane & 31);
+  const int arow = wm * 128 + (lane & 31);
+  int aoff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) aoff[ks] = arow * 8 + ((2 * ks + (lane >> 5)) ^ fl);
+  const int boff = (lcol0 * kLBRow + 8 * (lane >> 5)) / 8;
+
+  // One 64-k tile from (sA, sB, sC) while the next tile's weights Wn are expanded
+  // into (sBn, sCn).  R0 / R2: a group starts at k step 0 / 2.
+  auto tile = [&](auto R0c, auto R2c, const uint4* sA, const uint4* sB, const float* sC,
+                  const WStage& Wn, uint4* sBn, float* sCn, bool start) {
+    constexpr bool R0 = decltype(R0c)::value, R2 = decltype(R2c)::value;
+    float r0[2] = {1.f, 1.f}, r2[2] = {1.f, 1.f};
+    if (R0) factors(sC, 0, r0, start);
+    const float m = mult(Wn), nz = negz(Wn, m);
+    uint4* dn = sBn + (bcol * kLBRow + bhalf * 32) / 8;
+    bf16x8_t a[2][4], b[2][2];
+    auto ld = [&](int ks, int buf) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[buf][i] = __builtin_bit_cast(bf16x8_t, sA[aoff[ks] + i * 32 * 8]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[buf][j] = __builtin_bit_cast(bf16x8_t, sB[boff + ks * 2 + j * 32 * kLBRow / 8]);
+    };
+    ld(0, 0);
+    auto step = [&](auto KSc) {
+      constexpr int ks = decltype(KSc)::value;
+      constexpr bool RS = (R0 && ks == 0) || (R2 && ks == 2);
+      if (ks < 3) ld(ks + 1, (ks + 1) & 1);
+      if (R2 && ks == 2) factors(sC, 1, r2, true);
+      const uint32_t word = ks == 0 ? Wn.b.x : ks == 1 ? Wn.b.y : ks == 2 ? Wn.b.z : Wn.b.w;
+      const uint4 e = expand8m(word, m, nz);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if (R0 && ks == 0) acc[i][j] *= r0[j];
+          if (R2 && ks == 2) acc[i][j] *= r2[j];
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][i], b[ks & 1][j], acc[i][j],
+                                                              0, 0, 0);
+        }
+      dn[ks] = e;
+      // the next step's LDS reads first, then every MFMA behind its share of the
+      // vector work (its accumulator's rescale, the expansion)
+      if (ks < 3) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x2, RS ? 19 : 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
+    sCn[bhalf * kLN + bcol] = h2f(Wn.s);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  // Even tiles of modes 2 and 3 run the rescale step; in mode 3 its factors are
+  // exactly 1 unless a group starts (one code path keeps the registers in place).
+  auto tile_even = [&](int k0, const uint4* sA, const uint4* sB, const float* sC, const WStage& Wn,
+                       uint4* sBn, float* sCn) {
+    if constexpr (MODE == 0) tile(T_{}, T_{}, sA, sB, sC, Wn, sBn, sCn, true);
+    else tile(T_{}, F_{}, sA, sB, sC, Wn, sBn, sCn, MODE != 3 || k0 % G == 0);
+  };
+  auto tile_odd = [&](const uint4* sA, const uint4* sB, const float* sC, const WStage& Wn,
+                      uint4* sBn, float* sCn) {
+    if constexpr (MODE == 0) tile(T_{}, T_{}, sA, sB, sC, Wn, sBn, sCn, true);
+    else if constexpr (MODE == 1) tile(T_{}, F_{}, sA, sB, sC, Wn, sBn, sCn, true);
+    else tile(F_{}, F_{}, sA, sB, sC, Wn, sBn, sCn, false);
+  };
+
+  constexpr int nW = SYM ? 2 : 3;  // vector-memory loads per weight stage
+  WStage w0, w1;
+  issueA(sA0, 0);
+  loadW(w0, 0);
+  loadW(w1, kBK);
+  wait_vm<nW>();
+  expand_all(w0, sB0, sC0);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float c0 = sC0[lcol0 + 32 * j];
+    cref[j] = c0 != 0.f ? c0 : 1.f;  // the first tile's factors are then 1
+  }
+  // Tile t computes from stage t%2 while the DMA fills the other activation
+  // stage with tile t+1, the weights of tile t+1 (in registers since tile t-1)
+  // are expanded into the other weight stage, and tile t+2's weights load into
+  // the register stage just drained.  Pairs of tiles keep the stages static and
+  // the loop single-exit; an odd last tile runs after it.
+  int t = 0;
+  for (; t + 1 < T; t += 2) {
+    issueA(sA1, (t + 1) * kBK);
+    wait_vm<4 + nW>();
+    tile_even(t * kBK, sA0, sB0, sC0, w1, sB1, sC1);
+    loadW(w0, (t + 2) * kBK);
+    wait_vm<nW>();
+    __syncthreads();
+    issueA(sA0, (t + 2) * kBK);
+    wait_vm<4 + nW>();
+    tile_odd(sA1, sB1, sC1, w0, sB0, sC0);
+    loadW(w1, (t + 3) * kBK);
+    wait_vm<nW>();
+    __syncthreads();
+  }
+  if (t < T) tile_even(t * kBK, sA0, sB0, sC0, w1, sB1, sC1);
+
+  // lane holds column (lane & 31) and rows 8*(v/4) + 4*(lane/32) + v%4 of each MFMA tile
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int gn = n0 + lcol0 + 32 * j;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int gm = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (gm < M && gn < N) y[(size_t)gm * N + gn] = f32_to_bf16_rne(acc[i][j][v] * cref[j]);
+      }
+    }
+}
+
+template <bool SYM, int MODE>
+hipError_t launch_lds(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
+                      const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
+  const int64_t grid = (int64_t)((M + kLM - 1) / kLM) * ((N + kLN - 1) / kLN);
+  hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE>), dim3((unsigned)grid), dim3(kLT), 0, s, x,
+                     M, K, qw, sc, zr, N, G, y);
+  return hipGetLastError();
+}
+
+// Boundary pattern of the 256 x 256 kernel for this group size, or -1.
+int lds_mode(int K, int G) {
+  if (K % kBK != 0) return -1;
+  if (G == 32) return -1;  // two rescales per tile exceed the register budget
+  if (G == 64) return 1;
+  if (G == 128) return 2;
+  if (G % 256 == 0) return 3;
+  return -1;
+}
+
 template <int WM, bool SYM>
 hipError_t launch_t(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
                     const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
@@ -332,6 +621,12 @@ hipError_t launch_t(const uint16_t* x, int M, int K, const uint8_t* qw, const ui
 template <bool SYM>
 hipError_t dispatch(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
                     const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
+  switch (lds_mode(K, G)) {
+    case 1: return launch_lds<SYM, 1>(x, M, K, qw, sc, zr, N, G, y, s);
+    case 2: return launch_lds<SYM, 2>(x, M, K, qw, sc, zr, N, G, y, s);
+    case 3: return launch_lds<SYM, 3>(x, M, K, qw, sc, zr, N, G, y, s);
+    default: break;
+  }
   // 256-row tiles run two waves per SIMD and are faster per compute unit; the
   // 128-row tile (one wave per SIMD) wins when its tiles exactly fill the GPU
   // once while the 256-row tiles would leave compute units idle (measured on

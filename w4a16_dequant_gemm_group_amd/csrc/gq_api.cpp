@@ -194,6 +194,8 @@ gq_status gq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* 
                         uint16_t* y, void* stream) {
   if (gq_status s = check_w4_matmul(x, M, K, qweight, scales, zeros, N, p, y)) return s;
   if (K > kMaxGemmK || M > kMaxDim / 2) return GQ_ERR_UNSUPPORTED;
+  // one workgroup per output tile (128 or 256 rows x 256 columns)
+  if (((M + 127) / 128) * ((N + 255) / 256) > INT32_MAX) return GQ_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return GQ_OK;
   hipStream_t s = (hipStream_t)stream;
   if (gq_status st = check_device(s)) return st;
