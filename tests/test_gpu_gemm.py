@@ -102,3 +102,48 @@ def test_zero_scale_groups(G):
     assert np.all(bits16(y)[:, 0] & 0x7FFF == 0)
     assert_parity(bits16(y), ref, O.bf16_to_f64(x), wh, f"gemm zero-scale groups G={G}")
     assert_parity(bits16(yv), ref[:3], O.bf16_to_f64(x[:3]), wh, f"gemv zero-scale groups G={G}")
+
+
+@pytest.mark.parametrize("M,N,K,G,sym", [
+    (512, 512, 2048, 128, False),    # 4 tiles: K split in two halves of 16 tiles
+    (300, 700, 1216, 64, True),      # ragged, odd number of 64-k tiles, symmetric
+    (256, 256, 2560, 256, False),    # one tile, split on a 256-group boundary
+])
+def test_split_k_and_graph_capture(M, N, K, G, sym):
+    """Grids that fill at most half the GPU split K in two; both halves must
+    agree with the oracle.  Under graph capture the library hands out no
+    scratch, so the captured GEMM runs unsplit; every replay reproduces it."""
+    announce(f"gemm split-K M={M} N={N} K={K} G={G} sym={sym}")
+    w, _ = synth.weights(N, K, seed=K + 3)
+    x, _ = synth.activations(M, K, seed=M + 5, n_outlier_channels=4)
+    qw, s, z = _oracle_weights(w, G, sym)
+    xd, qd, sd = bf16_dev(x), u8_dev(qw), f16_dev(s)
+    zd = None if sym else f16_dev(z)
+    y_eager = B.gq_w4a16_gemm(xd, qd, sd, zd, G, sym)
+    y_again = B.gq_w4a16_gemm(xd, qd, sd, zd, G, sym)
+    torch.cuda.synchronize()
+    assert torch.equal(y_eager, y_again)  # the two-term combine does not depend on timing
+    ref = O.w4a16_reference(x, qw, s, None if sym else z, G, sym)
+    wh = O.dequantize_packed(qw, s, None if sym else z, G, sym)
+    assert_parity(bits16(y_eager), ref, O.bf16_to_f64(x), wh, f"split-K [{N},{K}] M={M}")
+
+    y_g = torch.empty_like(y_eager)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        B.gq_w4a16_gemm(xd, qd, sd, zd, G, sym, y=y_g)
+        with torch.cuda.graph(g, stream=stream):
+            B.gq_w4a16_gemm(xd, qd, sd, zd, G, sym, y=y_g)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    first = None
+    for rep in range(3):
+        y_g.zero_()
+        g.replay()
+        B.gq_w4a16_gemm(xd[:64], qd, sd, zd, G, sym)  # eager work between replays
+        torch.cuda.synchronize()
+        if first is None:
+            first = y_g.clone()
+            assert_parity(bits16(y_g), ref, O.bf16_to_f64(x), wh, f"captured [{N},{K}] M={M}")
+        assert torch.equal(y_g, first), f"replay {rep}"

@@ -371,11 +371,19 @@ struct WStage {
 // MODE: where groups start.  0: G = 32 (k steps 0 and 2 of every tile);
 // 1: G = 64 (every tile); 2: G = 128 (even tiles); 3: G a multiple of 256
 // (even tiles whose k0 is a multiple of G).
-template <bool SYM, int MODE>
+//
+// SPLIT: the grid holds two workgroups per output tile, the first covering
+// 64-k tiles [0, tsplit), the second [tsplit, K/64) (tsplit keeps whole
+// groups).  Each converts its running sum to the true scale; the first to finish
+// publishes it in `part` and raises the tile's flag, the second adds it to its
+// own (a sum of two terms, so the result does not depend on which finishes
+// first), writes Y and clears the tile's counter and flag for the next launch.
+// `sync` holds (counter, flag) per tile, zero between launches.
+template <bool SYM, int MODE, bool SPLIT>
 __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
-    uint16_t* __restrict__ y) {
+    uint16_t* __restrict__ y, uint32_t* __restrict__ sync, float* __restrict__ part, int tsplit) {
   __shared__ uint4 sA0[kLM * 8], sA1[kLM * 8];                        // 2 x 32 KiB
   __shared__ uint4 sB0[kLN * kLBRow / 8], sB1[kLN * kLBRow / 8];      // 2 x 36 KiB
   __shared__ float sC0[2 * kLN], sC1[2 * kLN];                        // scales per column half
@@ -384,11 +392,17 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
   const int ntm = (M + kLM - 1) / kLM;
-  const int m0 = (blockIdx.x % ntm) * kLM;
-  const int n0 = (blockIdx.x / ntm) * kLN;
+  const int ntiles = ntm * ((N + kLN - 1) / kLN);
+  const int split = SPLIT && (int)blockIdx.x >= ntiles;
+  const int tile_id = (int)blockIdx.x - split * ntiles;
+  const int m0 = (tile_id % ntm) * kLM;
+  const int n0 = (tile_id / ntm) * kLN;
   const int ng = K / G;
   const uint32_t rb = (uint32_t)K / 2;
-  const int T = K / kBK;
+  // this workgroup's 64-k tiles: [kt0, kt0 + T)
+  const int kt0 = SPLIT && split ? tsplit : 0;
+  const int T = SPLIT ? (split ? K / kBK - tsplit : tsplit) : K / kBK;
+  const int kb = kt0 * kBK;  // first k
 
   const rsrc_t rA = make_rsrc(x + (size_t)m0 * K, (uint64_t)(M - m0) * K * 2);
   const rsrc_t rB = make_rsrc(qw + (size_t)n0 * rb, (uint64_t)(N - n0) * rb);
@@ -537,9 +551,9 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
 
   constexpr int nW = SYM ? 2 : 3;  // vector-memory loads per weight stage
   WStage w0, w1;
-  issueA(sA0, 0);
-  loadW(w0, 0);
-  loadW(w1, kBK);
+  issueA(sA0, kb);
+  loadW(w0, kb);
+  loadW(w1, kb + kBK);
   wait_vm<nW>();
   expand_all(w0, sB0, sC0);
   __syncthreads();
@@ -553,22 +567,80 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
   // are expanded into the other weight stage, and tile t+2's weights load into
   // the register stage just drained.  Pairs of tiles keep the stages static and
   // the loop single-exit; an odd last tile runs after it.
+  // (kb is a multiple of the group size in tiles, so even/odd keep their roles)
   int t = 0;
   for (; t + 1 < T; t += 2) {
-    issueA(sA1, (t + 1) * kBK);
+    issueA(sA1, kb + (t + 1) * kBK);
     wait_vm<4 + nW>();
-    tile_even(t * kBK, sA0, sB0, sC0, w1, sB1, sC1);
-    loadW(w0, (t + 2) * kBK);
+    tile_even(kb + t * kBK, sA0, sB0, sC0, w1, sB1, sC1);
+    loadW(w0, kb + (t + 2) * kBK);
     wait_vm<nW>();
     __syncthreads();
-    issueA(sA0, (t + 2) * kBK);
+    issueA(sA0, kb + (t + 2) * kBK);
     wait_vm<4 + nW>();
     tile_odd(sA1, sB1, sC1, w0, sB0, sC0);
-    loadW(w1, (t + 3) * kBK);
+    loadW(w1, kb + (t + 3) * kBK);
     wait_vm<nW>();
     __syncthreads();
   }
-  if (t < T) tile_even(t * kBK, sA0, sB0, sC0, w1, sB1, sC1);
+  if (t < T) tile_even(kb + t * kBK, sA0, sB0, sC0, w1, sB1, sC1);
+
+  if constexpr (SPLIT) {
+    // Partial sums in the accumulator layout [tile][wave][128][lane], written
+    // and read as relaxed agent-scope atomics: those are coherent across the
+    // XCDs' L2 caches without the whole-cache write-back and invalidation that
+    // release/acquire fences would cost every other workgroup on the XCD.  The
+    // writer drains its stores before raising the flag; the reader loads the
+    // partials only after it has seen the flag.
+    float* slot = part + ((size_t)tile_id * 8 + wave) * 128 * 64 + lane;
+    __shared__ uint32_t s_first;
+    if (tid == 0) s_first = atomicAdd(&sync[2 * tile_id], 1u) == 0;
+    __syncthreads();
+    if (s_first) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            __hip_atomic_store(&slot[((i * 2 + j) * 16 + v) * 64], acc[i][j][v] * cref[j],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      wait_vm<0>();
+      __syncthreads();
+      if (tid == 0) __hip_atomic_store(&sync[2 * tile_id + 1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    // The other workgroup has already counted itself, so it is running and
+    // raises the flag after its stores; the bound only guards against a
+    // corrupted flag word.
+    if (tid == 0) {
+      for (int n = 0; n < (1 << 24); ++n) {
+        if (__hip_atomic_load(&sync[2 * tile_id + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
+    {
+#pragma clang fp contract(off)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            // round(a c) + round(a' c'): each half's product is rounded on its own
+            // (contraction off), so the sum does not depend on which half came first
+            const float o = __hip_atomic_load(&slot[((i * 2 + j) * 16 + v) * 64], __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+            acc[i][j][v] = acc[i][j][v] * cref[j] + o;
+          }
+    }
+    cref[0] = cref[1] = 1.f;  // acc now holds the true sum
+    if (tid == 0) {
+      sync[2 * tile_id] = 0;
+      sync[2 * tile_id + 1] = 0;
+    }
+  }
 
   // lane holds column (lane & 31) and rows 8*(v/4) + 4*(lane/32) + v%4 of each MFMA tile
 #pragma unroll
@@ -584,12 +656,30 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
     }
 }
 
+// Split K in two when the tiles fill at most half of the compute units and
+// each half keeps at least two groups' worth of 64-k tiles; the partial sums and
+// per-tile (counter, flag) words live in library scratch (not available while
+// the stream is captured: the tiles then run unsplit).
 template <bool SYM, int MODE>
 hipError_t launch_lds(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
                       const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
-  const int64_t grid = (int64_t)((M + kLM - 1) / kLM) * ((N + kLN - 1) / kLN);
-  hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE>), dim3((unsigned)grid), dim3(kLT), 0, s, x,
-                     M, K, qw, sc, zr, N, G, y);
+  const int64_t tiles = (int64_t)((M + kLM - 1) / kLM) * ((N + kLN - 1) / kLN);
+  const int T = K / kBK;
+  const int tpg = G >= kBK ? G / kBK : 1;  // 64-k tiles per group
+  const int tsplit = (T / 2) / std::max(tpg, 2) * std::max(tpg, 2);
+  if (2 * tiles <= num_cus() && tsplit >= 2 * tpg && T - tsplit >= 2 * tpg) {
+    const size_t sync_bytes = (size_t)((tiles * 8 + 255) / 256 * 256);
+    const size_t bytes = sync_bytes + (size_t)tiles * kLM * kLN * 4;
+    char* ws = (char*)stream_scratch(kScratchGemm, bytes, sync_bytes, s);
+    if (ws) {
+      hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE, true>), dim3((unsigned)(2 * tiles)),
+                         dim3(kLT), 0, s, x, M, K, qw, sc, zr, N, G, y, (uint32_t*)ws,
+                         (float*)(ws + sync_bytes), tsplit);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE, false>), dim3((unsigned)tiles), dim3(kLT), 0,
+                     s, x, M, K, qw, sc, zr, N, G, y, nullptr, nullptr, 0);
   return hipGetLastError();
 }
 

@@ -25,8 +25,6 @@
 // partial sums; a second kernel adds the slices in a fixed order (so the result
 // does not depend on scheduling) and rounds once to bf16 (nearest-even).
 #include <algorithm>
-#include <map>
-#include <mutex>
 #include <utility>
 
 #include "gq_internal.h"
@@ -267,32 +265,6 @@ __global__ __launch_bounds__(256) void gemv_split_finalize_kernel(const float* _
   y[i] = f32_to_bf16_rne(s);
 }
 
-// Split-K partial sums live in one buffer per (device, stream), grown on demand
-// and kept for the life of the process.  Calls on one stream are ordered;
-// different streams get different buffers.  While the stream is being
-// captured into a graph no allocation is made (nullptr: the caller takes
-// another path).
-void* split_workspace(size_t bytes, hipStream_t s) {
-  static std::mutex mu;
-  static std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> bufs;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-  std::lock_guard<std::mutex> lock(mu);
-  auto& b = bufs[{dev, s}];
-  if (b.second >= bytes) return b.first;
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
-  if (b.first) {
-    // the old buffer may still be read by work queued on s
-    if (hipStreamSynchronize(s) != hipSuccess) return nullptr;
-    hipFree(b.first);
-    b = {nullptr, 0};
-  }
-  void* p = nullptr;
-  if (hipMalloc(&p, bytes) != hipSuccess) return nullptr;
-  b = {p, bytes};
-  return p;
-}
 
 template <int CPG, bool SYM>
 hipError_t launch_cpg(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
@@ -333,7 +305,7 @@ hipError_t launch_w4a16_gemv_mfma(const uint16_t* x, int M, int64_t K, const uin
   *launched = false;
   const int splits = (int)((K + kKC - 1) / kKC);
   float* part = workspace ? (float*)workspace
-                          : (float*)split_workspace(gemv_workspace_bytes(M, K, N, G), s);
+                          : (float*)stream_scratch(kScratchGemv, gemv_workspace_bytes(M, K, N, G), 0, s);
   if (!part) return hipSuccess;  // no workspace (graph capture): the caller falls back
   hipError_t e;
   const int k = (int)K, n = (int)N;

@@ -1,8 +1,12 @@
 // C ABI of libgq: argument validation, device check and dispatch to the
 // kernels.  Validation runs entirely on the host before any HIP call, so an
 // invalid call never touches the device (and can be exercised without one).
+#include <algorithm>
 #include <atomic>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "gq_internal.h"
 
@@ -67,6 +71,38 @@ gq_status check_w4_matmul(const uint16_t* x, int64_t M, int64_t K, const uint8_t
 }  // namespace
 
 namespace gq {
+
+// Library scratch: one buffer per (device, stream, slot), grown on demand and
+// kept for the life of the process.  Calls on one stream are ordered; different
+// streams get different buffers.  A new buffer's first zero_bytes are cleared
+// (on s) before first use.  While s is being captured into a graph nullptr is
+// returned, even when a buffer exists (the caller takes another path): a graph
+// must not hold a buffer that a later, larger call on the stream would free.
+void* stream_scratch(int slot, size_t bytes, size_t zero_bytes, hipStream_t s) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, hipStream_t, int>, std::pair<void*, size_t>> bufs;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  auto& b = bufs[{dev, s, slot}];
+  if (b.second >= bytes) return b.first;
+  if (b.first) {
+    // the old buffer may still be used by work queued on s
+    if (hipStreamSynchronize(s) != hipSuccess) return nullptr;
+    hipFree(b.first);
+    b = {nullptr, 0};
+  }
+  void* p = nullptr;
+  if (hipMalloc(&p, bytes) != hipSuccess) return nullptr;
+  if (zero_bytes && hipMemsetAsync(p, 0, std::min(zero_bytes, bytes), s) != hipSuccess) {
+    hipFree(p);
+    return nullptr;
+  }
+  b = {p, bytes};
+  return p;
+}
 
 int num_cus() {
   int dev = 0;

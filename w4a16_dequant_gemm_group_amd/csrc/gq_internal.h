@@ -92,6 +92,10 @@ __device__ __forceinline__ double load_elem_f64(const void* p, int64_t i, gq_dty
 // Compute units of the current device (set by the C ABI's device check).
 int num_cus();
 
+// Library scratch per (device, stream, slot); nullptr while s is being captured.
+enum { kScratchGemv = 0, kScratchGemm = 1 };
+void* stream_scratch(int slot, size_t bytes, size_t zero_bytes, hipStream_t s);
+
 // ---------------------------------------------------------------------------
 // Launchers (arguments already validated by the C ABI layer)
 // ---------------------------------------------------------------------------
