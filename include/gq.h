@@ -123,6 +123,22 @@ gq_status gq_dequantize(const uint8_t* qweight, const uint16_t* scales, const ui
                         int64_t N, int64_t K, gq_qparams p, void* w_hat, gq_dtype out_dtype,
                         void* stream);
 
+/* Ingest of another layout into the canonical one [P2 "亲手实现": its fused
+ * matmul keeps int8 codes [n_groups, group, N] (K-major, N contiguous) and fp16
+ * scales [n_groups, N] from the symmetric quantizer of "核心思路"]:
+ *   codes      [n_groups, group, N] int8, 4-bit symmetric codes -8..7
+ *   scales     [n_groups, N] fp16
+ *   qweight    [N, K/2] symmetric packed form (nibble = code + 8, low nibble =
+ *              even k), K = n_groups * group; 16-byte aligned
+ *   scales_out [N, n_groups] fp16
+ * The result serves gq_w4a16_gemv / gq_w4a16_gemm with symmetric = 1 and
+ * group_size = group.  Codes outside -8..7 are masked to 4 bits, as in
+ * gq_pack_int4.  Errors: INVALID_ARG (group % 32 != 0, shapes, NULL),
+ * MISALIGNED, UNSUPPORTED (device). */
+gq_status gq_ingest_group_major(const int8_t* codes, const uint16_t* scales, int64_t n_groups,
+                                int64_t group, int64_t N, uint8_t* qweight, uint16_t* scales_out,
+                                void* stream);
+
 /* Fused W4A16 GEMV for decode, 1 <= M <= 16 [P1 sec.2 fused-kernel paragraph;
  * P2 "工作原理" figure right panel and "亲手实现"; P3 "直接答案" (decode is
  * memory-bound)]:
@@ -169,6 +185,20 @@ gq_status gq_w4a16_gemv_ws(const uint16_t* x, int64_t M, int64_t K, const uint8_
 gq_status gq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
                         const uint16_t* scales, const uint16_t* zeros, int64_t N, gq_qparams p,
                         uint16_t* y, void* stream);
+
+/* The fused matmuls with fp16 activations and fp16 output [P1 sec.2: the
+ * fused kernel multiplies BF16/FP16 activations]: the same product as
+ * gq_w4a16_gemv / gq_w4a16_gemm, x [M, K] fp16 and y [M, N] fp16 (rounded to
+ * nearest even; overflow gives +-inf), fp32 accumulation.  Supported shapes:
+ * gq_w4a16_gemv_f16 for M = 1 (K up to 26624); gq_w4a16_gemm_f16 for K % 64
+ * == 0 and group_size 64, 128 or a multiple of 256.  Other shapes return
+ * UNSUPPORTED.  Errors otherwise as the bf16 entry points. */
+gq_status gq_w4a16_gemv_f16(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                            const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                            gq_qparams p, uint16_t* y, void* stream);
+gq_status gq_w4a16_gemm_f16(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                            const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                            gq_qparams p, uint16_t* y, void* stream);
 
 /* Nested 4-bit super-block format [P2 "工作原理" figure, middle panel: 256
  * weights = 8 sub-blocks of 32, 6-bit scale and 6-bit min per sub-block, fp16

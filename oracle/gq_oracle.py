@@ -225,6 +225,19 @@ def w4a16_reference(x_bits, qweight, scales_bits, zeros_bits, group_size: int,
     return matmul_groupwise(bf16_to_f64(x_bits), w_hat, group_size)
 
 
+def ingest_group_major(codes_gkn, scales_gn_bits):
+    """The "量化" chapter's "亲手实现" layout -> the canonical one.
+
+    codes [n_groups, group, N] signed integers (its symmetric quantizer: -8..7 at
+    4 bits), scales [n_groups, N] fp16 bits -> (qweight uint8 [N, K/2] with
+    offset-binary nibbles, scales [N, n_groups] fp16 bits), K = n_groups * group.
+    Row n of the weight is column n of every group's [group, N] slab."""
+    c = np.asarray(codes_gkn, dtype=np.int64)
+    ng, g, n = c.shape
+    codes_nk = c.reshape(ng * g, n).T
+    return pack_int4(codes_nk, True), np.ascontiguousarray(np.asarray(scales_gn_bits, dtype=np.uint16).T)
+
+
 def quantize_to_storage(w_bits, bits, group_size, symmetric):
     """bf16 weight -> (codes, fp16 scale bits, fp16 zero bits or None) per R1-R5."""
     codes, s, z = quantize_groups(bf16_to_f64(w_bits), bits, group_size, symmetric)

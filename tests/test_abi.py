@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 12
+    assert len(names) == 15
     assert set(names) == set(B.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -163,3 +163,29 @@ def test_bench_entry_point_validation(lib):
     assert L.gq_stream_read(FAKE, 64, ctypes.c_void_p(4098), None) == B.GQ_ERR_MISALIGNED
     assert L.gq_stream_read(FAKE, 64, None, None) == B.GQ_ERR_INVALID_ARG
     assert L.gq_stream_read(None, 0, None, None) == B.GQ_OK
+
+
+
+def test_ingest_validation(lib):
+    L = lib
+    assert L.gq_ingest_group_major(FAKE, FAKE, 4, 48, 64, FAKE, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_ingest_group_major(FAKE, FAKE, 0, 32, 64, FAKE, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_ingest_group_major(FAKE, FAKE, 4, 32, -1, FAKE, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_ingest_group_major(None, FAKE, 4, 32, 64, FAKE, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_ingest_group_major(FAKE, FAKE, 4, 32, 64, FAKE_MIS, FAKE, None) == B.GQ_ERR_MISALIGNED
+    assert L.gq_ingest_group_major(None, None, 4, 32, 0, None, None, None) == B.GQ_OK
+
+
+
+def test_f16_entry_point_validation(lib):
+    L = lib
+    args = (FAKE, 1, 4096, FAKE, FAKE, FAKE, 4096)
+    # only M = 1 for the GEMV, only the 256x256 kernel's shapes for the GEMM
+    assert L.gq_w4a16_gemv_f16(FAKE, 2, 4096, FAKE, FAKE, FAKE, 4096, q(), FAKE, None) == B.GQ_ERR_UNSUPPORTED
+    assert L.gq_w4a16_gemv_f16(FAKE, 17, 4096, FAKE, FAKE, FAKE, 4096, q(), FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_w4a16_gemv_f16(FAKE, 1, 28672, FAKE, FAKE, FAKE, 64, q(), FAKE, None) == B.GQ_ERR_UNSUPPORTED
+    assert L.gq_w4a16_gemm_f16(FAKE, 64, 4096, FAKE, FAKE, FAKE, 4096, q(g=32), FAKE, None) == B.GQ_ERR_UNSUPPORTED
+    assert L.gq_w4a16_gemm_f16(FAKE, 64, 4128, FAKE, FAKE, FAKE, 4096, q(g=96), FAKE, None) == B.GQ_ERR_UNSUPPORTED
+    assert L.gq_w4a16_gemm_f16(FAKE_MIS, 64, 4096, FAKE, FAKE, FAKE, 4096, q(), FAKE, None) == B.GQ_ERR_MISALIGNED
+    assert L.gq_w4a16_gemm_f16(FAKE, 64, 4096, FAKE, FAKE, None, 4096, q(), FAKE, None) == B.GQ_ERR_INVALID_ARG
+    del args

@@ -1,0 +1,74 @@
+"""GPU parity of the fused matmuls with fp16 activations and fp16 output
+(gq_w4a16_gemv_f16 at M = 1, gq_w4a16_gemm_f16) against the oracle's float64
+group-by-group product of the same fp16 activations and exact dequantized
+weight, to the matmul parity bar."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import announce, device
+from oracle import gq_oracle as O
+from w4a16_dequant_gemm_group_amd import binding as B
+from w4a16_dequant_gemm_group_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _f16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(
+        torch.float16).to(device())
+
+
+def _weights(n, k, G, sym, seed):
+    w, _ = synth.weights(n, k, seed=seed)
+    codes, s, z = O.quantize_to_storage(w, 4, G, sym)
+    return O.pack_int4(codes, sym), s, z
+
+
+def _check(y, x_bits, qw, s, z, G, sym, what):
+    x64 = O.f16_to_f64(x_bits)
+    wh = O.dequantize_packed(qw, s, z, G, sym)
+    ref = O.matmul_groupwise(x64, wh, G)
+    yv = O.f16_to_f64(y.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+    ok, rel, ratio = O.within_parity(yv, ref, x64, wh)
+    announce(f"{what}: relF={rel:.3e} max/allowed={ratio:.3f}")
+    assert ok, (what, rel, ratio)
+
+
+@pytest.mark.parametrize("N,K,G,sym", [
+    (203, 6144, 128, False),
+    (4096, 14336, 32, True),
+    (130, 6400, 64, False),     # K not a multiple of 2048: per-lane offset tables
+    (1, 2048, 2048, True),
+])
+def test_gemv_f16(N, K, G, sym):
+    qw, s, z = _weights(N, K, G, sym, seed=N + K)
+    x, _ = synth.activations_f16(1, K, seed=K, n_outlier_channels=2)
+    y = B.gq_w4a16_gemv_f16(_f16_dev(x), torch.from_numpy(qw).to(device()), _f16_dev(s),
+                            None if sym else _f16_dev(z), G, sym)
+    torch.cuda.synchronize()
+    assert y.dtype == torch.float16
+    _check(y, x, qw, s, None if sym else z, G, sym, f"gemv f16 [{N},{K}] G={G} sym={sym}")
+
+
+@pytest.mark.parametrize("M,N,K,G,sym", [
+    (300, 260, 640, 128, False),     # ragged, split K
+    (2048, 512, 4096, 128, False),
+    (96, 300, 1216, 64, True),       # odd number of k tiles
+    (257, 131, 512, 512, False),
+])
+def test_gemm_f16(M, N, K, G, sym):
+    qw, s, z = _weights(N, K, G, sym, seed=M + N)
+    x, _ = synth.activations_f16(M, K, seed=M, n_outlier_channels=4)
+    y = B.gq_w4a16_gemm_f16(_f16_dev(x), torch.from_numpy(qw).to(device()), _f16_dev(s),
+                            None if sym else _f16_dev(z), G, sym)
+    torch.cuda.synchronize()
+    assert y.dtype == torch.float16
+    _check(y, x, qw, s, None if sym else z, G, sym, f"gemm f16 M={M} [{N},{K}] G={G} sym={sym}")
+
+
+def test_f16_unsupported_shapes_raise():
+    qw, s, z = _weights(64, 4096, 32, False, seed=1)
+    x, _ = synth.activations_f16(64, 4096, seed=2)
+    with pytest.raises(RuntimeError):   # G = 32 stays on the bf16-only GEMM kernel
+        B.gq_w4a16_gemm_f16(_f16_dev(x), torch.from_numpy(qw).to(device()), _f16_dev(s), _f16_dev(z), 32, False)

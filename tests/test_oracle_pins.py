@@ -453,3 +453,25 @@ def test_bf16_half_ulp_closed_form():
     v = rng.normal(0, 10, 5000).astype(np.float32).astype(np.float64)
     r = O.bf16_to_f64(O.f32_exact_to_bf16_bits(v))
     assert np.all(np.abs(r - v) <= O.bf16_half_ulp(v))
+
+
+def test_group_major_ingest_preserves_the_product():
+    """The chapter's layout (codes [n_groups, group, N], scales [n_groups, N]) and
+    its group-by-group product out += x[:, g] @ (q[g] * s[g]) must give, after
+    ingest into [N, K/2] + [N, K/G], exactly the canonical oracle product; a
+    transposed slab or a swapped nibble would not."""
+    rng = np.random.default_rng(11)
+    ng, g, n, m = 5, 32, 24, 3
+    codes = rng.integers(-8, 8, size=(ng, g, n))
+    scales = O.f64_to_f16_bits(rng.uniform(0.001, 0.05, size=(ng, n)))
+    x = O.f32_exact_to_bf16_bits(rng.normal(size=(m, ng * g)).astype(np.float32).astype(np.float64))
+    xf = O.bf16_to_f64(x)
+    s = O.f16_to_f64(scales)
+    page = np.zeros((m, n))
+    for gi in range(ng):   # the page's fused form, written independently of the oracle
+        page += xf[:, gi * g:(gi + 1) * g] @ (codes[gi].astype(np.float64) * s[gi])
+    qw, sc = O.ingest_group_major(codes, scales)
+    assert qw.shape == (n, ng * g // 2) and sc.shape == (n, ng)
+    assert np.array_equal(O.unpack_int4(qw, True)[3, 32:64], codes[1, :, 3])
+    canon = O.w4a16_reference(x, qw, sc, None, g, True)
+    assert np.allclose(canon, page, rtol=1e-12, atol=1e-12)

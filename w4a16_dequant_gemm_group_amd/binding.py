@@ -24,7 +24,8 @@ GQ_F32, GQ_F16, GQ_BF16 = 0, 1, 2
 EXPORTS = (
     "gq_status_str", "gq_version", "gq_packed_sizes", "gq_quantize_groups", "gq_pack_int4",
     "gq_dequantize", "gq_w4a16_gemv", "gq_w4a16_gemv_workspace_size", "gq_w4a16_gemv_ws",
-    "gq_w4a16_gemm", "gq_q4k_quantize", "gq_q4k_gemv",
+    "gq_w4a16_gemm", "gq_q4k_quantize", "gq_q4k_gemv", "gq_ingest_group_major",
+    "gq_w4a16_gemv_f16", "gq_w4a16_gemm_f16",
 )
 # comparators and probes (include/gq_bench.h)
 BENCH_EXPORTS = ("gq_bf16_gemv", "gq_stream_read")
@@ -70,6 +71,9 @@ def lib() -> ctypes.CDLL:
         "gq_q4k_quantize": [p, c, i64, i64, p, p],
         "gq_q4k_gemv": [p, i64, i64, p, i64, p, p],
         "gq_bf16_gemv": [p, i64, i64, p, i64, p, p],
+        "gq_ingest_group_major": [p, p, i64, i64, i64, p, p, p],
+        "gq_w4a16_gemv_f16": [p, i64, i64, p, p, p, i64, Q, p, p],
+        "gq_w4a16_gemm_f16": [p, i64, i64, p, p, p, i64, Q, p, p],
         "gq_stream_read": [p, i64, p, p],
     }
     for name, args in sig.items():
@@ -172,8 +176,9 @@ def gq_dequantize(qweight: torch.Tensor, scales: torch.Tensor, zeros: Optional[t
     return out
 
 
-def _matmul(fn, name, x, qweight, scales, zeros, group_size, symmetric, y, stream):
-    _need(x, "x", (torch.bfloat16,))
+def _matmul(fn, name, x, qweight, scales, zeros, group_size, symmetric, y, stream,
+            xdtype=torch.bfloat16):
+    _need(x, "x", (xdtype,))
     _need(qweight, "qweight", (torch.uint8,), x.device)
     _need(scales, "scales", (torch.float16,), x.device)
     if zeros is not None:
@@ -183,7 +188,7 @@ def _matmul(fn, name, x, qweight, scales, zeros, group_size, symmetric, y, strea
     if qweight.shape[1] * 2 != K:
         raise ValueError(f"qweight {tuple(qweight.shape)} does not match K={K}")
     if y is None:
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+        y = torch.empty((M, N), dtype=xdtype, device=x.device)
     _check(fn(_ptr(x), M, K, _ptr(qweight), _ptr(scales), _ptr(zeros), N,
               qparams(4, group_size, symmetric), _ptr(y), _stream(stream)), name)
     return y
@@ -237,6 +242,20 @@ def gq_w4a16_gemm(x, qweight, scales, zeros, group_size: int = 128, symmetric: b
                    group_size, symmetric, y, stream)
 
 
+def gq_w4a16_gemv_f16(x, qweight, scales, zeros, group_size: int = 128, symmetric: bool = False,
+                      y=None, stream=None):
+    """Fused W4A16 GEMV with fp16 activations, x fp16 [1, K] -> y fp16 [1, N]."""
+    return _matmul(lib().gq_w4a16_gemv_f16, "gq_w4a16_gemv_f16", x, qweight, scales, zeros,
+                   group_size, symmetric, y, stream, torch.float16)
+
+
+def gq_w4a16_gemm_f16(x, qweight, scales, zeros, group_size: int = 128, symmetric: bool = False,
+                      y=None, stream=None):
+    """Fused W4A16 GEMM with fp16 activations (fp16 MFMA), x fp16 [M, K] -> y fp16 [M, N]."""
+    return _matmul(lib().gq_w4a16_gemm_f16, "gq_w4a16_gemm_f16", x, qweight, scales, zeros,
+                   group_size, symmetric, y, stream, torch.float16)
+
+
 def gq_q4k_quantize(w: torch.Tensor, blocks=None, stream=None):
     """w [N, K] (K % 256 == 0) -> blocks uint8 [N, K/256, 144]."""
     _need(w, "w", tuple(_DT))
@@ -283,3 +302,21 @@ def gq_stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     _need(sink, "sink", (torch.int32, torch.uint32), buf.device)
     nbytes = buf.numel() * buf.element_size()
     _check(lib().gq_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "gq_stream_read")
+
+
+def gq_ingest_group_major(codes: torch.Tensor, scales: torch.Tensor, qweight=None, scales_out=None,
+                          stream=None):
+    """Group-major codes int8 [n_groups, group, N] + scales fp16 [n_groups, N] ->
+    (qweight uint8 [N, K/2], scales fp16 [N, n_groups]), symmetric, K = n_groups * group."""
+    _need(codes, "codes", (torch.int8,))
+    _need(scales, "scales", (torch.float16,), codes.device)
+    ng, g, N = codes.shape
+    if tuple(scales.shape) != (ng, N):
+        raise ValueError(f"scales is {tuple(scales.shape)}, expected ({ng}, {N})")
+    if qweight is None:
+        qweight = torch.empty((N, ng * g // 2), dtype=torch.uint8, device=codes.device)
+    if scales_out is None:
+        scales_out = torch.empty((N, ng), dtype=torch.float16, device=codes.device)
+    _check(lib().gq_ingest_group_major(_ptr(codes), _ptr(scales), ng, g, N, _ptr(qweight),
+                                       _ptr(scales_out), _stream(stream)), "gq_ingest_group_major")
+    return qweight, scales_out

@@ -63,6 +63,7 @@ constexpr int kBN = 256;
 constexpr uint32_t kOob = 0x80000000u;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -347,15 +348,36 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// 8 nibbles (k = 0..7 at bits 4p) -> 8 exact bf16 values m (q - z) in k order,
-// with nz = -z m and m = 1, or m = 0 for a group whose scale is 0.
+// two fp32 holding small integers -> packed fp16 pair (exact)
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
+// 8 nibbles (k = 0..7 at bits 4p) -> 8 exact bf16 (or, XF16, fp16) values
+// m (q - z) in k order, with nz = -z m and m = 1, or m = 0 for a group whose
+// scale is 0.
+template <bool XF16>
 __device__ __forceinline__ uint4 expand8m(uint32_t d, float m, float nz) {
   const uint32_t e = d & 0x0F0F0F0Fu, o = (d >> 4) & 0x0F0F0F0Fu;
   const float q0 = fmaf(ubyte_f32<0>(e), m, nz), q2 = fmaf(ubyte_f32<1>(e), m, nz);
   const float q4 = fmaf(ubyte_f32<2>(e), m, nz), q6 = fmaf(ubyte_f32<3>(e), m, nz);
   const float q1 = fmaf(ubyte_f32<0>(o), m, nz), q3 = fmaf(ubyte_f32<1>(o), m, nz);
   const float q5 = fmaf(ubyte_f32<2>(o), m, nz), q7 = fmaf(ubyte_f32<3>(o), m, nz);
+  if (XF16) return make_uint4(pack_f16(q0, q1), pack_f16(q2, q3), pack_f16(q4, q5), pack_f16(q6, q7));
   return make_uint4(pack_bf16(q0, q1), pack_bf16(q2, q3), pack_bf16(q4, q5), pack_bf16(q6, q7));
+}
+
+// 32 x 32 x 16 MFMA on 8-element operand registers of bf16 or fp16
+template <bool XF16>
+using opnd8_t = typename std::conditional<XF16, f16x8_t, bf16x8_t>::type;
+
+template <bool XF16>
+__device__ __forceinline__ f32x16_t mfma32(const opnd8_t<XF16>& a, const opnd8_t<XF16>& b,
+                                           const f32x16_t& c) {
+  if constexpr (XF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // Activation LDS tile: 16-byte chunk c of row r sits at position c ^ swz(r) of
@@ -379,7 +401,8 @@ struct WStage {
 // own (a sum of two terms, so the result does not depend on which finishes
 // first), writes Y and clears the tile's counter and flag for the next launch.
 // `sync` holds (counter, flag) per tile, zero between launches.
-template <bool SYM, int MODE, bool SPLIT>
+// XF16: fp16 activations and output (fp16 MFMA), otherwise bf16.
+template <bool SYM, int MODE, bool SPLIT, bool XF16 = false>
 __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
@@ -445,10 +468,10 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
   auto expand_all = [&](const WStage& S, uint4* sB, float* sC) {
     const float m = mult(S), nz = negz(S, m);
     uint4* d = sB + (bcol * kLBRow + bhalf * 32) / 8;
-    d[0] = expand8m(S.b.x, m, nz);
-    d[1] = expand8m(S.b.y, m, nz);
-    d[2] = expand8m(S.b.z, m, nz);
-    d[3] = expand8m(S.b.w, m, nz);
+    d[0] = expand8m<XF16>(S.b.x, m, nz);
+    d[1] = expand8m<XF16>(S.b.y, m, nz);
+    d[2] = expand8m<XF16>(S.b.z, m, nz);
+    d[3] = expand8m<XF16>(S.b.w, m, nz);
     sC[bhalf * kLN + bcol] = h2f(S.s);
   };
 
@@ -491,13 +514,13 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
     if (R0) factors(sC, 0, r0, start);
     const float m = mult(Wn), nz = negz(Wn, m);
     uint4* dn = sBn + (bcol * kLBRow + bhalf * 32) / 8;
-    bf16x8_t a[2][4], b[2][2];
+    opnd8_t<XF16> a[2][4], b[2][2];
     auto ld = [&](int ks, int buf) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[buf][i] = __builtin_bit_cast(bf16x8_t, sA[aoff[ks] + i * 32 * 8]);
+      for (int i = 0; i < 4; ++i) a[buf][i] = __builtin_bit_cast(opnd8_t<XF16>, sA[aoff[ks] + i * 32 * 8]);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        b[buf][j] = __builtin_bit_cast(bf16x8_t, sB[boff + ks * 2 + j * 32 * kLBRow / 8]);
+        b[buf][j] = __builtin_bit_cast(opnd8_t<XF16>, sB[boff + ks * 2 + j * 32 * kLBRow / 8]);
     };
     ld(0, 0);
     auto step = [&](auto KSc) {
@@ -506,15 +529,14 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
       if (ks < 3) ld(ks + 1, (ks + 1) & 1);
       if (R2 && ks == 2) factors(sC, 1, r2, true);
       const uint32_t word = ks == 0 ? Wn.b.x : ks == 1 ? Wn.b.y : ks == 2 ? Wn.b.z : Wn.b.w;
-      const uint4 e = expand8m(word, m, nz);
+      const uint4 e = expand8m<XF16>(word, m, nz);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           if (R0 && ks == 0) acc[i][j] *= r0[j];
           if (R2 && ks == 2) acc[i][j] *= r2[j];
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][i], b[ks & 1][j], acc[i][j],
-                                                              0, 0, 0);
+          acc[i][j] = mfma32<XF16>(a[ks & 1][i], b[ks & 1][j], acc[i][j]);
         }
       dn[ks] = e;
       // the next step's LDS reads first, then every MFMA behind its share of the
@@ -651,7 +673,10 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int gm = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (gm < M && gn < N) y[(size_t)gm * N + gn] = f32_to_bf16_rne(acc[i][j][v] * cref[j]);
+        if (gm < M && gn < N) {
+          const float v_ = acc[i][j][v] * cref[j];
+          y[(size_t)gm * N + gn] = XF16 ? __builtin_bit_cast(uint16_t, (_Float16)v_) : f32_to_bf16_rne(v_);
+        }
       }
     }
 }
@@ -660,7 +685,7 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
 // each half keeps at least two groups' worth of 64-k tiles; the partial sums and
 // per-tile (counter, flag) words live in library scratch (not available while
 // the stream is captured: the tiles then run unsplit).
-template <bool SYM, int MODE>
+template <bool SYM, int MODE, bool XF16 = false>
 hipError_t launch_lds(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
                       const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
   const int64_t tiles = (int64_t)((M + kLM - 1) / kLM) * ((N + kLN - 1) / kLN);
@@ -672,13 +697,13 @@ hipError_t launch_lds(const uint16_t* x, int M, int K, const uint8_t* qw, const 
     const size_t bytes = sync_bytes + (size_t)tiles * kLM * kLN * 4;
     char* ws = (char*)stream_scratch(kScratchGemm, bytes, sync_bytes, s);
     if (ws) {
-      hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE, true>), dim3((unsigned)(2 * tiles)),
+      hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE, true, XF16>), dim3((unsigned)(2 * tiles)),
                          dim3(kLT), 0, s, x, M, K, qw, sc, zr, N, G, y, (uint32_t*)ws,
                          (float*)(ws + sync_bytes), tsplit);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE, false>), dim3((unsigned)tiles), dim3(kLT), 0,
+  hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE, false, XF16>), dim3((unsigned)tiles), dim3(kLT), 0,
                      s, x, M, K, qw, sc, zr, N, G, y, nullptr, nullptr, 0);
   return hipGetLastError();
 }
@@ -728,6 +753,27 @@ hipError_t dispatch(const uint16_t* x, int M, int K, const uint8_t* qw, const ui
 }
 
 }  // namespace
+
+bool gemm_f16_supported(int64_t K, int G) { return lds_mode((int)K, G) >= 0; }
+
+template <bool SYM>
+hipError_t dispatch_f16(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
+                        const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
+  switch (lds_mode(K, G)) {
+    case 1: return launch_lds<SYM, 1, true>(x, M, K, qw, sc, zr, N, G, y, s);
+    case 2: return launch_lds<SYM, 2, true>(x, M, K, qw, sc, zr, N, G, y, s);
+    case 3: return launch_lds<SYM, 3, true>(x, M, K, qw, sc, zr, N, G, y, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_w4a16_gemm_f16(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                                 const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
+                                 int symmetric, uint16_t* y, hipStream_t s) {
+  if (symmetric)
+    return dispatch_f16<true>(x, (int)M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
+  return dispatch_f16<false>(x, (int)M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
+}
 
 hipError_t launch_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
                              const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,

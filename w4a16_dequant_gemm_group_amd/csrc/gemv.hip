@@ -42,10 +42,17 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kStepK = 2048;   // k covered by one wave load (64 lanes x 32)
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// fp16 pairs: v_dot2_f32_f16 (fp32 accumulation)
+__device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c,
+                                false);
 }
 
 // 8 nibbles of one dword (k offsets 0..7 at bits 4p) against the permuted
@@ -226,10 +233,19 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 
 // 8 nibbles (k = 0..7 at bits 4p) against activation pairs (x0,x2) (x4,x6)
 // (x1,x3) (x5,x7): the even and odd nibbles are split into bytes, and each
-// byte pair gets the exponent byte 0x43 from `magic` (0x43004300) by v_perm.
+// byte pair gets an exponent byte from `magic` by v_perm: 0x43 makes the bf16
+// value 128 + q (magic 0x43004300), 0x64 the fp16 value 1024 + q (0x64006400);
+// both are exact.  XF16: fp16 activations.
+template <bool XF16 = false>
 __device__ __forceinline__ float dot8_perm(uint32_t d, const uint4& xp, float a, uint32_t magic) {
   const uint32_t ev = d & 0x0F0F0F0Fu;
   const uint32_t od = (d >> 4) & 0x0F0F0F0Fu;
+  if (XF16) {
+    a = dot2h(__builtin_amdgcn_perm(ev, magic, 0x01050104u), xp.x, a);
+    a = dot2h(__builtin_amdgcn_perm(ev, magic, 0x01070106u), xp.y, a);
+    a = dot2h(__builtin_amdgcn_perm(od, magic, 0x01050104u), xp.z, a);
+    return dot2h(__builtin_amdgcn_perm(od, magic, 0x01070106u), xp.w, a);
+  }
   a = dot2(__builtin_amdgcn_perm(ev, magic, 0x01050104u), xp.x, a);
   a = dot2(__builtin_amdgcn_perm(ev, magic, 0x01070106u), xp.y, a);
   a = dot2(__builtin_amdgcn_perm(od, magic, 0x01050104u), xp.z, a);
@@ -245,6 +261,19 @@ __device__ __forceinline__ uint4 perm_x_pairs(uint4 v) {
   p.z = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);
   p.w = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);
   return p;
+}
+
+__device__ __forceinline__ float sum_f16x8(uint4 v) {
+  auto h = [](uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); };
+  float s = h(v.x & 0xFFFFu) + h(v.x >> 16);
+  s += h(v.y & 0xFFFFu) + h(v.y >> 16);
+  s += h(v.z & 0xFFFFu) + h(v.z >> 16);
+  s += h(v.w & 0xFFFFu) + h(v.w >> 16);
+  return s;
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
 __device__ __forceinline__ float sum_bf16x8(uint4 v) {
@@ -315,7 +344,7 @@ __device__ __forceinline__ void stream_load(StreamBuf& B, Cursor c, int N, uint3
   }
 }
 
-template <bool SYM>
+template <bool SYM, bool XF16>
 __device__ __forceinline__ void stream_compute(const StreamBuf& B, Cursor c, int T, int N, int lane,
                                                const uint4* xs, const float* sxs,
                                                uint16_t* __restrict__ y, uint32_t magic,
@@ -327,13 +356,13 @@ __device__ __forceinline__ void stream_compute(const StreamBuf& B, Cursor c, int
   const uint4* xp = xs + c.p * 256 + lane;
   const uint4 x0 = xp[0], x1 = xp[64], x2 = xp[128], x3 = xp[192];
   const float sx = sxs[c.p * 64 + lane];
-  const float init = -128.f * sx;
+  const float init = (XF16 ? -1024.f : -128.f) * sx;  // the magic offset of every weight
 #pragma unroll
   for (int r = 0; r < kSRpw; ++r) {
-    float a = dot8_perm(B.w[r].x, x0, init, magic);
-    a = dot8_perm(B.w[r].y, x1, a, magic);
-    a = dot8_perm(B.w[r].z, x2, a, magic);
-    a = dot8_perm(B.w[r].w, x3, a, magic);
+    float a = dot8_perm<XF16>(B.w[r].x, x0, init, magic);
+    a = dot8_perm<XF16>(B.w[r].y, x1, a, magic);
+    a = dot8_perm<XF16>(B.w[r].z, x2, a, magic);
+    a = dot8_perm<XF16>(B.w[r].w, x3, a, magic);
     const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)B.s[r]);
     const float z = SYM ? 8.f : (float)__builtin_bit_cast(_Float16, (uint16_t)B.z[r]);
     acc[r] = fmaf(sc, fmaf(-z, sx, a), acc[r]);
@@ -343,13 +372,13 @@ __device__ __forceinline__ void stream_compute(const StreamBuf& B, Cursor c, int
     for (int r = 0; r < kSRpw; ++r) {
       const float v = wave_sum_to_lane63(acc[r]);
       const int row = c.b * kSRpw + r;
-      if (lane == 63 && row < N) y[row] = f32_to_bf16_rne(v);
+      if (lane == 63 && row < N) y[row] = XF16 ? f32_to_f16_rne(v) : f32_to_bf16_rne(v);
     }
   }
 }
 
 // Requires N * K/2 < 2^32 and N * (K/G) * 2 < 2^32 (the launcher splits N).
-template <bool SYM, bool TAB>
+template <bool SYM, bool TAB, bool XF16>
 __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(
     const uint16_t* __restrict__ x, int K, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
@@ -369,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(
   const uint32_t sgs = TAB ? 0u : (uint32_t)(kStepK / G) * 2;
   const uint32_t vw = (uint32_t)lane * 16;
   const uint32_t vs = TAB ? 0u : (uint32_t)((lane * 32) / G) * 2;
-  const uint32_t magic = 0x43004300u;
+  const uint32_t magic = XF16 ? 0x64006400u : 0x43004300u;
   const rsrc_t rw = make_rsrc(qw, (uint32_t)N * rb);
   const rsrc_t rs = make_rsrc(scales, (uint32_t)N * ngb);
   const rsrc_t rz = make_rsrc(SYM ? (const void*)scales : (const void*)zeros, (uint32_t)N * ngb);
@@ -419,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(
         // p*256 + j*64 + l (j = 0..3), so the 16-byte LDS reads of a wave are
         // consecutive and free of bank conflicts
         xs[(c & ~255) | ((c & 3) << 6) | ((c >> 2) & 63)] = perm_x_pairs(v);
-        float sm = sum_bf16x8(v);
+        float sm = XF16 ? sum_f16x8(v) : sum_bf16x8(v);
         sm += __shfl_xor(sm, 1, 64);
         sm += __shfl_xor(sm, 2, 64);
         if ((c & 3) == 0) sxs[c >> 2] = sm;
@@ -435,25 +464,25 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(
       stream_load<SYM, TAB>(buf[(j + kSNbuf - 1) % kSNbuf], lc, N, rb, ngb, sgs, vw, vs, wtab, stab,
                             lane, rw, rs, rz);
       advance(lc, T, W);
-      stream_compute<SYM>(buf[j], cc, T, N, lane, xs, sxs, y, magic, acc);
+      stream_compute<SYM, XF16>(buf[j], cc, T, N, lane, xs, sxs, y, magic, acc);
       advance(cc, T, W);
     }
   }
 }
 
-template <bool SYM, bool TAB>
+template <bool SYM, bool TAB, bool XF16>
 hipError_t launch_stream(const uint16_t* x, int K, const uint8_t* qw, const uint16_t* sc,
                          const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
   const int T = (K + kStepK - 1) / kStepK;
   const size_t lds = (size_t)T * (256 * 16 + 64 * 4) + (TAB ? (size_t)T * 64 * 8 : 0);
   const int nb = (N + kSRpw - 1) / kSRpw;
   const int grid = std::max(1, std::min((nb + kWaves - 1) / kWaves, 2 * num_cus()));
-  hipLaunchKernelGGL((gemv_stream_kernel<SYM, TAB>), dim3(grid), dim3(kThreads), lds, s, x, K, qw,
-                     sc, zr, N, G, y);
+  hipLaunchKernelGGL((gemv_stream_kernel<SYM, TAB, XF16>), dim3(grid), dim3(kThreads), lds, s, x, K,
+                     qw, sc, zr, N, G, y);
   return hipGetLastError();
 }
 
-template <bool SYM>
+template <bool SYM, bool XF16 = false>
 hipError_t stream_m1(const uint16_t* x, int K, const uint8_t* qw, const uint16_t* sc,
                      const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
   // Rows per launch so that every byte offset fits 32 bits.
@@ -465,13 +494,24 @@ hipError_t stream_m1(const uint16_t* x, int K, const uint8_t* qw, const uint16_t
     const uint8_t* q = qw + n0 * rb;
     const uint16_t* a = sc + n0 * (K / G);
     const uint16_t* b = SYM ? zr : zr + n0 * (K / G);
-    hipError_t e = tab ? launch_stream<SYM, true>(x, K, q, a, b, n, G, y + n0, s)
-                       : launch_stream<SYM, false>(x, K, q, a, b, n, G, y + n0, s);
+    hipError_t e = tab ? launch_stream<SYM, true, XF16>(x, K, q, a, b, n, G, y + n0, s)
+                       : launch_stream<SYM, false, XF16>(x, K, q, a, b, n, G, y + n0, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 }  // namespace
+
+bool gemv_f16_supported(int M, int64_t K) {
+  return M == 1 && (K + kStepK - 1) / kStepK <= kSMaxT;
+}
+
+hipError_t launch_w4a16_gemv_f16(const uint16_t* x, int64_t K, const uint8_t* qweight,
+                                 const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
+                                 int symmetric, uint16_t* y, hipStream_t s) {
+  if (symmetric) return stream_m1<true, true>(x, (int)K, qweight, scales, zeros, (int)N, G, y, s);
+  return stream_m1<false, true>(x, (int)K, qweight, scales, zeros, (int)N, G, y, s);
+}
 
 hipError_t launch_w4a16_gemv(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
                              const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,

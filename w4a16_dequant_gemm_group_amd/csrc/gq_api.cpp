@@ -184,6 +184,20 @@ gq_status gq_dequantize(const uint8_t* qweight, const uint16_t* scales, const ui
                                         w_hat, out_dtype, s));
 }
 
+gq_status gq_ingest_group_major(const int8_t* codes, const uint16_t* scales, int64_t n_groups,
+                                int64_t group, int64_t N, uint8_t* qweight, uint16_t* scales_out,
+                                void* stream) {
+  if (n_groups < 1 || group < 1 || N < 0 || n_groups > kMaxDim || group > kMaxDim) return GQ_ERR_INVALID_ARG;
+  if (gq_status st = check_groups(N, n_groups * group, (int32_t)group)) return st;
+  if (N == 0) return GQ_OK;
+  if (!codes || !scales || !qweight || !scales_out) return GQ_ERR_INVALID_ARG;
+  if (!aligned16(qweight)) return GQ_ERR_MISALIGNED;
+  hipStream_t s = (hipStream_t)stream;
+  if (gq_status st = check_device(s)) return st;
+  return from_hip(gq::launch_ingest_group_major(codes, scales, n_groups, group, N, qweight,
+                                                scales_out, s));
+}
+
 gq_status gq_w4a16_gemv(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
                         const uint16_t* scales, const uint16_t* zeros, int64_t N, gq_qparams p,
                         uint16_t* y, void* stream) {
@@ -237,6 +251,33 @@ gq_status gq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* 
   if (gq_status st = check_device(s)) return st;
   return from_hip(gq::launch_w4a16_gemm(x, M, K, qweight, scales, zeros, N, p.group_size,
                                         p.symmetric, y, s));
+}
+
+gq_status gq_w4a16_gemv_f16(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                            const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                            gq_qparams p, uint16_t* y, void* stream) {
+  if (M > 16) return GQ_ERR_INVALID_ARG;
+  if (gq_status s = check_w4_matmul(x, M, K, qweight, scales, zeros, N, p, y)) return s;
+  if (M == 0 || N == 0) return GQ_OK;
+  if (!gq::gemv_f16_supported((int)M, K)) return GQ_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  if (gq_status st = check_device(s)) return st;
+  return from_hip(gq::launch_w4a16_gemv_f16(x, K, qweight, scales, zeros, N, p.group_size,
+                                            p.symmetric, y, s));
+}
+
+gq_status gq_w4a16_gemm_f16(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                            const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                            gq_qparams p, uint16_t* y, void* stream) {
+  if (gq_status s = check_w4_matmul(x, M, K, qweight, scales, zeros, N, p, y)) return s;
+  if (K > kMaxGemmK || M > kMaxDim / 2) return GQ_ERR_UNSUPPORTED;
+  if (((M + 255) / 256) * ((N + 255) / 256) > INT32_MAX / 2) return GQ_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return GQ_OK;
+  if (!gq::gemm_f16_supported(K, p.group_size)) return GQ_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  if (gq_status st = check_device(s)) return st;
+  return from_hip(gq::launch_w4a16_gemm_f16(x, M, K, qweight, scales, zeros, N, p.group_size,
+                                            p.symmetric, y, s));
 }
 
 gq_status gq_q4k_quantize(const void* w, gq_dtype w_dtype, int64_t N, int64_t K, uint8_t* blocks,

@@ -108,6 +108,9 @@ hipError_t launch_pack_int4(const void* codes, int64_t N, int64_t K, int symmetr
 hipError_t launch_dequantize(const uint8_t* qweight, const uint16_t* scales,
                              const uint16_t* zeros, int64_t N, int64_t K, int G, int symmetric,
                              void* out, gq_dtype odt, hipStream_t s);
+hipError_t launch_ingest_group_major(const int8_t* codes, const uint16_t* scales, int64_t ng,
+                                     int64_t group, int64_t N, uint8_t* qweight,
+                                     uint16_t* scales_out, hipStream_t s);
 // workspace: caller scratch of ws_bytes (>= gemv_workspace_bytes), or NULL to
 // use the library's per-stream scratch for the matrix-core path.
 hipError_t launch_w4a16_gemv(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
@@ -128,6 +131,16 @@ hipError_t launch_w4a16_gemv_mfma(const uint16_t* x, int M, int64_t K, const uin
 hipError_t launch_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
                              const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
                              int symmetric, uint16_t* y, hipStream_t s);
+// fp16 activations and output: the M = 1 streaming GEMV and the 256 x 256 GEMM
+// kernel (K % 64 == 0, G = 64, 128 or a multiple of 256).
+bool gemv_f16_supported(int M, int64_t K);
+hipError_t launch_w4a16_gemv_f16(const uint16_t* x, int64_t K, const uint8_t* qweight,
+                                 const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
+                                 int symmetric, uint16_t* y, hipStream_t s);
+bool gemm_f16_supported(int64_t K, int G);
+hipError_t launch_w4a16_gemm_f16(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                                 const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
+                                 int symmetric, uint16_t* y, hipStream_t s);
 hipError_t launch_q4k_quantize(const void* w, gq_dtype dt, int64_t N, int64_t K, uint8_t* blocks,
                                hipStream_t s);
 hipError_t launch_q4k_gemv(const uint16_t* x, int M, int64_t K, const uint8_t* blocks, int64_t N,

@@ -103,6 +103,60 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
   }
 }
 
+// Ingest of the group-major layout of the "量化" chapter's fused_matmul (codes
+// [n_groups, group, N], i.e. K-major with N contiguous): a 128 (k) x 64 (n) tile
+// is read row by row (64 consecutive bytes per wave load), transposed through
+// LDS, and written as 64 packed rows of 64 bytes (16-byte stores; K % 32 == 0,
+// so every 32-k chunk of a row is wholly inside or outside K).
+constexpr int kIngK = 128, kIngN = 64;
+
+__global__ __launch_bounds__(kThreads) void ingest_codes_kernel(const int8_t* __restrict__ codes,
+                                                              int64_t K, int64_t N,
+                                                              uint8_t* __restrict__ qweight) {
+  __shared__ int8_t tile[kIngK][kIngN + 4];
+  const int64_t ntn = (N + kIngN - 1) / kIngN;
+  const int64_t k0 = (int64_t)blockIdx.x / ntn * kIngK;
+  const int64_t n0 = (int64_t)blockIdx.x % ntn * kIngN;
+  const int t = threadIdx.x;
+  {
+    const int nc = t & (kIngN - 1);
+    const int64_t n = n0 + nc;
+    for (int kr = t / kIngN; kr < kIngK; kr += kThreads / kIngN) {
+      const int64_t k = k0 + kr;
+      tile[kr][nc] = (k < K && n < N) ? codes[k * N + n] : (int8_t)0;
+    }
+  }
+  __syncthreads();
+  const int nr = t >> 2;             // output row within the tile
+  const int jb = (t & 3) * 16;       // first packed byte (32 k values)
+  const int64_t n = n0 + nr;
+  if (n >= N || k0 + 2 * jb >= K) return;
+  uint32_t w[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int kk = 2 * (jb + 4 * d + b);
+      const uint32_t lo = ((uint32_t)(int)tile[kk][nr] + 8u) & 15u;
+      const uint32_t hi = ((uint32_t)(int)tile[kk + 1][nr] + 8u) & 15u;
+      v |= (lo | (hi << 4)) << (8 * b);
+    }
+    w[d] = v;
+  }
+  *(uint4*)(qweight + n * (K / 2) + k0 / 2 + jb) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// scales [n_groups, N] -> [N, n_groups]: one thread per element.
+__global__ __launch_bounds__(kThreads) void transpose_scales_kernel(const uint16_t* __restrict__ in,
+                                                                  int64_t ng, int64_t N,
+                                                                  uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= ng * N) return;
+  const int64_t n = i / ng, g = i - n * ng;
+  out[i] = in[g * N + n];
+}
+
 inline unsigned blocks_for(int64_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
 
 }  // namespace
@@ -130,6 +184,21 @@ hipError_t launch_dequantize(const uint8_t* qweight, const uint16_t* scales,
   const int64_t total = N * (K / 2);
   hipLaunchKernelGGL(dequantize_kernel, dim3(blocks_for(total)), dim3(kThreads), 0, s, qweight,
                      scales, zeros, N, K, G, symmetric, out, odt);
+  return hipGetLastError();
+}
+
+hipError_t launch_ingest_group_major(const int8_t* codes, const uint16_t* scales, int64_t ng,
+                                     int64_t group, int64_t N, uint8_t* qweight,
+                                     uint16_t* scales_out, hipStream_t s) {
+  const int64_t K = ng * group;
+  const int64_t tiles = ((N + kIngN - 1) / kIngN) * ((K + kIngK - 1) / kIngK);
+  if (tiles > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ingest_codes_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, codes, K, N,
+                     qweight);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(transpose_scales_kernel, dim3(blocks_for(ng * N)), dim3(kThreads), 0, s, scales,
+                     ng, N, scales_out);
   return hipGetLastError();
 }
 

@@ -73,6 +73,19 @@ def activations(m: int, k: int, seed: int, n_outlier_channels: int = 0,
     return f32_to_bf16_bits(x), cols
 
 
+def activations_f16(m: int, k: int, seed: int, n_outlier_channels: int = 0,
+                    outlier_gain: float = 50.0):
+    """As ``activations`` but rounded to fp16 (nearest even); returns
+    ``(x_fp16_bits, outlier_cols)``."""
+    rng = np.random.default_rng(seed)
+    x = rng.normal(0.0, 1.0, size=(m, k)).astype(np.float32)
+    cols = np.zeros(0, np.int64)
+    if n_outlier_channels:
+        cols = np.sort(rng.choice(k, n_outlier_channels, replace=False))
+        x[:, cols] *= np.float32(outlier_gain)
+    return x.astype(np.float16).view(np.uint16), cols
+
+
 def tiny_reference():
     """Tiny case: W [256, 512] ~ N(0, 0.02), input channels 7 and 300 scaled x50,
     X [1, 512] ~ N(0, 1); one generator (seed 0), W drawn first, then X."""
