@@ -46,7 +46,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "W4A16 dequant-GEMV HBM GB/s & % peak (M=1); MFMA TFLOP/s at M=2048"
-GEMV_SOURCE = os.path.join(ROOT, "w4a16_dequant_gemm_group_amd", "csrc", "gemv.hip")
+# the streaming kernel's sources: traffic counters taken before a change to
+# either no longer describe the kernel
+GEMV_SOURCES = [os.path.join(ROOT, "w4a16_dequant_gemm_group_amd", "csrc", f)
+                for f in ("gemv.hip", "stream_util.h")]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "w4a16_gemv_stream_traffic.json")
 GEMV_KERNEL = "gemv_stream_kernel"
 CALIB_BYTES = 256 << 20          # calibration copy: reads and writes this many bytes
@@ -63,8 +66,11 @@ def gemv_bytes(n, k, g, m=1, sym=False):
 
 
 def source_digest() -> str:
-    with open(GEMV_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for p in GEMV_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 # ----------------------------------------------------------------------------

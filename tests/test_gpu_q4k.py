@@ -40,8 +40,11 @@ def test_quantize_other_dtypes(dtype):
 
 
 @pytest.mark.parametrize("M", [1, 2, 4, 16])
-@pytest.mark.parametrize("N,K", [(77, 2304), (64, 256), (33, 18432)])
+@pytest.mark.parametrize("N,K", [(77, 2304), (64, 256), (33, 18432), (1031, 4096), (37, 28672)])
 def test_gemv_small(M, N, K):
+    """M = 1 with K up to 26624 takes the streaming kernel (ragged last step at
+    2304 and 256, a second x staging pass at 18432, several row pairs per wave
+    at 1031 rows); 28672 and M > 1 take the per-workgroup kernel."""
     w, x = synth.small(N, K, M, seed=N + M)
     blocks = O.q4k_encode(O.q4k_quantize(O.bf16_to_f64(w)))
     y = B.gq_q4k_gemv(bf16_dev(x), u8_dev(blocks))

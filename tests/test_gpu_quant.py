@@ -90,6 +90,12 @@ def test_pack_and_dequant_bit_exact():
         assert np.array_equal(bits16(outb), O.f32_exact_to_bf16_bits(wh_ref))
         outh = B.gq_dequantize(u8_dev(qw_ref), sd, zd, G, sym, torch.float16)
         assert np.array_equal(bits16(outh), O.f64_to_f16_bits(wh_ref))
+        # an output 2 bytes off a 16-byte boundary takes the per-byte kernel
+        n, k = wh_ref.shape
+        buf = torch.empty(n * k + 8, dtype=torch.bfloat16, device=device())
+        outm = buf[1:1 + n * k].view(n, k)
+        B.gq_dequantize(u8_dev(qw_ref), sd, zd, G, sym, torch.bfloat16, out=outm)
+        assert np.array_equal(bits16(outm), O.f32_exact_to_bf16_bits(wh_ref))
 
 
 def test_full_size_o_projection():

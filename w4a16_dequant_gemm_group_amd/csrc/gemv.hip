@@ -33,27 +33,16 @@
 #include <algorithm>
 
 #include "gq_internal.h"
+#include "stream_util.h"
 
 namespace gq {
 namespace {
 
+using namespace stream_util;
+
 constexpr int kThreads = 256;  // 4 wavefronts
 constexpr int kWaves = kThreads / 64;
 constexpr int kStepK = 2048;   // k covered by one wave load (64 lanes x 32)
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
-// fp16 pairs: v_dot2_f32_f16 (fp32 accumulation)
-__device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c,
-                                false);
-}
 
 // 8 nibbles of one dword (k offsets 0..7 at bits 4p) against the permuted
 // activation dwords (x0,x4) (x1,x5) (x2,x6) (x3,x7).
@@ -215,92 +204,9 @@ hipError_t dispatch(const uint16_t* x, int M, int K, const uint8_t* qw, const ui
 // M = 1 streaming kernel
 // ---------------------------------------------------------------------------
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kSRpw = 2;    // rows per work item
 constexpr int kSNbuf = 3;   // register buffers (items in flight + 1)
 constexpr int kSMaxT = 13;  // 2048-steps of x that fit the LDS budget
-constexpr uint32_t kOob = 0x80000000u;  // an offset past every buffer's range
-
-// Raw buffer descriptor over [base, base + bytes); every field wave-uniform.
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)base;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, (int)n,
-                                           0x00020000);
-}
-
-// 8 nibbles (k = 0..7 at bits 4p) against activation pairs (x0,x2) (x4,x6)
-// (x1,x3) (x5,x7): the even and odd nibbles are split into bytes, and each
-// byte pair gets an exponent byte from `magic` by v_perm: 0x43 makes the bf16
-// value 128 + q (magic 0x43004300), 0x64 the fp16 value 1024 + q (0x64006400);
-// both are exact.  XF16: fp16 activations.
-template <bool XF16 = false>
-__device__ __forceinline__ float dot8_perm(uint32_t d, const uint4& xp, float a, uint32_t magic) {
-  const uint32_t ev = d & 0x0F0F0F0Fu;
-  const uint32_t od = (d >> 4) & 0x0F0F0F0Fu;
-  if (XF16) {
-    a = dot2h(__builtin_amdgcn_perm(ev, magic, 0x01050104u), xp.x, a);
-    a = dot2h(__builtin_amdgcn_perm(ev, magic, 0x01070106u), xp.y, a);
-    a = dot2h(__builtin_amdgcn_perm(od, magic, 0x01050104u), xp.z, a);
-    return dot2h(__builtin_amdgcn_perm(od, magic, 0x01070106u), xp.w, a);
-  }
-  a = dot2(__builtin_amdgcn_perm(ev, magic, 0x01050104u), xp.x, a);
-  a = dot2(__builtin_amdgcn_perm(ev, magic, 0x01070106u), xp.y, a);
-  a = dot2(__builtin_amdgcn_perm(od, magic, 0x01050104u), xp.z, a);
-  a = dot2(__builtin_amdgcn_perm(od, magic, 0x01070106u), xp.w, a);
-  return a;
-}
-
-// x0..x7 (bf16, natural order in v) -> pairs (x0,x2) (x4,x6) (x1,x3) (x5,x7).
-__device__ __forceinline__ uint4 perm_x_pairs(uint4 v) {
-  uint4 p;
-  p.x = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);
-  p.y = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);
-  p.z = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);
-  p.w = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);
-  return p;
-}
-
-__device__ __forceinline__ float sum_f16x8(uint4 v) {
-  auto h = [](uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); };
-  float s = h(v.x & 0xFFFFu) + h(v.x >> 16);
-  s += h(v.y & 0xFFFFu) + h(v.y >> 16);
-  s += h(v.z & 0xFFFFu) + h(v.z >> 16);
-  s += h(v.w & 0xFFFFu) + h(v.w >> 16);
-  return s;
-}
-
-__device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
-  return __builtin_bit_cast(uint16_t, (_Float16)f);
-}
-
-__device__ __forceinline__ float sum_bf16x8(uint4 v) {
-  float s = bf16_to_f32(v.x & 0xFFFFu) + bf16_to_f32(v.x >> 16);
-  s += bf16_to_f32(v.y & 0xFFFFu) + bf16_to_f32(v.y >> 16);
-  s += bf16_to_f32(v.z & 0xFFFFu) + bf16_to_f32(v.z >> 16);
-  s += bf16_to_f32(v.w & 0xFFFFu) + bf16_to_f32(v.w >> 16);
-  return s;
-}
-
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                               ROW_MASK, 0xF, ROW_MASK == 0xF));
-}
-
-// Sum over the 64 lanes; the total lands in lane 63.
-__device__ __forceinline__ float wave_sum_to_lane63(float v) {
-  v += dpp_f32<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
-  v += dpp_f32<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
-  v += dpp_f32<0x124, 0xF>(v);  // row_ror:4
-  v += dpp_f32<0x128, 0xF>(v);  // row_ror:8  (every lane holds its row's sum)
-  v += dpp_f32<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
-  v += dpp_f32<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
-  return v;
-}
-
 // Scale and zero stay 16-bit in registers: widening them where the loop
 // carries them would force a wait on every outstanding load.
 struct StreamBuf {
@@ -431,6 +337,8 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(
 #pragma unroll
   for (int j = 0; j < kSNbuf - 1; ++j) {
     stream_load<SYM, TAB>(buf[j], lc, N, rb, ngb, sgs, vw, vs, wtab, stab, lane, rw, rs, rz);
+    // keep the loads in item order: the loop's waits assume it
+    __builtin_amdgcn_sched_barrier(0);
     advance(lc, T, W);
   }
 
@@ -438,12 +346,14 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(
 #pragma unroll
     for (int i = 0; i < kXr; ++i) {
       const int c = c0 + threadIdx.x + kThreads * i;
-      uint4 v = xv[i];
-      if (c0 > 0) {
-        v = make_uint4(0, 0, 0, 0);
-        if (c < T * 256 && c * 8 < K) v = *(const uint4*)(x + c * 8);
-      }
+      // every load issued here is consumed here: a load left in flight on
+      // some path would make the main loop wait for all loads at its head
       if (c0 + kThreads * i < T * 256) {  // uniform over the block
+        uint4 v = xv[i];
+        if (c0 > 0) {
+          v = make_uint4(0, 0, 0, 0);
+          if (c * 8 < K) v = *(const uint4*)(x + c * 8);
+        }
         // chunk c = 8 x values; lane l of step p reads its four chunks at
         // p*256 + j*64 + l (j = 0..3), so the 16-byte LDS reads of a wave are
         // consecutive and free of bank conflicts
@@ -457,17 +367,30 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(
   }
   __syncthreads();
 
-  while (cc.b < nb) {
+  // Whole buffer rounds in the loop, the last 0-2 items (already loaded) after
+  // it: with its only exit at the bottom, the loop head waits for exactly the
+  // item it multiplies (an exit in the middle would merge just-issued loads
+  // into the head's wait), and no item is computed twice or padded.
+  const int b0 = (int)blockIdx.x * kWaves + wave;
+  const int items = b0 < nb ? ((nb - 1 - b0) / W + 1) * T : 0;
+  const int rounds = items / kSNbuf, rest = items % kSNbuf;
+  for (int it = 0; it < rounds; ++it) {
 #pragma unroll
     for (int j = 0; j < kSNbuf; ++j) {
-      if (cc.b >= nb) break;
       stream_load<SYM, TAB>(buf[(j + kSNbuf - 1) % kSNbuf], lc, N, rb, ngb, sgs, vw, vs, wtab, stab,
                             lane, rw, rs, rz);
+      __builtin_amdgcn_sched_barrier(0);  // issue the loads before this item's wait
       advance(lc, T, W);
       stream_compute<SYM, XF16>(buf[j], cc, T, N, lane, xs, sxs, y, magic, acc);
       advance(cc, T, W);
     }
   }
+  static_assert(kSNbuf == 3, "the tail below finishes at most two prefetched items");
+  if (rest > 0) {
+    stream_compute<SYM, XF16>(buf[0], cc, T, N, lane, xs, sxs, y, magic, acc);
+    advance(cc, T, W);
+  }
+  if (rest > 1) stream_compute<SYM, XF16>(buf[1], cc, T, N, lane, xs, sxs, y, magic, acc);
 }
 
 template <bool SYM, bool TAB, bool XF16>

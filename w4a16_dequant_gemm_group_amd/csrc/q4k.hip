@@ -8,11 +8,16 @@
 //   [10] mn_0..7 likewise  [16] 128 nibble bytes, sub-block j at 16+16j.
 // x^ = d*sc_j*q - dmin*mn_j.
 //
-// The GEMV uses the layout of the plain INT4 GEMV: lane l of a wave owns the
+// The GEMVs use the layout of the plain INT4 GEMV: lane l of a wave owns the
 // 32 weights at k = 2048 t + 32 l, which here is sub-block l%8 of block
 // 8t + l/8; it loads the block's 16-byte header (the eight lanes of one block
-// share one address) and its 16 nibble bytes, both as dwordx4.
+// share one address) and its 16 nibble bytes, both as dwordx4.  M = 1 with x
+// in LDS (K <= 26624) runs the persistent streaming kernel of the INT4 GEMV;
+// other M and longer K run a per-workgroup kernel that stages x in k chunks.
+#include <algorithm>
+
 #include "gq_internal.h"
+#include "stream_util.h"
 
 namespace gq {
 namespace {
@@ -206,6 +211,160 @@ __global__ __launch_bounds__(kThreads) void q4k_gemv_kernel(const uint16_t* __re
     }
 }
 
+// ---------------------------------------------------------------------------
+// M = 1: the streaming structure of the packed INT4 GEMV.  Persistent
+// workgroups stage x once (permuted pairs + chunk sums) and each wave walks
+// (row pair, 2048-wide k step) items with three register buffers, two items'
+// loads in flight.  Lane l loads, per row, the 16-byte header of block 8t + l/8
+// and the 16 nibble bytes of its sub-block l % 8 with raw buffer loads (the
+// header address is shared by 8 lanes); lanes past K and rows past N read zero
+// from the range check.
+// ---------------------------------------------------------------------------
+constexpr int kQRpw = 2;    // rows per item
+constexpr int kQNbuf = 3;   // register buffers
+constexpr int kQMaxT = 13;  // 2048-steps of x in LDS
+
+struct QBuf {
+  uint4 h[kQRpw], w[kQRpw];
+};
+
+__global__ __launch_bounds__(kThreads) void q4k_stream_kernel(const uint16_t* __restrict__ x, int K,
+                                                              const uint8_t* __restrict__ blocks,
+                                                              int N, uint16_t* __restrict__ y) {
+  namespace su = stream_util;
+  extern __shared__ uint4 lds[];
+  const int T = (K + kStepK - 1) / kStepK;
+  uint4* xs = lds;                      // [T][4][64] permuted x pairs
+  float* sxs = (float*)(xs + T * 256);  // [T * 64] chunk sums
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nb = (N + kQRpw - 1) / kQRpw;
+  const int W = gridDim.x * kWaves;
+  const uint32_t row_bytes = (uint32_t)(K / 256) * kBlockBytes;
+  const su::rsrc_t rb = su::make_rsrc(blocks, (uint32_t)N * row_bytes);
+  const uint32_t hoff = (uint32_t)(lane >> 3) * kBlockBytes;
+  const uint32_t woff = hoff + 16u + 16u * (uint32_t)(lane & 7);
+  const uint32_t o6 = 6u * (uint32_t)(lane & 7);  // bit offset of this lane's sub-block fields
+  const bool shi = o6 >= 32, mhi = o6 >= 16;
+
+  auto load = [&](QBuf& B, int b, int t) {
+    const bool kin = t * kStepK + lane * 32 < K;
+    const uint32_t step = (uint32_t)t * 8u * kBlockBytes;
+    const uint32_t vh = kin ? hoff + step : su::kOob, vw = kin ? woff + step : su::kOob;
+#pragma unroll
+    for (int r = 0; r < kQRpw; ++r) {
+      const uint32_t row = (uint32_t)min(b * kQRpw + r, N);  // row N reads out of range
+      const auto h = __builtin_amdgcn_raw_buffer_load_b128(rb, vh, row * row_bytes, 0);
+      const auto w = __builtin_amdgcn_raw_buffer_load_b128(rb, vw, row * row_bytes, 2);
+      B.h[r] = make_uint4(h[0], h[1], h[2], h[3]);
+      B.w[r] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  };
+
+  // x: first loads before the weight prefetch, staged after it
+  constexpr int kXr = 8;
+  uint4 xv[kXr];
+#pragma unroll
+  for (int i = 0; i < kXr; ++i) {
+    const int c = threadIdx.x + kThreads * i;
+    xv[i] = make_uint4(0, 0, 0, 0);
+    if (i < T && c * 8 < K) xv[i] = *(const uint4*)(x + c * 8);
+  }
+  QBuf buf[kQNbuf];
+  float acc[kQRpw] = {0.f, 0.f};
+  int lb = (int)blockIdx.x * kWaves + wave, lt = 0;  // next item to load
+  int cb = lb, ct = 0;                               // next item to compute
+  auto advance = [&](int& b, int& t) {
+    if (++t == T) {
+      t = 0;
+      b += W;
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < kQNbuf - 1; ++j) {
+    load(buf[j], lb, lt);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads in item order: the loop's waits assume it
+    advance(lb, lt);
+  }
+  for (int c0 = 0; c0 < T * 256; c0 += kXr * kThreads) {
+#pragma unroll
+    for (int i = 0; i < kXr; ++i) {
+      const int c = c0 + threadIdx.x + kThreads * i;
+      // every load issued here is consumed here: a load left in flight on
+      // some path would make the main loop wait for all loads at its head
+      if (c0 + kThreads * i < T * 256) {  // uniform over the block
+        uint4 v = xv[i];
+        if (c0 > 0) {
+          v = make_uint4(0, 0, 0, 0);
+          if (c * 8 < K) v = *(const uint4*)(x + c * 8);
+        }
+        xs[(c & ~255) | ((c & 3) << 6) | ((c >> 2) & 63)] = su::perm_x_pairs(v);
+        float sm = su::sum_bf16x8(v);
+        sm += __shfl_xor(sm, 1, 64);
+        sm += __shfl_xor(sm, 2, 64);
+        if ((c & 3) == 0) sxs[c >> 2] = sm;
+      }
+    }
+  }
+  __syncthreads();
+
+  auto compute = [&](const QBuf& B, int b, int t) {
+    if (t == 0) acc[0] = acc[1] = 0.f;
+    const uint4* xp = xs + t * 256 + lane;
+    const uint4 x0 = xp[0], x1 = xp[64], x2 = xp[128], x3 = xp[192];
+    const float sx = sxs[t * 64 + lane];
+    const float init = -128.f * sx;  // bf16 128 + q: remove the offset of the 32 weights
+#pragma unroll
+    for (int r = 0; r < kQRpw; ++r) {
+      float a = su::dot8_perm(B.w[r].x, x0, init, 0x43004300u);
+      a = su::dot8_perm(B.w[r].y, x1, a, 0x43004300u);
+      a = su::dot8_perm(B.w[r].z, x2, a, 0x43004300u);
+      a = su::dot8_perm(B.w[r].w, x3, a, 0x43004300u);
+      const uint4 h = B.h[r];
+      const float d = f16_to_f32((uint16_t)(h.x & 0xFFFFu));
+      const float dmin = f16_to_f32((uint16_t)(h.x >> 16));
+      // 6-bit fields by 32-bit funnel shifts: the scale sits at bit 6 sub of
+      // {h.w : h.z : h.y}, the min at bit 6 sub + 48; each lane picks the two
+      // dwords holding its field
+      const uint32_t sc6 = __builtin_amdgcn_alignbit(shi ? h.w : h.z, shi ? h.z : h.y, o6 & 31u) & 63u;
+      const uint32_t mn6 = __builtin_amdgcn_alignbit(h.w, mhi ? h.w : h.z, (o6 + 16u) & 31u) & 63u;
+      const float S = d * (float)sc6;
+      const float Mn = dmin * (float)mn6;
+      acc[r] = fmaf(S, a, fmaf(-Mn, sx, acc[r]));
+    }
+    if (t == T - 1) {
+#pragma unroll
+      for (int r = 0; r < kQRpw; ++r) {
+        const float v = su::wave_sum_to_lane63(acc[r]);
+        const int row = b * kQRpw + r;
+        if (lane == 63 && row < N) y[row] = f32_to_bf16_rne(v);
+      }
+    }
+  };
+  // Whole buffer rounds in the loop, the last 0-2 items (already loaded) after
+  // it: with its only exit at the bottom, the loop head waits for exactly the
+  // item it multiplies, and no item is computed twice or padded.
+  const int b0 = (int)blockIdx.x * kWaves + wave;
+  const int items = b0 < nb ? ((nb - 1 - b0) / W + 1) * T : 0;
+  const int rounds = items / kQNbuf, rest = items % kQNbuf;
+  for (int it = 0; it < rounds; ++it) {
+#pragma unroll
+    for (int j = 0; j < kQNbuf; ++j) {
+      load(buf[(j + kQNbuf - 1) % kQNbuf], lb, lt);
+      __builtin_amdgcn_sched_barrier(0);  // issue the loads before this item's wait
+      advance(lb, lt);
+      compute(buf[j], cb, ct);
+      advance(cb, ct);
+    }
+  }
+  static_assert(kQNbuf == 3, "the tail below finishes at most two prefetched items");
+  if (rest > 0) {
+    compute(buf[0], cb, ct);
+    advance(cb, ct);
+  }
+  if (rest > 1) compute(buf[1], cb, ct);
+}
+
 template <int MT, int RPW, int T>
 hipError_t launch_t(const uint16_t* x, int M, int K, const uint8_t* b, int N, uint16_t* y,
                     hipStream_t s) {
@@ -230,6 +389,22 @@ hipError_t launch_q4k_gemv(const uint16_t* x, int M, int64_t K, const uint8_t* b
                            uint16_t* y, hipStream_t s) {
   const int steps = (int)((K + kStepK - 1) / kStepK);
   const int k = (int)K, n = (int)N;
+  if (M == 1 && steps <= kQMaxT) {
+    // rows per launch so that every byte offset fits 32 bits
+    const uint64_t row_bytes = (uint64_t)(K / 256) * kBlockBytes;
+    const int64_t cap = (int64_t)(((uint64_t)1 << 31) / row_bytes);
+    const size_t lds = (size_t)steps * (256 * 16 + 64 * 4);
+    for (int64_t n0 = 0; n0 < N; n0 += cap) {
+      const int nn = (int)std::min<int64_t>(cap, N - n0);
+      const int nb = (nn + kQRpw - 1) / kQRpw;
+      const int grid = std::max(1, std::min((nb + kWaves - 1) / kWaves, 2 * num_cus()));
+      hipLaunchKernelGGL(q4k_stream_kernel, dim3(grid), dim3(kThreads), lds, s, x, k,
+                         blocks + n0 * row_bytes, nn, y + n0);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   if (M == 1) {
     switch (steps) {
       case 1: return launch_t<1, 2, 1>(x, M, k, blocks, n, y, s);

@@ -157,6 +157,44 @@ __global__ __launch_bounds__(kThreads) void transpose_scales_kernel(const uint16
   out[i] = in[g * N + n];
 }
 
+// One thread expands 8 consecutive weights of a row (4 packed bytes, one group:
+// G is a multiple of 32) and writes them with 16-byte stores.  Needs qweight
+// 4-byte and the output 16-byte aligned; the per-byte kernel serves the rest.
+__global__ __launch_bounds__(kThreads) void dequantize8_kernel(
+    const uint8_t* __restrict__ qweight, const uint16_t* __restrict__ scales,
+    const uint16_t* __restrict__ zeros, int64_t N, int64_t K, int G, int symmetric,
+    void* __restrict__ out, gq_dtype odt) {
+  const int64_t per_row = K / 8;
+  const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (j >= N * per_row) return;
+  const int64_t row = j / per_row;
+  const int64_t k = 8 * (j - row * per_row);
+  const int64_t gi = row * (K / G) + k / G;
+  const float S = f16_to_f32(scales[gi]);
+  const float z = symmetric ? 8.0f : f16_to_f32(zeros[gi]);
+  const uint32_t d = *(const uint32_t*)(qweight + row * (K / 2) + k / 2);
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = S * ((float)((d >> (4 * i)) & 15u) - z);  // exact in fp32
+  const int64_t o = row * K + k;
+  if (odt == GQ_F32) {
+    float4* p = (float4*)((float*)out + o);
+    p[0] = make_float4(v[0], v[1], v[2], v[3]);
+    p[1] = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = odt == GQ_BF16 ? f32_to_bf16_rne(v[2 * i])
+                                          : __builtin_bit_cast(uint16_t, (_Float16)v[2 * i]);
+      const uint32_t hi = odt == GQ_BF16 ? f32_to_bf16_rne(v[2 * i + 1])
+                                          : __builtin_bit_cast(uint16_t, (_Float16)v[2 * i + 1]);
+      h[i] = lo | (hi << 16);
+    }
+    *(uint4*)((uint16_t*)out + o) = make_uint4(h[0], h[1], h[2], h[3]);
+  }
+}
+
 inline unsigned blocks_for(int64_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
 
 }  // namespace
@@ -181,6 +219,12 @@ hipError_t launch_pack_int4(const void* codes, int64_t N, int64_t K, int symmetr
 hipError_t launch_dequantize(const uint8_t* qweight, const uint16_t* scales,
                              const uint16_t* zeros, int64_t N, int64_t K, int G, int symmetric,
                              void* out, gq_dtype odt, hipStream_t s) {
+  if (((uintptr_t)qweight & 3u) == 0 && ((uintptr_t)out & 15u) == 0 && K % 8 == 0 && G % 8 == 0) {
+    const int64_t total8 = N * (K / 8);
+    hipLaunchKernelGGL(dequantize8_kernel, dim3(blocks_for(total8)), dim3(kThreads), 0, s, qweight,
+                       scales, zeros, N, K, G, symmetric, out, odt);
+    return hipGetLastError();
+  }
   const int64_t total = N * (K / 2);
   hipLaunchKernelGGL(dequantize_kernel, dim3(blocks_for(total)), dim3(kThreads), 0, s, qweight,
                      scales, zeros, N, K, G, symmetric, out, odt);
