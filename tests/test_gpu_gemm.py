@@ -104,6 +104,60 @@ def test_zero_scale_groups(G):
     assert_parity(bits16(yv), ref[:3], O.bf16_to_f64(x[:3]), wh, f"gemv zero-scale groups G={G}")
 
 
+def test_last_round_split():
+    """300 output tiles on 256 compute units: 256 whole tiles, then the last
+    44 tiles with K split in two (88 workgroups).  Columns sampled from both
+    launches against the oracle; two calls agree bit for bit."""
+    M, N, K, G = 256, 300 * 256, 1024, 128
+    announce(f"gemm last-round split M={M} N={N} K={K} G={G}")
+    w, _ = synth.weights(N, K, seed=17)
+    x, _ = synth.activations(M, K, seed=19, n_outlier_channels=4)
+    codes, scales, zeros = B.gq_quantize_groups(bf16_dev(w), 4, G, False)
+    qw = B.gq_pack_int4(codes)
+    xd = bf16_dev(x)
+    y = B.gq_w4a16_gemm(xd, qw, scales, zeros, G, False)
+    y2 = B.gq_w4a16_gemm(xd, qw, scales, zeros, G, False)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    rng = np.random.default_rng(23)
+    cut = 256 * 256  # first column of the split launch (one 256-row M tile)
+    rows = np.sort(np.concatenate([rng.choice(cut, 64, replace=False),
+                                   cut + rng.choice(N - cut, 64, replace=False)]))
+    qw_ref, s_ref, z_ref = _oracle_weights(w[rows], G, False)
+    assert np.array_equal(qw.cpu().numpy()[rows], qw_ref)
+    ref = O.w4a16_reference(x, qw_ref, s_ref, z_ref, G, False)
+    wh = O.dequantize_packed(qw_ref, s_ref, z_ref, G, False)
+    assert_parity(bits16(y)[:, rows], ref, O.bf16_to_f64(x), wh, f"last-round split [{N},{K}] M={M}")
+
+
+def test_split_scratch_reuse():
+    """Split GEMMs of falling then rising tile counts on one stream reuse the
+    library scratch without reallocating it: the per-tile counters of the
+    later, larger split must not overlap partial sums an earlier, smaller split
+    left behind.  Checked against the oracle and for bit-equal repeats."""
+    M, K, G = 512, 2048, 128
+    announce("gemm split scratch reuse: 128, 4, then 64 split tiles")
+    def run(n, seed):
+        w, _ = synth.weights(n, K, seed=seed)
+        x, _ = synth.activations(M, K, seed=seed + 1, n_outlier_channels=4)
+        codes, scales, zeros = B.gq_quantize_groups(bf16_dev(w), 4, G, False)
+        qw = B.gq_pack_int4(codes)
+        args = (bf16_dev(x), qw, scales, zeros, G, False)
+        return w, x, qw, args, B.gq_w4a16_gemm(*args)
+    run(64 * 256, 31)   # 128 tiles: the largest scratch
+    run(2 * 256, 37)    # 4 tiles: partial sums at the start of the buffer
+    w, x, qw, args, y = run(32 * 256, 41)  # 64 tiles: counters span more words
+    y2 = B.gq_w4a16_gemm(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    rows = np.sort(np.random.default_rng(43).choice(w.shape[0], 96, replace=False))
+    qw_ref, s_ref, z_ref = _oracle_weights(w[rows], G, False)
+    assert np.array_equal(qw.cpu().numpy()[rows], qw_ref)
+    ref = O.w4a16_reference(x, qw_ref, s_ref, z_ref, G, False)
+    wh = O.dequantize_packed(qw_ref, s_ref, z_ref, G, False)
+    assert_parity(bits16(y)[:, rows], ref, O.bf16_to_f64(x), wh, "split after smaller split, sampled")
+
+
 @pytest.mark.parametrize("M,N,K,G,sym", [
     (512, 512, 2048, 128, False),    # 4 tiles: K split in two halves of 16 tiles
     (300, 700, 1216, 64, True),      # ragged, odd number of 64-k tiles, symmetric

@@ -394,6 +394,7 @@ struct WStage {
 // 1: G = 64 (every tile); 2: G = 128 (even tiles); 3: G a multiple of 256
 // (even tiles whose k0 is a multiple of G).
 //
+// The launch covers output tiles [tile0, tile0 + nt) in the M-fastest order.
 // SPLIT: the grid holds two workgroups per output tile, the first covering
 // 64-k tiles [0, tsplit), the second [tsplit, K/64) (tsplit keeps whole
 // groups).  Each converts its running sum to the true scale; the first to finish
@@ -406,7 +407,8 @@ template <bool SYM, int MODE, bool SPLIT, bool XF16 = false>
 __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
-    uint16_t* __restrict__ y, uint32_t* __restrict__ sync, float* __restrict__ part, int tsplit) {
+    uint16_t* __restrict__ y, uint32_t* __restrict__ sync, float* __restrict__ part, int tsplit,
+    int tile0, int nt) {
   __shared__ uint4 sA0[kLM * 8], sA1[kLM * 8];                        // 2 x 32 KiB
   __shared__ uint4 sB0[kLN * kLBRow / 8], sB1[kLN * kLBRow / 8];      // 2 x 36 KiB
   __shared__ float sC0[2 * kLN], sC1[2 * kLN];                        // scales per column half
@@ -415,9 +417,9 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
   const int ntm = (M + kLM - 1) / kLM;
-  const int ntiles = ntm * ((N + kLN - 1) / kLN);
-  const int split = SPLIT && (int)blockIdx.x >= ntiles;
-  const int tile_id = (int)blockIdx.x - split * ntiles;
+  const int split = SPLIT && (int)blockIdx.x >= nt;
+  const int lt = (int)blockIdx.x - split * nt;  // tile within the launch: its sync and partial slot
+  const int tile_id = tile0 + lt;
   const int m0 = (tile_id % ntm) * kLM;
   const int n0 = (tile_id / ntm) * kLN;
   const int ng = K / G;
@@ -614,9 +616,9 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
     // release/acquire fences would cost every other workgroup on the XCD.  The
     // writer drains its stores before raising the flag; the reader loads the
     // partials only after it has seen the flag.
-    float* slot = part + ((size_t)tile_id * 8 + wave) * 128 * 64 + lane;
+    float* slot = part + ((size_t)lt * 8 + wave) * 128 * 64 + lane;
     __shared__ uint32_t s_first;
-    if (tid == 0) s_first = atomicAdd(&sync[2 * tile_id], 1u) == 0;
+    if (tid == 0) s_first = atomicAdd(&sync[2 * lt], 1u) == 0;
     __syncthreads();
     if (s_first) {
 #pragma unroll
@@ -629,7 +631,7 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       wait_vm<0>();
       __syncthreads();
-      if (tid == 0) __hip_atomic_store(&sync[2 * tile_id + 1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) __hip_atomic_store(&sync[2 * lt + 1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
     // The other workgroup has already counted itself, so it is running and
@@ -637,7 +639,7 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
     // corrupted flag word.
     if (tid == 0) {
       for (int n = 0; n < (1 << 24); ++n) {
-        if (__hip_atomic_load(&sync[2 * tile_id + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+        if (__hip_atomic_load(&sync[2 * lt + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
         __builtin_amdgcn_s_sleep(2);
       }
     }
@@ -659,8 +661,8 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
     }
     cref[0] = cref[1] = 1.f;  // acc now holds the true sum
     if (tid == 0) {
-      sync[2 * tile_id] = 0;
-      sync[2 * tile_id + 1] = 0;
+      sync[2 * lt] = 0;
+      sync[2 * lt + 1] = 0;
     }
   }
 
@@ -681,10 +683,13 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
     }
 }
 
-// Split K in two when the tiles fill at most half of the compute units and
-// each half keeps at least two groups' worth of 64-k tiles; the partial sums and
-// per-tile (counter, flag) words live in library scratch (not available while
-// the stream is captured: the tiles then run unsplit).
+// Split K in two for the tiles of a round that fills at most half of the
+// compute units: all tiles when there are at most half as many as compute
+// units, else the last partial round (launched after the full rounds, so its
+// 2r half-tile workgroups run side by side).  Each half keeps at least two
+// groups' worth of 64-k tiles; the partial sums and the per-tile (counter,
+// flag) words live in two library scratch slots (not available while the
+// stream is captured: the tiles then run unsplit).
 template <bool SYM, int MODE, bool XF16 = false>
 hipError_t launch_lds(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
                       const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
@@ -692,19 +697,29 @@ hipError_t launch_lds(const uint16_t* x, int M, int K, const uint8_t* qw, const 
   const int T = K / kBK;
   const int tpg = G >= kBK ? G / kBK : 1;  // 64-k tiles per group
   const int tsplit = (T / 2) / std::max(tpg, 2) * std::max(tpg, 2);
-  if (2 * tiles <= num_cus() && tsplit >= 2 * tpg && T - tsplit >= 2 * tpg) {
-    const size_t sync_bytes = (size_t)((tiles * 8 + 255) / 256 * 256);
-    const size_t bytes = sync_bytes + (size_t)tiles * kLM * kLN * 4;
-    char* ws = (char*)stream_scratch(kScratchGemm, bytes, sync_bytes, s);
-    if (ws) {
-      hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE, true, XF16>), dim3((unsigned)(2 * tiles)),
-                         dim3(kLT), 0, s, x, M, K, qw, sc, zr, N, G, y, (uint32_t*)ws,
-                         (float*)(ws + sync_bytes), tsplit);
+  const int64_t cus = num_cus();
+  const int64_t tail = tiles <= cus ? tiles : tiles % cus;  // tiles of the last round
+  if (tail > 0 && 2 * tail <= cus && tsplit >= 2 * tpg && T - tsplit >= 2 * tpg) {
+    const size_t sync_bytes = (size_t)tail * 8;
+    uint32_t* sync = (uint32_t*)stream_scratch(kScratchGemmSync, sync_bytes, sync_bytes, s);
+    float* part = (float*)stream_scratch(kScratchGemm, (size_t)tail * kLM * kLN * 4, 0, s);
+    if (sync && part) {
+      const int64_t full = tiles - tail;  // a multiple of the CU count: whole rounds
+      if (full > 0) {
+        hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE, false, XF16>), dim3((unsigned)full),
+                           dim3(kLT), 0, s, x, M, K, qw, sc, zr, N, G, y, nullptr, nullptr, 0, 0,
+                           (int)full);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE, true, XF16>), dim3((unsigned)(2 * tail)),
+                         dim3(kLT), 0, s, x, M, K, qw, sc, zr, N, G, y, sync, part, tsplit,
+                         (int)full, (int)tail);
       return hipGetLastError();
     }
   }
   hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE, false, XF16>), dim3((unsigned)tiles), dim3(kLT), 0,
-                     s, x, M, K, qw, sc, zr, N, G, y, nullptr, nullptr, 0);
+                     s, x, M, K, qw, sc, zr, N, G, y, nullptr, nullptr, 0, 0, (int)tiles);
   return hipGetLastError();
 }
 

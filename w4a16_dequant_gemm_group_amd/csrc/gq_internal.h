@@ -93,7 +93,12 @@ __device__ __forceinline__ double load_elem_f64(const void* p, int64_t i, gq_dty
 int num_cus();
 
 // Library scratch per (device, stream, slot); nullptr while s is being captured.
-enum { kScratchGemv = 0, kScratchGemm = 1 };
+// The first zero_bytes of a newly allocated buffer are cleared on s; a reused
+// buffer keeps what the last user left.  Words that must be zero at every
+// launch (the split GEMM's per-tile counters and flags) get a slot of their
+// own that nothing else writes, cleared whole when allocated and reset by the
+// launch that used them.
+enum { kScratchGemv = 0, kScratchGemm = 1, kScratchGemmSync = 2 };
 void* stream_scratch(int slot, size_t bytes, size_t zero_bytes, hipStream_t s);
 
 // ---------------------------------------------------------------------------
