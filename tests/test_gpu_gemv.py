@@ -145,6 +145,35 @@ def test_misaligned_pointer_rejected():
     assert e.value.status == B.GQ_ERR_MISALIGNED
 
 
+def test_slice_reduction_counters_reused():
+    """With library scratch and a grid of at most two rounds, the last
+    workgroup of each 64-row group adds the K slices (per-group counters reset
+    after use); larger grids and a caller's workspace use a second kernel.
+    Calls of falling and rising N and M on one stream must match the workspace
+    path bit for bit, and the oracle on sampled rows."""
+    K, G = 4096, 128
+    for M, N, seed in ((8, 3000, 90), (4, 64, 91), (16, 1000, 92), (8, 20000, 94), (8, 3000, 93)):
+        announce(f"small-batch slice reduction M={M} N={N} K={K}")
+        w, x = synth.small(N, K, M, seed=seed)
+        codes, sd, zd = B.gq_quantize_groups(bf16_dev(w), 4, G, False)
+        qd = B.gq_pack_int4(codes)
+        xd = bf16_dev(x)
+        y_lib = B.gq_w4a16_gemv(xd, qd, sd, zd, G, False)
+        y_lib2 = B.gq_w4a16_gemv(xd, qd, sd, zd, G, False)
+        ws = torch.empty(B.gq_w4a16_gemv_workspace_size(M, K, N, G, False), dtype=torch.uint8,
+                         device=xd.device)
+        y_ws = B.gq_w4a16_gemv(xd, qd, sd, zd, G, False, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y_lib, y_ws) and torch.equal(y_lib, y_lib2)
+        rows = np.sort(np.random.default_rng(seed).choice(N, min(N, 256), replace=False))
+        qw, s, z = _oracle_weights(w[rows], G, False)
+        assert np.array_equal(qd.cpu().numpy()[rows], qw)
+        ref = O.w4a16_reference(x, qw, s, z, G, False)
+        wh = O.dequantize_packed(qw, s, z, G, False)
+        assert_parity(bits16(y_lib)[:, rows], ref, O.bf16_to_f64(x), wh,
+                      f"[{N},{K}] M={M} slice reduction, sampled")
+
+
 def test_workspace_entry_point_and_graph_replays():
     # gq_w4a16_gemv_ws (caller scratch) and gq_w4a16_gemv (library scratch) run
     # the same kernels: identical bits.  Captured into a graph, the call gets its

@@ -203,19 +203,31 @@ def gq_w4a16_gemv_workspace_size(M: int, K: int, N: int, group_size: int = 128,
     return int(b.value)
 
 
+def _capturing(stream) -> bool:
+    if stream is None:
+        return torch.cuda.is_current_stream_capturing()
+    if not hasattr(stream, "cuda_stream"):
+        return True  # a raw handle: take the path that is safe under capture
+    with torch.cuda.stream(stream):
+        return torch.cuda.is_current_stream_capturing()
+
+
 def gq_w4a16_gemv(x, qweight, scales, zeros, group_size: int = 128, symmetric: bool = False,
                   y=None, stream=None, workspace=None):
     """Fused W4A16 GEMV, x bf16 [M<=16, K] -> y bf16 [M, N].
 
-    When the call needs scratch (gq_w4a16_gemv_workspace_size > 0) it is taken
-    from torch's allocator on the call's stream (or `workspace`, a uint8 GPU
-    tensor) and passed to gq_w4a16_gemv_ws, so the call is also safe under
-    stream capture."""
+    Eager calls use gq_w4a16_gemv (library scratch).  When the call needs
+    scratch (gq_w4a16_gemv_workspace_size > 0) and the stream is being
+    captured, or `workspace` (a uint8 GPU tensor) is given, the scratch comes
+    from torch's allocator on the call's stream (or is `workspace`) and the call
+    goes to gq_w4a16_gemv_ws: a captured graph then holds no pointer into
+    library scratch that a later call could reallocate.  Both give the same
+    bits."""
     _need(x, "x", (torch.bfloat16,))
     M, K = x.shape
     N = qweight.shape[0]
     need = gq_w4a16_gemv_workspace_size(M, K, N, group_size, symmetric) if M <= 16 else 0
-    if need == 0 and workspace is None:
+    if workspace is None and (need == 0 or not _capturing(stream)):
         return _matmul(lib().gq_w4a16_gemv, "gq_w4a16_gemv", x, qweight, scales, zeros,
                        group_size, symmetric, y, stream)
     if workspace is None:

@@ -95,10 +95,11 @@ int num_cus();
 // Library scratch per (device, stream, slot); nullptr while s is being captured.
 // The first zero_bytes of a newly allocated buffer are cleared on s; a reused
 // buffer keeps what the last user left.  Words that must be zero at every
-// launch (the split GEMM's per-tile counters and flags) get a slot of their
+// launch (the split GEMM's per-tile counters and flags, the small-batch
+// GEMV's per-row-group counters) get a slot of their
 // own that nothing else writes, cleared whole when allocated and reset by the
 // launch that used them.
-enum { kScratchGemv = 0, kScratchGemm = 1, kScratchGemmSync = 2 };
+enum { kScratchGemv = 0, kScratchGemm = 1, kScratchGemmSync = 2, kScratchGemvSync = 3 };
 void* stream_scratch(int slot, size_t bytes, size_t zero_bytes, hipStream_t s);
 
 // ---------------------------------------------------------------------------
