@@ -574,10 +574,12 @@ def run_extras(torch, B, synth, to_dev, dev, stream, shapes, W, X, gate, fused_s
     log(f"group sweep down M=1: { {k_: v['us']['median'] for k_, v in sweep.items()} }")
     del wd, xd, yd
 
-    # ---- small batch M in {1,4,8,16}, symmetric g32, rotating weight copies ---------
-    sym_w = {}
+    # ---- small batch M in {1,2,3,4,8,16}, symmetric g32, rotating weight copies -----
+    sym_w, gate_w = {}, {}
     for name, n, k in shapes:
         w, _ = synth.decode_case(name)
+        if name in ("o", "down"):  # K = 4096 and K = 14336: both kernels of each M
+            gate_w[name] = w
         codes, s, _ = B.gq_quantize_groups(to_dev(w), 4, 32, True)
         sym_w[name] = (B.gq_pack_int4(codes, True), s)
         del codes
@@ -586,10 +588,13 @@ def run_extras(torch, B, synth, to_dev, dev, stream, shapes, W, X, gate, fused_s
     sym_copies = [sym_w] + [{nm: tuple(t.clone() for t in sym_w[nm]) for nm, _, _ in shapes}
                             for _ in range(Rs - 1)]
     sb = {}
-    for m in (1, 4, 8, 16):
+    for m in (1, 2, 3, 4, 8, 16):
         xs = {nm: to_dev(synth.activations(m, k, seed=2000 + synth.SHAPE_ORDER.index(nm))[0])
               for nm, _, k in shapes}
         ys = {nm: torch.empty((m, n), dtype=torch.bfloat16, device=dev) for nm, n, _ in shapes}
+        for nm, w in gate_w.items():
+            xb = xs[nm].view(torch.int16).cpu().numpy().view(np.uint16)
+            gate(f"{nm} M={m} sym g32", w, xb, *sym_w[nm], None, 32, True)
 
         def sb_step(i):
             c = sym_copies[i % Rs]
@@ -600,7 +605,7 @@ def run_extras(torch, B, synth, to_dev, dev, stream, shapes, W, X, gate, fused_s
         tot_b = sum(gemv_bytes(n, k, 32, m, True) for _, n, k in shapes)
         sb[f"M={m}"] = {"us_per_step": round(us, 2), "GB/s": round(tot_b / (us * 1e-6) / 1e9, 1),
                         "TFLOP/s": round(2.0 * m * sum(n * k for _, n, k in shapes) / (us * 1e-6) / 1e12, 2)}
-    del sym_copies, sym_w
+    del sym_copies, sym_w, gate_w
     ex["small_batch_sym_g32"] = sb
     log(f"small batch {sb}")
 

@@ -22,10 +22,13 @@
  * Conventions for every entry point
  *   - Pointers are device pointers (HIP global memory) unless marked "host".
  *     The caller owns every buffer.  libgq keeps a per-device architecture
- *     check and allocates nothing, with one exception: gq_w4a16_gemv for
- *     4 <= M <= 16 keeps a split-K scratch buffer per (device, stream), grown on
- *     demand and held until the process ends (gq_w4a16_gemv_ws takes it from
- *     the caller instead).
+ *     check and allocates nothing, with two exceptions, both per (device,
+ *     stream), grown on demand, held until the process ends and never handed
+ *     out while the stream is being captured (the call then runs unsplit
+ *     kernels): gq_w4a16_gemv on its matrix-core path (below) keeps split-K
+ *     partial sums (gq_w4a16_gemv_ws takes them from the caller instead), and
+ *     gq_w4a16_gemm keeps split-K partial sums and per-tile counters when its
+ *     output tiles fill at most half of the GPU.
  *   - All matrices are dense, row-major, contiguous.  W is [N, K] = out x in,
  *     so Y = X W^T [P1 sec.2]; groups run along K (the reduction axis).
  *   - fp16 / bf16 values are passed as uint16_t bit patterns.
@@ -154,9 +157,11 @@ gq_status gq_w4a16_gemv(const uint16_t* x, int64_t M, int64_t K, const uint8_t* 
                         uint16_t* y, void* stream);
 
 /* Scratch (bytes) that gq_w4a16_gemv_ws needs for these arguments, 0 when the
- * call runs without any.  With 4 <= M <= 16 (group_size 32, 64 or a multiple of
- * 128, K % 256 == 0) the GEMV runs on the matrix cores
- * split along K into 1024-wide slices and keeps fp32 partial sums per slice:
+ * call runs without any.  1 <= M <= 4 runs a streaming kernel that needs none
+ * while x fits its LDS stage (K <= 26624, 34816, 22528, 16384 for M = 1, 2,
+ * 3, 4).  Otherwise, with 4 <= M <= 16, group_size 32, 64 or a multiple of
+ * 128 and K % 256 == 0, the GEMV runs on the matrix cores split along K into
+ * 1024-wide slices and keeps fp32 partial sums per slice:
  * ceil(K / 1024) * M * N * 4 bytes.  Errors: those of gq_w4a16_gemv's argument
  * checks; INVALID_ARG for a NULL `bytes`. */
 gq_status gq_w4a16_gemv_workspace_size(int64_t M, int64_t K, int64_t N, gq_qparams p,

@@ -117,11 +117,14 @@ def test_other_entry_point_validation(lib):
 
 
 def test_gemv_workspace_size_and_validation(lib):
-    # the matrix-core path (4 <= M <= 16, G in {32, 64, 128k}, K % 256 == 0)
+    # the matrix-core path (4 <= M <= 16, G in {32, 64, 128k}, K % 256 == 0,
+    # and for M <= 4 only where x is too long for the streaming kernel's LDS)
     # keeps ceil(K / 1024) * M * N fp32 partial sums; other calls need none
     assert B.gq_w4a16_gemv_workspace_size(16, 14336, 4096, 32, True) == 14 * 16 * 4096 * 4
     assert B.gq_w4a16_gemv_workspace_size(8, 6400, 203, 128) == 7 * 8 * 203 * 4
-    assert B.gq_w4a16_gemv_workspace_size(4, 4096, 4096, 128) == 4 * 4 * 4096 * 4
+    assert B.gq_w4a16_gemv_workspace_size(4, 18432, 4096, 128) == 18 * 4 * 4096 * 4
+    assert B.gq_w4a16_gemv_workspace_size(4, 16384, 4096, 128) == 0
+    assert B.gq_w4a16_gemv_workspace_size(4, 4096, 4096, 128) == 0
     assert B.gq_w4a16_gemv_workspace_size(3, 4096, 4096, 128) == 0
     assert B.gq_w4a16_gemv_workspace_size(1, 4096, 4096, 128) == 0
     assert B.gq_w4a16_gemv_workspace_size(8, 6528, 203, 128) == 0   # K % 256 != 0

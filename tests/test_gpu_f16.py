@@ -40,6 +40,9 @@ def _check(y, x_bits, qw, s, z, G, sym, what):
     (4096, 14336, 32, True),
     (130, 6400, 64, False),     # K not a multiple of 2048: per-lane offset tables
     (1, 2048, 2048, True),
+    (77, 6144, 64, False),      # two lanes per group
+    (203, 4096, 64, True),
+    (9001, 2048, 256, False),   # several items per wave
 ])
 def test_gemv_f16(N, K, G, sym):
     qw, s, z = _weights(N, K, G, sym, seed=N + K)

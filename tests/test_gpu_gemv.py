@@ -73,6 +73,33 @@ def test_k_extents(K):
     _run(x, qw, s, z, G, False, f"[67,{K}] M=1 G={G}")
 
 
+@pytest.mark.parametrize("sym,G", [(False, 32), (True, 32), (False, 64), (True, 64), (False, 128),
+                                   (True, 128), (False, 256), (True, 512), (False, 1024),
+                                   (False, 2048)])
+@pytest.mark.parametrize("N,K", [(203, 6144), (9001, 2048)])
+def test_m1_stream_group_sizes(N, K, sym, G):
+    # M = 1 with K a multiple of 2048 (fixed per-lane offsets) for every group
+    # size that divides 2048: one to 64 lanes per group.  N is odd (the last
+    # row pair has one real row); N = 9001 gives every wave several items.
+    w, x = synth.small(N, K, 1, seed=N + G + sym)
+    qw, s, z = _oracle_weights(w, G, sym)
+    rows = None if N < 1000 else np.r_[0:64, N - 64:N]
+    _run(x, qw, s, z, G, sym, f"[{N},{K}] M=1 sym={sym} G={G} (stream)", rows=rows)
+
+
+@pytest.mark.parametrize("M", [2, 3, 4])
+@pytest.mark.parametrize("N,K,sym,G", [
+    (16387, 4096, False, 128),   # enough items for four weight rows per item (M >= 3)
+    (203, 10240, True, 32),      # x needs one workgroup of 8 waves per compute unit (M >= 3)
+    (203, 10368, False, 128),    # the same with per-lane offset tables (K % 2048 != 0)
+])
+def test_stream_multi_row_layouts(M, N, K, sym, G):
+    w, x = synth.small(N, K, M, seed=N + K + M)
+    qw, s, z = _oracle_weights(w, G, sym)
+    rows = None if N < 1000 else np.r_[0:64, N // 2:N // 2 + 64, N - 67:N]
+    _run(x, qw, s, z, G, sym, f"[{N},{K}] M={M} sym={sym} G={G} (stream, M > 1)", rows=rows)
+
+
 def test_group_equals_k_and_outlier_blowup():
     """Per-row (group = K) quantization of the outlier case loses far more
     accuracy than group 128 (S08 page, outlier remarks); both GPU results are
@@ -105,9 +132,12 @@ def test_decode_shapes_full_size(name):
     assert_parity(bits16(y)[:, rows], ref, O.bf16_to_f64(x), wh, f"{name} {w.shape} M=1 full, sampled")
 
 
-@pytest.mark.parametrize("M", [4, 8, 16])
-def test_small_batch_full_size_sym_g32(M):
-    w, _ = synth.decode_case("down")
+@pytest.mark.parametrize("name,M", [("down", 2), ("down", 4), ("down", 8), ("down", 16),
+                                    ("gate_up", 2), ("gate_up", 3), ("gate_up", 4), ("qkv", 4)])
+def test_small_batch_full_size_sym_g32(name, M):
+    # M <= 4 at K = 4096 (and M = 2 on down) take the streaming kernel, the
+    # rest the matrix-core kernel
+    w, _ = synth.decode_case(name)
     x, _ = synth.activations(M, w.shape[1], seed=2003)
     rows = np.sort(np.random.default_rng(4).choice(w.shape[0], 256, replace=False))
     codes, scales, _ = B.gq_quantize_groups(bf16_dev(w), 4, 32, True)
@@ -117,7 +147,7 @@ def test_small_batch_full_size_sym_g32(M):
     qw_ref, s_ref, _ = _oracle_weights(w[rows], 32, True)
     ref = O.w4a16_reference(x, qw_ref, s_ref, None, 32, True)
     wh = O.dequantize_packed(qw_ref, s_ref, None, 32, True)
-    assert_parity(bits16(y)[:, rows], ref, O.bf16_to_f64(x), wh, f"down M={M} sym g32 full, sampled")
+    assert_parity(bits16(y)[:, rows], ref, O.bf16_to_f64(x), wh, f"{name} M={M} sym g32 full, sampled")
 
 
 def test_special_inputs():
@@ -152,7 +182,7 @@ def test_slice_reduction_counters_reused():
     Calls of falling and rising N and M on one stream must match the workspace
     path bit for bit, and the oracle on sampled rows."""
     K, G = 4096, 128
-    for M, N, seed in ((8, 3000, 90), (4, 64, 91), (16, 1000, 92), (8, 20000, 94), (8, 3000, 93)):
+    for M, N, seed in ((8, 3000, 90), (5, 64, 91), (16, 1000, 92), (8, 20000, 94), (8, 3000, 93)):
         announce(f"small-batch slice reduction M={M} N={N} K={K}")
         w, x = synth.small(N, K, M, seed=seed)
         codes, sd, zd = B.gq_quantize_groups(bf16_dev(w), 4, G, False)

@@ -18,11 +18,13 @@
 // S.  The row's 64 lane partials are summed across the wave and rounded once
 // to bf16 (nearest-even).
 //
-// gemv_stream_kernel (M = 1): persistent workgroups; x is staged once per
+// gemv_stream_kernel (M = 1..4): persistent workgroups; x is staged once per
 // workgroup into LDS (pre-permuted into the pairs the nibble extraction yields,
 // plus every chunk sum).  Each wave walks a sequence of work items (a pair of
 // rows x one 2048-wide k step) with three register buffers, so two items' loads
-// are in flight while one is multiplied.  Loads are raw buffer loads with the
+// are in flight while one is multiplied.  With M > 1 activation rows each
+// weight is unpacked once and multiplied against every row, so the vector work
+// per weight grows by the dot products only and the weights stream once.  Loads are raw buffer loads with the
 // nontemporal hint against whole-matrix descriptors; anything past the matrix
 // (rows beyond N, lanes beyond a ragged K) reads as zero from the hardware's
 // range check, so the loads are unconditional and the compiler's wait counts
@@ -201,21 +203,31 @@ hipError_t dispatch(const uint16_t* x, int M, int K, const uint8_t* qw, const ui
 
 
 // ---------------------------------------------------------------------------
-// M = 1 streaming kernel
+// Streaming kernel, M = 1..4
 // ---------------------------------------------------------------------------
 
-constexpr int kSRpw = 2;    // rows per work item
 constexpr int kSNbuf = 3;   // register buffers (items in flight + 1)
-constexpr int kSMaxT = 13;  // 2048-steps of x that fit the LDS budget
+constexpr int kSMaxT = 13;  // M = 1: 2048-steps of x that fit the LDS budget
+constexpr int kSMaxM = 4;   // activation rows the streaming kernel takes
+constexpr size_t kSLdsMulti = 80 * 1024;  // M > 1: LDS of two workgroups per compute unit
+constexpr size_t kSLdsOne = 156 * 1024;   // M > 1: LDS of one workgroup per compute unit
+
+// LDS bytes of the streaming kernel: per activation row and 2048-step 4 KiB of
+// permuted pairs and 64 chunk sums; per step 512 B of offset tables (TAB).
+size_t stream_lds_bytes(int M, int64_t K, bool tab) {
+  const int64_t T = (K + kStepK - 1) / kStepK;
+  return (size_t)(M * T * (256 * 16 + 64 * 4) + (tab ? T * 64 * 8 : 0));
+}
 // Scale and zero stay 16-bit in registers: widening them where the loop
 // carries them would force a wait on every outstanding load.
+template <int RPW>
 struct StreamBuf {
-  uint4 w[kSRpw];
-  uint16_t s[kSRpw], z[kSRpw];
+  uint4 w[RPW];
+  uint16_t s[RPW], z[RPW];
 };
 
 struct Cursor {
-  int b, p;  // row pair, k step
+  int b, p;  // row block (RPW rows), k step
 };
 
 __device__ __forceinline__ void advance(Cursor& c, int T, int W) {
@@ -228,8 +240,8 @@ __device__ __forceinline__ void advance(Cursor& c, int T, int W) {
 // TAB: per-(step, lane) byte offsets come from LDS tables (ragged K or a group
 // size that does not divide 2048); otherwise they are lane constants plus a
 // uniform per-step term.
-template <bool SYM, bool TAB>
-__device__ __forceinline__ void stream_load(StreamBuf& B, Cursor c, int N, uint32_t rb, uint32_t ngb,
+template <int RPW, bool SYM, bool TAB>
+__device__ __forceinline__ void stream_load(StreamBuf<RPW>& B, Cursor c, int N, uint32_t rb, uint32_t ngb,
                                             uint32_t sgs, uint32_t vw, uint32_t vs,
                                             const uint32_t* wtab, const uint32_t* stab, int lane,
                                             rsrc_t rw, rsrc_t rs, rsrc_t rz) {
@@ -241,8 +253,8 @@ __device__ __forceinline__ void stream_load(StreamBuf& B, Cursor c, int N, uint3
     us = 0;
   }
 #pragma unroll
-  for (int r = 0; r < kSRpw; ++r) {
-    const uint32_t row = (uint32_t)min(c.b * kSRpw + r, N);  // row N reads out of range
+  for (int r = 0; r < RPW; ++r) {
+    const uint32_t row = (uint32_t)min(c.b * RPW + r, N);  // row N reads out of range
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, ow, row * rb + uw, 2);
     B.w[r] = make_uint4(v[0], v[1], v[2], v[3]);
     B.s[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, os, row * ngb + us, 2);
@@ -250,55 +262,95 @@ __device__ __forceinline__ void stream_load(StreamBuf& B, Cursor c, int N, uint3
   }
 }
 
-template <bool SYM, bool XF16>
-__device__ __forceinline__ void stream_compute(const StreamBuf& B, Cursor c, int T, int N, int lane,
-                                               const uint4* xs, const float* sxs,
+template <int MT, int RPW, bool SYM, bool XF16>
+__device__ __forceinline__ void stream_compute(const StreamBuf<RPW>& B, Cursor c, int T, int N, int ldy,
+                                               int lane, const uint4* xs, const float* sxs,
                                                uint16_t* __restrict__ y, uint32_t magic,
-                                               float (&acc)[kSRpw]) {
+                                               float (&acc)[MT][RPW]) {
   if (c.p == 0) {
 #pragma unroll
-    for (int r = 0; r < kSRpw; ++r) acc[r] = 0.f;
-  }
-  const uint4* xp = xs + c.p * 256 + lane;
-  const uint4 x0 = xp[0], x1 = xp[64], x2 = xp[128], x3 = xp[192];
-  const float sx = sxs[c.p * 64 + lane];
-  const float init = (XF16 ? -1024.f : -128.f) * sx;  // the magic offset of every weight
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-  for (int r = 0; r < kSRpw; ++r) {
-    float a = dot8_perm<XF16>(B.w[r].x, x0, init, magic);
-    a = dot8_perm<XF16>(B.w[r].y, x1, a, magic);
-    a = dot8_perm<XF16>(B.w[r].z, x2, a, magic);
-    a = dot8_perm<XF16>(B.w[r].w, x3, a, magic);
-    const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)B.s[r]);
-    const float z = SYM ? 8.f : (float)__builtin_bit_cast(_Float16, (uint16_t)B.z[r]);
-    acc[r] = fmaf(sc, fmaf(-z, sx, a), acc[r]);
+      for (int r = 0; r < RPW; ++r) acc[m][r] = 0.f;
+  }
+  constexpr float kOff = XF16 ? -1024.f : -128.f;  // the magic offset of every weight
+  if constexpr (MT == 1) {
+    const uint4* xp = xs + c.p * 256 + lane;
+    const uint4 x0 = xp[0], x1 = xp[64], x2 = xp[128], x3 = xp[192];
+    const float sx = sxs[c.p * 64 + lane];
+    const float init = kOff * sx;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      float a = dot8_perm<XF16>(B.w[r].x, x0, init, magic);
+      a = dot8_perm<XF16>(B.w[r].y, x1, a, magic);
+      a = dot8_perm<XF16>(B.w[r].z, x2, a, magic);
+      a = dot8_perm<XF16>(B.w[r].w, x3, a, magic);
+      const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)B.s[r]);
+      const float z = SYM ? 8.f : (float)__builtin_bit_cast(_Float16, (uint16_t)B.z[r]);
+      acc[0][r] = fmaf(sc, fmaf(-z, sx, a), acc[0][r]);
+    }
+  } else {
+    // activation row m: permuted pairs at xs[m T 256 ..], chunk sums at sxs[m T 64 ..]
+    uint4 xq[MT][4];
+    float sx[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const uint4* xp = xs + (m * T + c.p) * 256 + lane;
+      xq[m][0] = xp[0];
+      xq[m][1] = xp[64];
+      xq[m][2] = xp[128];
+      xq[m][3] = xp[192];
+      sx[m] = sxs[(m * T + c.p) * 64 + lane];
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const uint4 u0 = unpack8_words(B.w[r].x, magic), u1 = unpack8_words(B.w[r].y, magic);
+      const uint4 u2 = unpack8_words(B.w[r].z, magic), u3 = unpack8_words(B.w[r].w, magic);
+      const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)B.s[r]);
+      const float z = SYM ? 8.f : (float)__builtin_bit_cast(_Float16, (uint16_t)B.z[r]);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        float a = dot8_words<XF16>(u0, xq[m][0], kOff * sx[m]);
+        a = dot8_words<XF16>(u1, xq[m][1], a);
+        a = dot8_words<XF16>(u2, xq[m][2], a);
+        a = dot8_words<XF16>(u3, xq[m][3], a);
+        acc[m][r] = fmaf(sc, fmaf(-z, sx[m], a), acc[m][r]);
+      }
+    }
   }
   if (c.p == T - 1) {
 #pragma unroll
-    for (int r = 0; r < kSRpw; ++r) {
-      const float v = wave_sum_to_lane63(acc[r]);
-      const int row = c.b * kSRpw + r;
-      if (lane == 63 && row < N) y[row] = XF16 ? f32_to_f16_rne(v) : f32_to_bf16_rne(v);
-    }
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const float v = wave_sum_to_lane63(acc[m][r]);
+        const int row = c.b * RPW + r;
+        if (lane == 63 && row < N)
+          y[(size_t)m * ldy + row] = XF16 ? f32_to_f16_rne(v) : f32_to_bf16_rne(v);
+      }
   }
 }
 
+// MT activation rows (x [MT, K]); y row m at y + m * ldy.  RPW weight rows
+// per work item (more rows reuse each activation read from LDS more often);
+// NT threads per workgroup.
 // Requires N * K/2 < 2^32 and N * (K/G) * 2 < 2^32 (the launcher splits N).
-template <bool SYM, bool TAB, bool XF16>
-__global__ __launch_bounds__(kThreads) void gemv_stream_kernel(
+template <int MT, int RPW, int NT, bool SYM, bool TAB, bool XF16>
+__global__ __launch_bounds__(NT) void gemv_stream_kernel(
     const uint16_t* __restrict__ x, int K, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
-    uint16_t* __restrict__ y) {
+    uint16_t* __restrict__ y, int ldy) {
   extern __shared__ uint4 lds[];
   const int T = (K + kStepK - 1) / kStepK;
-  uint4* xs = lds;                                      // [T][4][64] permuted x pairs
-  float* sxs = (float*)(xs + T * 256);                  // [T * 64] chunk sums
-  uint32_t* wtab = (uint32_t*)(sxs + T * 64);           // [T * 64] (TAB only)
+  uint4* xs = lds;                                      // [MT][T][4][64] permuted x pairs
+  float* sxs = (float*)(xs + MT * T * 256);             // [MT][T * 64] chunk sums
+  uint32_t* wtab = (uint32_t*)(sxs + MT * T * 64);      // [T * 64] (TAB only)
   uint32_t* stab = wtab + T * 64;                       // [T * 64] (TAB only)
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nb = (N + kSRpw - 1) / kSRpw;
-  const int W = gridDim.x * kWaves;
+  constexpr int NW = NT / 64;  // waves per workgroup
+  const int nb = (N + RPW - 1) / RPW;
+  const int W = gridDim.x * NW;
   const uint32_t rb = (uint32_t)K / 2;
   const uint32_t ngb = (uint32_t)(K / G) * 2;
   const uint32_t sgs = TAB ? 0u : (uint32_t)(kStepK / G) * 2;
@@ -310,7 +362,7 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(
   const rsrc_t rz = make_rsrc(SYM ? (const void*)scales : (const void*)zeros, (uint32_t)N * ngb);
 
   if (TAB) {  // byte offsets per (step, lane); lanes past K read out of range
-    for (int i = threadIdx.x; i < T * 64; i += kThreads) {
+    for (int i = threadIdx.x; i < T * 64; i += NT) {
       const int k = (i >> 6) * kStepK + (i & 63) * 32;
       wtab[i] = k < K ? (uint32_t)k / 2 : kOob;
       stab[i] = k < K ? (uint32_t)(k / G) * 2 : kOob;
@@ -319,49 +371,56 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(
   }
 
   // x: issue the first loads before the weight prefetch, stage after it.
+  // Flat chunk f = m T 256 + c holds x[m, 8c .. 8c + 8); a quad of lanes holds
+  // one 32-chunk of one row (T 256 is a multiple of 4).
   constexpr int kXr = 8;
+  const int TC = T * 256;  // chunks per activation row
   uint4 xv[kXr];
 #pragma unroll
   for (int i = 0; i < kXr; ++i) {
-    const int c = threadIdx.x + kThreads * i;
+    const int f = threadIdx.x + NT * i;
+    const int m = MT == 1 ? 0 : f / TC, c = f - m * TC;
     xv[i] = make_uint4(0, 0, 0, 0);
-    if (i < T && c * 8 < K) xv[i] = *(const uint4*)(x + c * 8);
+    if (f < MT * TC && c * 8 < K) xv[i] = *(const uint4*)(x + (size_t)m * K + c * 8);
   }
 
-  StreamBuf buf[kSNbuf];
-  float acc[kSRpw];
+  StreamBuf<RPW> buf[kSNbuf];
+  float acc[MT][RPW];
 #pragma unroll
-  for (int r = 0; r < kSRpw; ++r) acc[r] = 0.f;
-  Cursor lc{(int)blockIdx.x * kWaves + wave, 0};
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) acc[m][r] = 0.f;
+  Cursor lc{(int)blockIdx.x * NW + wave, 0};
   Cursor cc = lc;
 #pragma unroll
   for (int j = 0; j < kSNbuf - 1; ++j) {
-    stream_load<SYM, TAB>(buf[j], lc, N, rb, ngb, sgs, vw, vs, wtab, stab, lane, rw, rs, rz);
+    stream_load<RPW, SYM, TAB>(buf[j], lc, N, rb, ngb, sgs, vw, vs, wtab, stab, lane, rw, rs, rz);
     // keep the loads in item order: the loop's waits assume it
     __builtin_amdgcn_sched_barrier(0);
     advance(lc, T, W);
   }
 
-  for (int c0 = 0; c0 < T * 256; c0 += kXr * kThreads) {
+  for (int c0 = 0; c0 < MT * TC; c0 += kXr * NT) {
 #pragma unroll
     for (int i = 0; i < kXr; ++i) {
-      const int c = c0 + threadIdx.x + kThreads * i;
+      const int f = c0 + threadIdx.x + NT * i;
+      const int m = MT == 1 ? 0 : f / TC, c = f - m * TC;
       // every load issued here is consumed here: a load left in flight on
       // some path would make the main loop wait for all loads at its head
-      if (c0 + kThreads * i < T * 256) {  // uniform over the block
+      if (f < MT * TC) {
         uint4 v = xv[i];
         if (c0 > 0) {
           v = make_uint4(0, 0, 0, 0);
-          if (c * 8 < K) v = *(const uint4*)(x + c * 8);
+          if (c * 8 < K) v = *(const uint4*)(x + (size_t)m * K + c * 8);
         }
         // chunk c = 8 x values; lane l of step p reads its four chunks at
         // p*256 + j*64 + l (j = 0..3), so the 16-byte LDS reads of a wave are
         // consecutive and free of bank conflicts
-        xs[(c & ~255) | ((c & 3) << 6) | ((c >> 2) & 63)] = perm_x_pairs(v);
+        xs[m * TC + ((c & ~255) | ((c & 3) << 6) | ((c >> 2) & 63))] = perm_x_pairs(v);
         float sm = XF16 ? sum_f16x8(v) : sum_bf16x8(v);
         sm += __shfl_xor(sm, 1, 64);
         sm += __shfl_xor(sm, 2, 64);
-        if ((c & 3) == 0) sxs[c >> 2] = sm;
+        if ((c & 3) == 0) sxs[m * T * 64 + (c >> 2)] = sm;
       }
     }
   }
@@ -371,43 +430,67 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_kernel(
   // it: with its only exit at the bottom, the loop head waits for exactly the
   // item it multiplies (an exit in the middle would merge just-issued loads
   // into the head's wait), and no item is computed twice or padded.
-  const int b0 = (int)blockIdx.x * kWaves + wave;
+  const int b0 = (int)blockIdx.x * NW + wave;
   const int items = b0 < nb ? ((nb - 1 - b0) / W + 1) * T : 0;
   const int rounds = items / kSNbuf, rest = items % kSNbuf;
   for (int it = 0; it < rounds; ++it) {
 #pragma unroll
     for (int j = 0; j < kSNbuf; ++j) {
-      stream_load<SYM, TAB>(buf[(j + kSNbuf - 1) % kSNbuf], lc, N, rb, ngb, sgs, vw, vs, wtab, stab,
+      stream_load<RPW, SYM, TAB>(buf[(j + kSNbuf - 1) % kSNbuf], lc, N, rb, ngb, sgs, vw, vs, wtab, stab,
                             lane, rw, rs, rz);
       __builtin_amdgcn_sched_barrier(0);  // issue the loads before this item's wait
       advance(lc, T, W);
-      stream_compute<SYM, XF16>(buf[j], cc, T, N, lane, xs, sxs, y, magic, acc);
+      stream_compute<MT, RPW, SYM, XF16>(buf[j], cc, T, N, ldy, lane, xs, sxs, y, magic, acc);
       advance(cc, T, W);
     }
   }
   static_assert(kSNbuf == 3, "the tail below finishes at most two prefetched items");
   if (rest > 0) {
-    stream_compute<SYM, XF16>(buf[0], cc, T, N, lane, xs, sxs, y, magic, acc);
+    stream_compute<MT, RPW, SYM, XF16>(buf[0], cc, T, N, ldy, lane, xs, sxs, y, magic, acc);
     advance(cc, T, W);
   }
-  if (rest > 1) stream_compute<SYM, XF16>(buf[1], cc, T, N, lane, xs, sxs, y, magic, acc);
+  if (rest > 1) stream_compute<MT, RPW, SYM, XF16>(buf[1], cc, T, N, ldy, lane, xs, sxs, y, magic, acc);
 }
 
-template <bool SYM, bool TAB, bool XF16>
-hipError_t launch_stream(const uint16_t* x, int K, const uint8_t* qw, const uint16_t* sc,
-                         const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
-  const int T = (K + kStepK - 1) / kStepK;
-  const size_t lds = (size_t)T * (256 * 16 + 64 * 4) + (TAB ? (size_t)T * 64 * 8 : 0);
-  const int nb = (N + kSRpw - 1) / kSRpw;
-  const int grid = std::max(1, std::min((nb + kWaves - 1) / kWaves, 2 * num_cus()));
-  hipLaunchKernelGGL((gemv_stream_kernel<SYM, TAB, XF16>), dim3(grid), dim3(kThreads), lds, s, x, K,
-                     qw, sc, zr, N, G, y);
+template <int MT, int RPW, bool SYM, bool TAB, bool XF16>
+hipError_t launch_stream_rpw(const uint16_t* x, int K, const uint8_t* qw, const uint16_t* sc,
+                             const uint16_t* zr, int N, int G, uint16_t* y, int ldy, hipStream_t s) {
+  const size_t lds = stream_lds_bytes(MT, K, TAB);
+  const int nb = (N + RPW - 1) / RPW;
+  if constexpr (MT > 1) {
+    if (lds > kSLdsMulti) {  // one workgroup of 8 waves per compute unit
+      const int grid = std::max(1, std::min((nb + 7) / 8, num_cus()));
+      hipLaunchKernelGGL((gemv_stream_kernel<MT, RPW, 512, SYM, TAB, XF16>), dim3(grid), dim3(512),
+                         lds, s, x, K, qw, sc, zr, N, G, y, ldy);
+      return hipGetLastError();
+    }
+  }
+  const int grid = std::max(1, std::min((nb + 3) / 4, 2 * num_cus()));
+  hipLaunchKernelGGL((gemv_stream_kernel<MT, RPW, 256, SYM, TAB, XF16>), dim3(grid), dim3(256), lds,
+                     s, x, K, qw, sc, zr, N, G, y, ldy);
   return hipGetLastError();
 }
 
-template <bool SYM, bool XF16 = false>
-hipError_t stream_m1(const uint16_t* x, int K, const uint8_t* qw, const uint16_t* sc,
-                     const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
+// Two weight rows per item; with three or more activation rows four, when
+// every wave still gets about four items (each activation read from LDS then
+// serves four rows; with fewer items per wave the tail costs more than that
+// saves: measured on the Llama-3-8B shapes, four rows win on [28672, 4096]
+// only).
+template <int MT, bool SYM, bool TAB, bool XF16>
+hipError_t launch_stream(const uint16_t* x, int K, const uint8_t* qw, const uint16_t* sc,
+                         const uint16_t* zr, int N, int G, uint16_t* y, int ldy, hipStream_t s) {
+  if constexpr (MT >= 3) {
+    const int64_t T = (K + kStepK - 1) / kStepK;
+    const int64_t waves = (int64_t)num_cus() * 8;
+    if ((int64_t)((N + 3) / 4) * T >= 4 * waves)
+      return launch_stream_rpw<MT, 4, SYM, TAB, XF16>(x, K, qw, sc, zr, N, G, y, ldy, s);
+  }
+  return launch_stream_rpw<MT, 2, SYM, TAB, XF16>(x, K, qw, sc, zr, N, G, y, ldy, s);
+}
+
+template <int MT, bool SYM, bool XF16 = false>
+hipError_t stream_m(const uint16_t* x, int K, const uint8_t* qw, const uint16_t* sc,
+                    const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
   // Rows per launch so that every byte offset fits 32 bits.
   const uint64_t rb = (uint64_t)K / 2, ngb = (uint64_t)(K / G) * 2;
   const int64_t cap = (int64_t)std::min<uint64_t>(((uint64_t)1 << 31) / rb, ((uint64_t)1 << 31) / ngb);
@@ -417,13 +500,29 @@ hipError_t stream_m1(const uint16_t* x, int K, const uint8_t* qw, const uint16_t
     const uint8_t* q = qw + n0 * rb;
     const uint16_t* a = sc + n0 * (K / G);
     const uint16_t* b = SYM ? zr : zr + n0 * (K / G);
-    hipError_t e = tab ? launch_stream<SYM, true, XF16>(x, K, q, a, b, n, G, y + n0, s)
-                       : launch_stream<SYM, false, XF16>(x, K, q, a, b, n, G, y + n0, s);
+    hipError_t e = tab ? launch_stream<MT, SYM, true, XF16>(x, K, q, a, b, n, G, y + n0, N, s)
+                       : launch_stream<MT, SYM, false, XF16>(x, K, q, a, b, n, G, y + n0, N, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
+
+template <bool SYM>
+hipError_t stream_any(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
+                      const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
+  switch (M) {
+    case 1: return stream_m<1, SYM>(x, K, qw, sc, zr, N, G, y, s);
+    case 2: return stream_m<2, SYM>(x, K, qw, sc, zr, N, G, y, s);
+    case 3: return stream_m<3, SYM>(x, K, qw, sc, zr, N, G, y, s);
+    default: return stream_m<4, SYM>(x, K, qw, sc, zr, N, G, y, s);
+  }
+}
 }  // namespace
+
+bool gemv_stream_supported(int M, int64_t K) {
+  if (M == 1) return (K + kStepK - 1) / kStepK <= kSMaxT;
+  return M >= 2 && M <= kSMaxM && stream_lds_bytes(M, K, true) <= kSLdsOne;
+}
 
 bool gemv_f16_supported(int M, int64_t K) {
   return M == 1 && (K + kStepK - 1) / kStepK <= kSMaxT;
@@ -432,17 +531,17 @@ bool gemv_f16_supported(int M, int64_t K) {
 hipError_t launch_w4a16_gemv_f16(const uint16_t* x, int64_t K, const uint8_t* qweight,
                                  const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
                                  int symmetric, uint16_t* y, hipStream_t s) {
-  if (symmetric) return stream_m1<true, true>(x, (int)K, qweight, scales, zeros, (int)N, G, y, s);
-  return stream_m1<false, true>(x, (int)K, qweight, scales, zeros, (int)N, G, y, s);
+  if (symmetric) return stream_m<1, true, true>(x, (int)K, qweight, scales, zeros, (int)N, G, y, s);
+  return stream_m<1, false, true>(x, (int)K, qweight, scales, zeros, (int)N, G, y, s);
 }
 
 hipError_t launch_w4a16_gemv(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
                              const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
                              int symmetric, uint16_t* y, void* workspace, size_t ws_bytes,
                              hipStream_t s) {
-  if (M == 1 && (K + kStepK - 1) / kStepK <= kSMaxT) {
-    if (symmetric) return stream_m1<true>(x, (int)K, qweight, scales, zeros, (int)N, G, y, s);
-    return stream_m1<false>(x, (int)K, qweight, scales, zeros, (int)N, G, y, s);
+  if (gemv_stream_supported(M, K)) {
+    if (symmetric) return stream_any<true>(x, M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
+    return stream_any<false>(x, M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
   }
   if (gemv_mfma_supported(M, K, N, G)) {
     (void)ws_bytes;  // checked against gemv_workspace_bytes by the caller

@@ -366,7 +366,7 @@ bool gemv_mfma_supported(int M, int64_t K, int64_t N, int G) {
 }
 
 size_t gemv_workspace_bytes(int M, int64_t K, int64_t N, int G) {
-  if (!gemv_mfma_supported(M, K, N, G)) return 0;
+  if (gemv_stream_supported(M, K) || !gemv_mfma_supported(M, K, N, G)) return 0;
   return (size_t)((K + kKC - 1) / kKC) * (size_t)M * (size_t)N * sizeof(float);
 }
 

@@ -58,6 +58,32 @@ __device__ __forceinline__ float dot8_perm(uint32_t d, const uint4& xp, float a,
   return a;
 }
 
+// The four 16-bit pair words of dot8_perm (same order), for reuse against
+// several activation rows.
+__device__ __forceinline__ uint4 unpack8_words(uint32_t d, uint32_t magic) {
+  const uint32_t ev = d & 0x0F0F0F0Fu;
+  const uint32_t od = (d >> 4) & 0x0F0F0F0Fu;
+  return make_uint4(__builtin_amdgcn_perm(ev, magic, 0x01050104u),
+                    __builtin_amdgcn_perm(ev, magic, 0x01070106u),
+                    __builtin_amdgcn_perm(od, magic, 0x01050104u),
+                    __builtin_amdgcn_perm(od, magic, 0x01070106u));
+}
+
+// a + u . xp over four pair words (bf16 pairs, or fp16 pairs if XF16)
+template <bool XF16 = false>
+__device__ __forceinline__ float dot8_words(const uint4& u, const uint4& xp, float a) {
+  if (XF16) {
+    a = dot2h(u.x, xp.x, a);
+    a = dot2h(u.y, xp.y, a);
+    a = dot2h(u.z, xp.z, a);
+    return dot2h(u.w, xp.w, a);
+  }
+  a = dot2(u.x, xp.x, a);
+  a = dot2(u.y, xp.y, a);
+  a = dot2(u.z, xp.z, a);
+  return dot2(u.w, xp.w, a);
+}
+
 // x0..x7 (bf16, natural order in v) -> pairs (x0,x2) (x4,x6) (x1,x3) (x5,x7).
 __device__ __forceinline__ uint4 perm_x_pairs(uint4 v) {
   uint4 p;
