@@ -100,6 +100,34 @@ def test_stream_multi_row_layouts(M, N, K, sym, G):
     _run(x, qw, s, z, G, sym, f"[{N},{K}] M={M} sym={sym} G={G} (stream, M > 1)", rows=rows)
 
 
+@pytest.mark.parametrize("M", [5, 8, 9, 16])
+@pytest.mark.parametrize("N,K,sym,G", [
+    (203, 4096, True, 32), (203, 4096, False, 64), (203, 4096, False, 128),
+    (203, 4096, True, 256), (203, 4096, False, 512), (203, 4096, True, 1024),
+    (16387, 4096, False, 128),   # several row blocks per workgroup
+])
+def test_mfma_stream_shapes(M, N, K, sym, G):
+    # the matrix-core GEMV with every activation row in LDS and K split over a
+    # workgroup's waves (no scratch): all group classes, a partial last row
+    # block, rows beyond M dropped
+    assert B.gq_w4a16_gemv_workspace_size(M, K, N, G, sym) == 0
+    w, x = synth.small(N, K, M, seed=N + K + M + G)
+    qw, s, z = _oracle_weights(w, G, sym)
+    rows = None if N < 1000 else np.r_[0:64, N // 2:N // 2 + 64, N - 67:N]
+    _run(x, qw, s, z, G, sym, f"[{N},{K}] M={M} sym={sym} G={G} (matrix cores, streaming)", rows=rows)
+
+
+@pytest.mark.parametrize("M", [5, 8])
+@pytest.mark.parametrize("K", [2048, 8192])
+def test_mfma_stream_k_extents(M, K):
+    # 8 staged rows: K = 2048 runs 4 waves with one 512-wide item each, K = 8192
+    # 8 waves with two items each
+    assert B.gq_w4a16_gemv_workspace_size(M, K, 333, 64, False) == 0
+    w, x = synth.small(333, K, M, seed=M + K)
+    qw, s, z = _oracle_weights(w, 64, False)
+    _run(x, qw, s, z, 64, False, f"[333,{K}] M={M} asym G=64 (matrix cores, streaming)")
+
+
 def test_group_equals_k_and_outlier_blowup():
     """Per-row (group = K) quantization of the outlier case loses far more
     accuracy than group 128 (S08 page, outlier remarks); both GPU results are
@@ -133,10 +161,11 @@ def test_decode_shapes_full_size(name):
 
 
 @pytest.mark.parametrize("name,M", [("down", 2), ("down", 4), ("down", 8), ("down", 16),
-                                    ("gate_up", 2), ("gate_up", 3), ("gate_up", 4), ("qkv", 4)])
+                                    ("gate_up", 2), ("gate_up", 3), ("gate_up", 4), ("qkv", 4),
+                                    ("gate_up", 8), ("gate_up", 16), ("o", 12)])
 def test_small_batch_full_size_sym_g32(name, M):
-    # M <= 4 at K = 4096 (and M = 2 on down) take the streaming kernel, the
-    # rest the matrix-core kernel
+    # M <= 4 take the dot-product streaming kernel, M > 4 at K = 4096 the
+    # matrix-core streaming kernel, M > 4 on down the split-K matrix-core kernel
     w, _ = synth.decode_case(name)
     x, _ = synth.activations(M, w.shape[1], seed=2003)
     rows = np.sort(np.random.default_rng(4).choice(w.shape[0], 256, replace=False))
@@ -181,7 +210,7 @@ def test_slice_reduction_counters_reused():
     after use); larger grids and a caller's workspace use a second kernel.
     Calls of falling and rising N and M on one stream must match the workspace
     path bit for bit, and the oracle on sampled rows."""
-    K, G = 4096, 128
+    K, G = 4608, 128  # not a multiple of 2048: the split-K matrix-core path
     for M, N, seed in ((8, 3000, 90), (5, 64, 91), (16, 1000, 92), (8, 20000, 94), (8, 3000, 93)):
         announce(f"small-batch slice reduction M={M} N={N} K={K}")
         w, x = synth.small(N, K, M, seed=seed)
@@ -209,12 +238,13 @@ def test_workspace_entry_point_and_graph_replays():
     # the same kernels: identical bits.  Captured into a graph, the call gets its
     # scratch from torch's allocator and every replay must reproduce the eager
     # result, with other eager work on the stream between replays.
-    M, K, N, G = 12, 4096, 1000, 32
+    # (K = 4608 keeps the call on the split-K matrix-core path)
+    M, K, N, G = 12, 4608, 1000, 32
     w, x = synth.small(N, K, M, seed=77)
     qw, s, _ = _oracle_weights(w, G, True)
     xd, qd, sd = bf16_dev(x), u8_dev(qw), f16_dev(s)
     need = B.gq_w4a16_gemv_workspace_size(M, K, N, G, True)
-    assert need == 4 * M * N * 4
+    assert need == 5 * M * N * 4
     y_lib = B.gq_w4a16_gemv(xd, qd, sd, None, G, True)
     ws = torch.zeros(need + 64, dtype=torch.uint8, device=xd.device)
     y_ws = B.gq_w4a16_gemv(xd, qd, sd, None, G, True, workspace=ws)

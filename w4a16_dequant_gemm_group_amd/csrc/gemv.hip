@@ -543,6 +543,8 @@ hipError_t launch_w4a16_gemv(const uint16_t* x, int M, int64_t K, const uint8_t*
     if (symmetric) return stream_any<true>(x, M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
     return stream_any<false>(x, M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
   }
+  if (gemv_mfma_stream_supported(M, K, N, G))
+    return launch_w4a16_gemv_mfma_stream(x, M, K, qweight, scales, zeros, N, G, symmetric, y, s);
   if (gemv_mfma_supported(M, K, N, G)) {
     (void)ws_bytes;  // checked against gemv_workspace_bytes by the caller
     bool launched = false;

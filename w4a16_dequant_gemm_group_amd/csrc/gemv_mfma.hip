@@ -323,6 +323,238 @@ __global__ __launch_bounds__(256) void gemv_split_finalize_kernel(const float* _
 }
 
 
+// ---------------------------------------------------------------------------
+// Streaming variant (no scratch): every activation row in LDS, K split over the
+// waves of a workgroup, partial tiles added in LDS
+// ---------------------------------------------------------------------------
+//
+// A workgroup of NW waves owns a 16-row block of W at a time (persistent over
+// row blocks); wave w covers k in [w K/NW, (w+1) K/NW) in items of 512: lane
+// (n, g) loads 16 bytes of row n at k = k0 + 128 L + 32 g (L = 0..3) and the
+// scales (and zeros) of row n for the item, two items ahead of the one it
+// multiplies.  The operands, MFMAs and per-segment corrections are those of the
+// tile kernel above.  At the end of a row block each wave writes its 16 x 16
+// partial tile to LDS and, after a barrier, 16 M threads add the NW tiles in
+// wave order (deterministic) and store y rounded once to bf16.
+//
+// GQ: group size 32 << GQ (GQ = 4: 512 or any multiple of 512).  MR: staged
+// activation rows (8 or 16, >= M).  Requires K % (NW * 512) == 0 and the LDS of
+// mfma_stream_lds_bytes.
+constexpr int kMSItem = 512;  // k per item
+
+size_t mfma_stream_lds_bytes(int MR, int NW, int64_t K) {
+  return (size_t)MR * (size_t)(K / 8 + 1) * 16 + (size_t)(K / 32) * 16 * 4 + (size_t)NW * 64 * 16;
+}
+
+template <int GQ, bool SYM>
+struct MsBuf {
+  static constexpr int kHalves = GQ >= 4 ? 1 : (16 >> GQ);  // scale halves per item and lane
+  static constexpr int kWords = (kHalves + 1) / 2;
+  uint4 w[4];
+  uint32_t s[kWords], z[SYM ? 1 : kWords];
+};
+
+template <int GQ, bool SYM>
+__device__ __forceinline__ void ms_load(MsBuf<GQ, SYM>& B, int rb, int k0, int n, int g, int N, int K,
+                                        int G, rsrc_t rw, rsrc_t rs, rsrc_t rz) {
+  const int row = rb * 16 + n;
+  const bool rin = row < N;
+  const uint32_t rbytes = (uint32_t)K / 2;
+  const uint32_t wo = rin ? (uint32_t)row * rbytes + (uint32_t)(k0 + 32 * g) / 2 : kOob;
+#pragma unroll
+  for (int L = 0; L < 4; ++L) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, wo, rin ? 64u * L : 0u, 2);
+    B.w[L] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+  const uint32_t so = rin ? ((uint32_t)row * (uint32_t)(K / G) + (uint32_t)(k0 / G)) * 2u : kOob;
+  auto ld = [&](rsrc_t r, uint32_t* d) {
+    if constexpr (GQ == 0) {
+      const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, so, 0, 0);
+      const auto b = __builtin_amdgcn_raw_buffer_load_b128(r, so, rin ? 16u : 0u, 0);
+      d[0] = a[0]; d[1] = a[1]; d[2] = a[2]; d[3] = a[3];
+      d[4] = b[0]; d[5] = b[1]; d[6] = b[2]; d[7] = b[3];
+    } else if constexpr (GQ == 1) {
+      const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, so, 0, 0);
+      d[0] = a[0]; d[1] = a[1]; d[2] = a[2]; d[3] = a[3];
+    } else if constexpr (GQ == 2) {
+      const auto a = __builtin_amdgcn_raw_buffer_load_b64(r, so, 0, 0);
+      d[0] = a[0]; d[1] = a[1];
+    } else if constexpr (GQ == 3) {
+      d[0] = __builtin_amdgcn_raw_buffer_load_b32(r, so, 0, 0);
+    } else {
+      d[0] = __builtin_amdgcn_raw_buffer_load_b16(r, so, 0, 0);
+    }
+  };
+  ld(rs, B.s);
+  if (!SYM) ld(rz, B.z);
+}
+
+// scale/zero half of 32-chunk j (0..15) of the item
+template <int GQ>
+__device__ __forceinline__ uint16_t ms_half(const uint32_t* v, int j) {
+  const int h = GQ >= 4 ? 0 : (j >> GQ);
+  return (uint16_t)(v[h >> 1] >> (16 * (h & 1)));
+}
+
+template <int MR, int NW, int GQ, bool SYM>
+__global__ __launch_bounds__(NW * 64) void gemv_mfma_stream_kernel(
+    const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
+    uint16_t* __restrict__ y) {
+  constexpr int CPG = GQ >= 2 ? 4 : (1 << GQ);  // 32-chunks per correction segment
+  extern __shared__ uint4 lds4[];
+  const int XR = K / 8 + 1;                      // uint4 per staged x row (+1: no bank conflicts)
+  uint4* xs = lds4;                              // [MR][XR] permuted pairs
+  float* sxs = (float*)(xs + MR * XR);           // [K / 32][16] chunk sums (0 for m >= MR)
+  float* red = sxs + (K / 32) * 16;              // [NW][64][4] partial tiles
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int NB = (N + 15) / 16;
+  const int kw = K / NW;                         // k per wave
+  const int IPW = kw / kMSItem;                  // items per wave and row block
+  const rsrc_t rw = make_rsrc(qw, (uint32_t)N * (uint32_t)(K / 2));
+  const rsrc_t rs = make_rsrc(scales, (uint32_t)N * (uint32_t)(K / G) * 2);
+  const rsrc_t rz = make_rsrc(SYM ? (const void*)scales : (const void*)zeros, (uint32_t)N * (uint32_t)(K / G) * 2);
+  const int nrb = (int)blockIdx.x < NB ? (NB - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  const int items = nrb * IPW;                   // the same for every wave of the workgroup
+
+  // item i -> (row block, k0)
+  auto item_rb = [&](int i) { return (int)blockIdx.x + (i / IPW) * (int)gridDim.x; };
+  auto item_k0 = [&](int i) { return w * kw + (i % IPW) * kMSItem; };
+
+  MsBuf<GQ, SYM> buf[3];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    if (j < items) ms_load<GQ, SYM>(buf[j], item_rb(j), item_k0(j), n, g, N, K, G, rw, rs, rz);
+
+  // stage x (rows >= M and the chunk sums of rows >= MR are zero), eight
+  // 16-byte loads per thread in flight before any is used; MR K / 8 is a
+  // multiple of 8 NW 64, so every lane runs every batch (the quad shuffles)
+  constexpr int kUX = 8;
+  for (int f0 = 0; f0 < MR * (K / 8); f0 += kUX * NW * 64) {
+    uint4 v[kUX];
+#pragma unroll
+    for (int u = 0; u < kUX; ++u) {
+      const int f = f0 + u * NW * 64 + (int)threadIdx.x;
+      const int m = f / (K / 8), c = f - m * (K / 8);
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (m < M) v[u] = *(const uint4*)(x + (size_t)m * K + (size_t)c * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < kUX; ++u) {
+      const int f = f0 + u * NW * 64 + (int)threadIdx.x;
+      const int m = f / (K / 8), c = f - m * (K / 8);
+      xs[m * XR + c] = perm_x(v[u]);
+      float sm = dot2(v[u].x, 0x3F803F80u, 0.f);  // bf16 1.0 pairs
+      sm = dot2(v[u].y, 0x3F803F80u, sm);
+      sm = dot2(v[u].z, 0x3F803F80u, sm);
+      sm = dot2(v[u].w, 0x3F803F80u, sm);
+      sm += __shfl_xor(sm, 1, 64);
+      sm += __shfl_xor(sm, 2, 64);
+      if ((c & 3) == 0) sxs[(c >> 2) * 16 + m] = sm;
+    }
+  }
+  if (MR < 16) {
+    for (int i = threadIdx.x; i < (K / 32) * (16 - MR); i += NW * 64)
+      sxs[(i / (16 - MR)) * 16 + MR + i % (16 - MR)] = 0.f;
+  }
+  __syncthreads();
+
+  const uint32_t magic = 0x43004300u;
+  const int xrow = (n % MR) * XR;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const MsBuf<GQ, SYM>& B, int i) {
+    const int k0 = item_k0(i);
+    const int xc0 = k0 / 8, ch0 = k0 / 32;
+    f32x4_t D = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int L = 0; L < 4; ++L) {
+      uint32_t e0 = B.w[L].x, e1 = B.w[L].y, e2 = B.w[L].z, e3 = B.w[L].w;
+      transpose4(e0, e1, e2, e3);
+      const uint32_t ev[4] = {e0, e1, e2, e3};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 A = xs[xrow + xc0 + 16 * L + 4 * c + g];
+        const uint4 Bv = unpack8(ev[c], magic);
+        const f32x4_t Cin = (c % CPG == 0) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : D;
+        D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A),
+                                                    __builtin_bit_cast(bf16x8_t, Bv), Cin, 0, 0, 0);
+        if (c % CPG == CPG - 1) {
+          const int j = 4 * L + c;  // last 32-chunk of the segment
+          const float sc = f16_to_f32(ms_half<GQ>(B.s, j));
+          const float zc = 128.f + (SYM ? 8.f : f16_to_f32(ms_half<GQ>(B.z, j)));
+          float4 sx = *(const float4*)&sxs[(ch0 + j) * 16 + 4 * g];
+#pragma unroll
+          for (int q = 1; q < CPG; ++q) {
+            const float4 t = *(const float4*)&sxs[(ch0 + j - q) * 16 + 4 * g];
+            sx.x += t.x;
+            sx.y += t.y;
+            sx.z += t.z;
+            sx.w += t.w;
+          }
+          acc[0] = fmaf(sc, fmaf(-zc, sx.x, D[0]), acc[0]);
+          acc[1] = fmaf(sc, fmaf(-zc, sx.y, D[1]), acc[1]);
+          acc[2] = fmaf(sc, fmaf(-zc, sx.z, D[2]), acc[2]);
+          acc[3] = fmaf(sc, fmaf(-zc, sx.w, D[3]), acc[3]);
+        }
+      }
+    }
+    if (i % IPW == IPW - 1) {  // the row block is done: add the waves' tiles
+      *(float4*)&red[(w * 64 + lane) * 4] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      acc[0] = acc[1] = acc[2] = acc[3] = 0.f;
+      __syncthreads();
+      const int t = threadIdx.x;
+      if (t < 16 * M) {
+        const int m = t >> 4, nn = t & 15, rb = item_rb(i);
+        const int src = (nn + 16 * (m >> 2)) * 4 + (m & 3);
+        float v = 0.f;
+        for (int u = 0; u < NW; ++u) v += red[u * 256 + src];
+        const int row = rb * 16 + nn;
+        if (row < N) y[(size_t)m * N + row] = f32_to_bf16_rne(v);
+      }
+      __syncthreads();
+    }
+  };
+
+  // three register buffers: item i + 2 loads while item i is multiplied; whole
+  // rounds in the loop, the last 0-2 items after it
+  const int rounds = items / 3, rest = items % 3;
+  int i = 0;
+  for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      if (i + 2 < items)
+        ms_load<GQ, SYM>(buf[(j + 2) % 3], item_rb(i + 2), item_k0(i + 2), n, g, N, K, G, rw, rs, rz);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(buf[j], i);
+      ++i;
+    }
+  }
+  if (rest > 0) compute(buf[0], i++);
+  if (rest > 1) compute(buf[1], i++);
+}
+
+template <int MR, int NW, bool SYM>
+hipError_t launch_ms(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
+                     const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
+  const size_t lds = mfma_stream_lds_bytes(MR, NW, K);
+  const int per_cu = lds <= 80 * 1024 ? 2 : 1;
+  const int grid = std::max(1, std::min((N + 15) / 16, per_cu * num_cus()));
+#define GQ_MS_LAUNCH(GQ_)                                                                          \
+  hipLaunchKernelGGL((gemv_mfma_stream_kernel<MR, NW, GQ_, SYM>), dim3(grid), dim3(NW * 64), lds, \
+                     s, x, M, K, qw, sc, zr, N, G, y)
+  switch (G) {
+    case 32: GQ_MS_LAUNCH(0); break;
+    case 64: GQ_MS_LAUNCH(1); break;
+    case 128: GQ_MS_LAUNCH(2); break;
+    case 256: GQ_MS_LAUNCH(3); break;
+    default: GQ_MS_LAUNCH(4); break;
+  }
+#undef GQ_MS_LAUNCH
+  return hipGetLastError();
+}
+
 template <int CPG, bool SYM, bool FUSE>
 hipError_t launch_cpg(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
                       const uint16_t* zr, int N, int G, float* part, int splits, uint32_t* cnt,
@@ -356,6 +588,43 @@ hipError_t launch_all(const uint16_t* x, int M, int K, const uint8_t* qw, const 
 
 }  // namespace
 
+// The streaming matrix-core GEMV: 8 or 16 staged rows; 8 waves per workgroup
+// (one workgroup per compute unit), or with 8 staged rows and more than two
+// row blocks per compute unit 4 waves (two workgroups per compute unit: more
+// row blocks in flight; measured on [28672, 4096] 25 against 31 us at M = 8,
+// while [6144, 4096] and [4096, 4096] gain 0.7 and 1.2 us from 8 waves).
+static void mfma_stream_config(int M, int64_t K, int64_t N, int* MR, int* NW) {
+  *MR = M <= 8 ? 8 : 16;
+  *NW = M <= 8 && ((N + 15) / 16 > 2 * (int64_t)num_cus() || K % (8 * kMSItem) != 0) ? 4 : 8;
+}
+
+bool gemv_mfma_stream_supported(int M, int64_t K, int64_t N, int G) {
+  if (M < 4 || M > 16) return false;
+  if (G % 32 != 0 || (G < 512 && 512 % G != 0) || (G >= 512 && G % 512 != 0)) return false;
+  int MR, NW;
+  mfma_stream_config(M, K, N, &MR, &NW);
+  if (K % (NW * kMSItem) != 0) return false;
+  if (mfma_stream_lds_bytes(MR, NW, K) > (NW == 4 ? 80 * 1024 : 156 * 1024)) return false;
+  if (N * (K / 2) >= ((int64_t)1 << 31) || (int64_t)M * K * 2 >= ((int64_t)1 << 31)) return false;
+  return true;
+}
+
+hipError_t launch_w4a16_gemv_mfma_stream(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
+                                         const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                                         int G, int symmetric, uint16_t* y, hipStream_t s) {
+  int MR, NW;
+  mfma_stream_config(M, K, N, &MR, &NW);
+  const int k = (int)K, n = (int)N;
+  if (MR == 8 && NW == 4)
+    return symmetric ? launch_ms<8, 4, true>(x, M, k, qweight, scales, zeros, n, G, y, s)
+                     : launch_ms<8, 4, false>(x, M, k, qweight, scales, zeros, n, G, y, s);
+  if (MR == 8)
+    return symmetric ? launch_ms<8, 8, true>(x, M, k, qweight, scales, zeros, n, G, y, s)
+                     : launch_ms<8, 8, false>(x, M, k, qweight, scales, zeros, n, G, y, s);
+  return symmetric ? launch_ms<16, 8, true>(x, M, k, qweight, scales, zeros, n, G, y, s)
+                   : launch_ms<16, 8, false>(x, M, k, qweight, scales, zeros, n, G, y, s);
+}
+
 bool gemv_mfma_supported(int M, int64_t K, int64_t N, int G) {
   if (M < 4 || M > 16) return false;
   if (G != 32 && G != 64 && G % 128 != 0) return false;
@@ -366,7 +635,9 @@ bool gemv_mfma_supported(int M, int64_t K, int64_t N, int G) {
 }
 
 size_t gemv_workspace_bytes(int M, int64_t K, int64_t N, int G) {
-  if (gemv_stream_supported(M, K) || !gemv_mfma_supported(M, K, N, G)) return 0;
+  if (gemv_stream_supported(M, K) || gemv_mfma_stream_supported(M, K, N, G) ||
+      !gemv_mfma_supported(M, K, N, G))
+    return 0;
   return (size_t)((K + kKC - 1) / kKC) * (size_t)M * (size_t)N * sizeof(float);
 }
 

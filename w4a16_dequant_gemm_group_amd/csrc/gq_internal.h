@@ -125,6 +125,12 @@ hipError_t launch_w4a16_gemv(const uint16_t* x, int M, int64_t K, const uint8_t*
                              hipStream_t s);
 // Whether the persistent streaming GEMV (M = 1..4, no scratch) takes M rows at this K.
 bool gemv_stream_supported(int M, int64_t K);
+// Small-batch GEMV on the matrix cores with every activation row in LDS and K
+// split over the waves of a workgroup (no scratch), where it fits.
+bool gemv_mfma_stream_supported(int M, int64_t K, int64_t N, int G);
+hipError_t launch_w4a16_gemv_mfma_stream(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
+                                         const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                                         int G, int symmetric, uint16_t* y, hipStream_t s);
 // Small-batch GEMV on the matrix cores (4 <= M <= 16, split along K).  Sets
 // *launched = false without launching when it cannot run this call (no split
 // workspace while the stream is being captured); the caller then uses the
