@@ -25,7 +25,7 @@
  *     check and allocates nothing, with two exceptions, both per (device,
  *     stream), grown on demand, held until the process ends and never handed
  *     out while the stream is being captured (the call then runs unsplit
- *     kernels): gq_w4a16_gemv on its matrix-core path (below) keeps split-K
+ *     kernels): gq_w4a16_gemv on its split-K matrix-core path (below) keeps split-K
  *     partial sums (gq_w4a16_gemv_ws takes them from the caller instead), and
  *     gq_w4a16_gemm keeps split-K partial sums and per-tile counters when its
  *     output tiles fill at most half of the GPU.
@@ -159,8 +159,12 @@ gq_status gq_w4a16_gemv(const uint16_t* x, int64_t M, int64_t K, const uint8_t* 
 /* Scratch (bytes) that gq_w4a16_gemv_ws needs for these arguments, 0 when the
  * call runs without any.  1 <= M <= 4 runs a streaming kernel that needs none
  * while x fits its LDS stage (K <= 26624, 34816, 22528, 16384 for M = 1, 2,
- * 3, 4).  Otherwise, with 4 <= M <= 16, group_size 32, 64 or a multiple of
- * 128 and K % 256 == 0, the GEMV runs on the matrix cores split along K into
+ * 3, 4).  5 <= M <= 16 (and M = 4 beyond that K) runs a matrix-core kernel
+ * that needs none either when x fits its LDS stage and the group size is 32,
+ * 64, 128, 256 or a multiple of 512: K = 2048 or 4096 (also 8192 with
+ * M <= 8 and at most 32 rows per compute unit) for M <= 8, K = 4096 for
+ * M > 8.  Otherwise, with 4 <= M <= 16, group_size 32, 64 or a multiple of 128
+ * and K % 256 == 0, the GEMV runs on the matrix cores split along K into
  * 1024-wide slices and keeps fp32 partial sums per slice:
  * ceil(K / 1024) * M * N * 4 bytes.  Errors: those of gq_w4a16_gemv's argument
  * checks; INVALID_ARG for a NULL `bytes`. */
