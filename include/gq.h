@@ -160,10 +160,10 @@ gq_status gq_w4a16_gemv(const uint16_t* x, int64_t M, int64_t K, const uint8_t* 
  * call runs without any.  1 <= M <= 4 runs a streaming kernel that needs none
  * while x fits its LDS stage (K <= 26624, 34816, 22528, 16384 for M = 1, 2,
  * 3, 4).  5 <= M <= 16 (and M = 4 beyond that K) runs a matrix-core kernel
- * that needs none either when x fits its LDS stage and the group size is 32,
- * 64, 128, 256 or a multiple of 512: K = 2048 or 4096 (also 8192 with
- * M <= 8 and at most 32 rows per compute unit) for M <= 8, K = 4096 for
- * M > 8.  Otherwise, with 4 <= M <= 16, group_size 32, 64 or a multiple of 128
+ * that needs none either when the group size is 32,
+ * 64, 128, 256 or a multiple of 512 and K is a multiple of 512: any such K
+ * for M <= 8 (x staged in chunks of up to 8192 columns), K <= 4096 for M > 8.
+ * Otherwise, with 4 <= M <= 16, group_size 32, 64 or a multiple of 128
  * and K % 256 == 0, the GEMV runs on the matrix cores split along K into
  * 1024-wide slices and keeps fp32 partial sums per slice:
  * ceil(K / 1024) * M * N * 4 bytes.  Errors: those of gq_w4a16_gemv's argument

@@ -117,17 +117,19 @@ def test_other_entry_point_validation(lib):
 
 
 def test_gemv_workspace_size_and_validation(lib):
-    # the matrix-core path (4 <= M <= 16, G in {32, 64, 128k}, K % 256 == 0,
-    # and for M <= 4 only where x is too long for the streaming kernel's LDS)
+    # the split-K matrix-core path (4 <= M <= 16, G in {32, 64, 128k}, K % 256
+    # == 0, where neither streaming kernel takes the call: K % 512 != 0 for M > 4)
     # keeps ceil(K / 1024) * M * N fp32 partial sums; other calls need none
-    assert B.gq_w4a16_gemv_workspace_size(16, 14336, 4096, 32, True) == 14 * 16 * 4096 * 4
+    assert B.gq_w4a16_gemv_workspace_size(16, 14080, 4096, 32, True) == 14 * 16 * 4096 * 4
     assert B.gq_w4a16_gemv_workspace_size(8, 6400, 203, 128) == 7 * 8 * 203 * 4
-    assert B.gq_w4a16_gemv_workspace_size(4, 18432, 4096, 128) == 18 * 4 * 4096 * 4
+    assert B.gq_w4a16_gemv_workspace_size(4, 18176, 4096, 128) == 18 * 4 * 4096 * 4
     assert B.gq_w4a16_gemv_workspace_size(4, 16384, 4096, 128) == 0
     assert B.gq_w4a16_gemv_workspace_size(4, 4096, 4096, 128) == 0
     assert B.gq_w4a16_gemv_workspace_size(8, 4096, 4096, 128) == 0    # streaming matrix-core path
     assert B.gq_w4a16_gemv_workspace_size(16, 4096, 4096, 32, True) == 0
-    assert B.gq_w4a16_gemv_workspace_size(8, 4608, 4096, 128) == 5 * 8 * 4096 * 4
+    assert B.gq_w4a16_gemv_workspace_size(8, 14336, 4096, 32, True) == 0   # K in chunks
+    assert B.gq_w4a16_gemv_workspace_size(16, 14336, 4096, 32, True) == 14 * 16 * 4096 * 4
+    assert B.gq_w4a16_gemv_workspace_size(8, 4352, 4096, 128) == 5 * 8 * 4096 * 4
     assert B.gq_w4a16_gemv_workspace_size(3, 4096, 4096, 128) == 0
     assert B.gq_w4a16_gemv_workspace_size(1, 4096, 4096, 128) == 0
     assert B.gq_w4a16_gemv_workspace_size(8, 6528, 203, 128) == 0   # K % 256 != 0
@@ -137,13 +139,13 @@ def test_gemv_workspace_size_and_validation(lib):
     assert lib.gq_w4a16_gemv_workspace_size(8, 4096, 64, q(g=48), ctypes.byref(nbytes)) == B.GQ_ERR_INVALID_ARG
     assert lib.gq_w4a16_gemv_workspace_size(8, 4096, 64, q(), None) == B.GQ_ERR_INVALID_ARG
     # a needed workspace that is missing, too small or misaligned is rejected before any device call
-    need = B.gq_w4a16_gemv_workspace_size(8, 4608, 4096, 128)
-    args = (FAKE, 8, 4608, FAKE, FAKE, FAKE, 4096, q(), FAKE)
+    need = B.gq_w4a16_gemv_workspace_size(8, 4352, 4096, 128)
+    args = (FAKE, 8, 4352, FAKE, FAKE, FAKE, 4096, q(), FAKE)
     assert lib.gq_w4a16_gemv_ws(*args, None, need, None) == B.GQ_ERR_INVALID_ARG
     assert lib.gq_w4a16_gemv_ws(*args, FAKE, need - 4, None) == B.GQ_ERR_INVALID_ARG
     assert lib.gq_w4a16_gemv_ws(*args, FAKE_MIS, need, None) == B.GQ_ERR_MISALIGNED
     # the plain GEMV checks still apply
-    assert lib.gq_w4a16_gemv_ws(FAKE, 17, 4608, FAKE, FAKE, FAKE, 4096, q(), FAKE, FAKE, need, None) == B.GQ_ERR_INVALID_ARG
+    assert lib.gq_w4a16_gemv_ws(FAKE, 17, 4352, FAKE, FAKE, FAKE, 4096, q(), FAKE, FAKE, need, None) == B.GQ_ERR_INVALID_ARG
 
 
 def test_bench_entry_point_validation(lib):

@@ -117,12 +117,14 @@ def test_mfma_stream_shapes(M, N, K, sym, G):
     _run(x, qw, s, z, G, sym, f"[{N},{K}] M={M} sym={sym} G={G} (matrix cores, streaming)", rows=rows)
 
 
-@pytest.mark.parametrize("M", [5, 8])
-@pytest.mark.parametrize("K", [2048, 8192])
+@pytest.mark.parametrize("M", [5, 8, 13])
+@pytest.mark.parametrize("K", [1024, 2048, 6144, 8192, 14336, 16896])
 def test_mfma_stream_k_extents(M, K):
-    # 8 staged rows: K = 2048 runs 4 waves with one 512-wide item each, K = 8192
-    # 8 waves with two items each
-    assert B.gq_w4a16_gemv_workspace_size(M, K, 333, 64, False) == 0
+    # 8 staged rows: K = 2048 runs 4 waves with one 512-wide item each, 8192 8
+    # waves with two; longer K runs in chunks of x staged one after the other, a
+    # partial last chunk loading zeros (16 staged rows beyond K = 4096 take the
+    # split-K kernel)
+    assert (B.gq_w4a16_gemv_workspace_size(M, K, 333, 64, False) == 0) == (M <= 8 or K <= 4096)
     w, x = synth.small(333, K, M, seed=M + K)
     qw, s, z = _oracle_weights(w, 64, False)
     _run(x, qw, s, z, 64, False, f"[333,{K}] M={M} asym G=64 (matrix cores, streaming)")
@@ -210,7 +212,7 @@ def test_slice_reduction_counters_reused():
     after use); larger grids and a caller's workspace use a second kernel.
     Calls of falling and rising N and M on one stream must match the workspace
     path bit for bit, and the oracle on sampled rows."""
-    K, G = 4608, 128  # not a multiple of 2048: the split-K matrix-core path
+    K, G = 4352, 128  # not a multiple of 512: the split-K matrix-core path
     for M, N, seed in ((8, 3000, 90), (5, 64, 91), (16, 1000, 92), (8, 20000, 94), (8, 3000, 93)):
         announce(f"small-batch slice reduction M={M} N={N} K={K}")
         w, x = synth.small(N, K, M, seed=seed)
@@ -238,8 +240,8 @@ def test_workspace_entry_point_and_graph_replays():
     # the same kernels: identical bits.  Captured into a graph, the call gets its
     # scratch from torch's allocator and every replay must reproduce the eager
     # result, with other eager work on the stream between replays.
-    # (K = 4608 keeps the call on the split-K matrix-core path)
-    M, K, N, G = 12, 4608, 1000, 32
+    # (K = 4352, not a multiple of 512, keeps the call on the split-K matrix-core path)
+    M, K, N, G = 12, 4352, 1000, 32
     w, x = synth.small(N, K, M, seed=77)
     qw, s, _ = _oracle_weights(w, G, True)
     xd, qd, sd = bf16_dev(x), u8_dev(qw), f16_dev(s)

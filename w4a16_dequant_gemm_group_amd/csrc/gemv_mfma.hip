@@ -337,9 +337,14 @@ __global__ __launch_bounds__(256) void gemv_split_finalize_kernel(const float* _
 // partial tile to LDS and, after a barrier, 16 M threads add the NW tiles in
 // wave order (deterministic) and store y rounded once to bf16.
 //
+// When x is too long for LDS, K runs in chunks of KC (a multiple of NW 512):
+// the workgroup stages x[:, chunk] before each chunk's items (a barrier on
+// either side) and the tiles keep accumulating until the row block ends; items
+// at or past K (a partial last chunk) load zeros.
+//
 // GQ: group size 32 << GQ (GQ = 4: 512 or any multiple of 512).  MR: staged
-// activation rows (8 or 16, >= M).  Requires K % (NW * 512) == 0 and the LDS of
-// mfma_stream_lds_bytes.
+// activation rows (8 or 16, >= M).  Requires K % 512 == 0, KC % (NW * 512) ==
+// 0 and the LDS of mfma_stream_lds_bytes(MR, NW, KC).
 constexpr int kMSItem = 512;  // k per item
 
 size_t mfma_stream_lds_bytes(int MR, int NW, int64_t K) {
@@ -358,7 +363,7 @@ template <int GQ, bool SYM>
 __device__ __forceinline__ void ms_load(MsBuf<GQ, SYM>& B, int rb, int k0, int n, int g, int N, int K,
                                         int G, rsrc_t rw, rsrc_t rs, rsrc_t rz) {
   const int row = rb * 16 + n;
-  const bool rin = row < N;
+  const bool rin = row < N && k0 < K;  // k0 >= K: an item past a partial last chunk
   const uint32_t rbytes = (uint32_t)K / 2;
   const uint32_t wo = rin ? (uint32_t)row * rbytes + (uint32_t)(k0 + 32 * g) / 2 : kOob;
 #pragma unroll
@@ -396,22 +401,24 @@ __device__ __forceinline__ uint16_t ms_half(const uint32_t* v, int j) {
   return (uint16_t)(v[h >> 1] >> (16 * (h & 1)));
 }
 
-template <int MR, int NW, int GQ, bool SYM>
+template <int MR, int NW, int GQ, bool SYM, bool CHUNKED>
 __global__ __launch_bounds__(NW * 64) void gemv_mfma_stream_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
-    uint16_t* __restrict__ y) {
+    uint16_t* __restrict__ y, int KC) {
   constexpr int CPG = GQ >= 2 ? 4 : (1 << GQ);  // 32-chunks per correction segment
   extern __shared__ uint4 lds4[];
-  const int XR = K / 8 + 1;                      // uint4 per staged x row (+1: no bank conflicts)
-  uint4* xs = lds4;                              // [MR][XR] permuted pairs
-  float* sxs = (float*)(xs + MR * XR);           // [K / 32][16] chunk sums (0 for m >= MR)
-  float* red = sxs + (K / 32) * 16;              // [NW][64][4] partial tiles
+  const int XR = KC / 8 + 1;                     // uint4 per staged x row (+1: no bank conflicts)
+  uint4* xs = lds4;                              // [MR][XR] permuted pairs of the chunk
+  float* sxs = (float*)(xs + MR * XR);           // [KC / 32][16] chunk sums (0 for m >= MR)
+  float* red = sxs + (KC / 32) * 16;             // [NW][64][4] partial tiles
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int NB = (N + 15) / 16;
-  const int kw = K / NW;                         // k per wave
-  const int IPW = kw / kMSItem;                  // items per wave and row block
+  const int NCH = (K + KC - 1) / KC;             // K chunks
+  const int kw = KC / NW;                        // k per wave and chunk
+  const int IPC = kw / kMSItem;                  // items per wave and chunk
+  const int IPW = NCH * IPC;                     // items per wave and row block
   const rsrc_t rw = make_rsrc(qw, (uint32_t)N * (uint32_t)(K / 2));
   const rsrc_t rs = make_rsrc(scales, (uint32_t)N * (uint32_t)(K / G) * 2);
   const rsrc_t rz = make_rsrc(SYM ? (const void*)scales : (const void*)zeros, (uint32_t)N * (uint32_t)(K / G) * 2);
@@ -420,42 +427,50 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_stream_kernel(
 
   // item i -> (row block, k0)
   auto item_rb = [&](int i) { return (int)blockIdx.x + (i / IPW) * (int)gridDim.x; };
-  auto item_k0 = [&](int i) { return w * kw + (i % IPW) * kMSItem; };
+  auto item_k0 = [&](int i) {
+    const int j = i % IPW;
+    return (j / IPC) * KC + w * kw + (j % IPC) * kMSItem;
+  };
 
   MsBuf<GQ, SYM> buf[3];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
     if (j < items) ms_load<GQ, SYM>(buf[j], item_rb(j), item_k0(j), n, g, N, K, G, rw, rs, rz);
 
-  // stage x (rows >= M and the chunk sums of rows >= MR are zero), eight
-  // 16-byte loads per thread in flight before any is used; MR K / 8 is a
-  // multiple of 8 NW 64, so every lane runs every batch (the quad shuffles)
-  constexpr int kUX = 8;
-  for (int f0 = 0; f0 < MR * (K / 8); f0 += kUX * NW * 64) {
-    uint4 v[kUX];
+  // stage x[:, kb .. kb + KC) (rows >= M, k >= K and the chunk sums of rows
+  // >= MR are zero), eight 16-byte loads per thread in flight before any is
+  // used; MR KC / 8 is a multiple of 8 NW 64, so every lane runs every batch
+  // (the quad shuffles)
+  auto stage = [&](int kb) {
+    constexpr int kUX = 8;
+    const int CC = KC / 8;  // 16-byte chunks per row
+    for (int f0 = 0; f0 < MR * CC; f0 += kUX * NW * 64) {
+      uint4 v[kUX];
 #pragma unroll
-    for (int u = 0; u < kUX; ++u) {
-      const int f = f0 + u * NW * 64 + (int)threadIdx.x;
-      const int m = f / (K / 8), c = f - m * (K / 8);
-      v[u] = make_uint4(0, 0, 0, 0);
-      if (m < M) v[u] = *(const uint4*)(x + (size_t)m * K + (size_t)c * 8);
-    }
+      for (int u = 0; u < kUX; ++u) {
+        const int f = f0 + u * NW * 64 + (int)threadIdx.x;
+        const int m = f / CC, c = f - m * CC;
+        v[u] = make_uint4(0, 0, 0, 0);
+        if (m < M && kb + c * 8 < K) v[u] = *(const uint4*)(x + (size_t)m * K + (size_t)(kb + c * 8));
+      }
 #pragma unroll
-    for (int u = 0; u < kUX; ++u) {
-      const int f = f0 + u * NW * 64 + (int)threadIdx.x;
-      const int m = f / (K / 8), c = f - m * (K / 8);
-      xs[m * XR + c] = perm_x(v[u]);
-      float sm = dot2(v[u].x, 0x3F803F80u, 0.f);  // bf16 1.0 pairs
-      sm = dot2(v[u].y, 0x3F803F80u, sm);
-      sm = dot2(v[u].z, 0x3F803F80u, sm);
-      sm = dot2(v[u].w, 0x3F803F80u, sm);
-      sm += __shfl_xor(sm, 1, 64);
-      sm += __shfl_xor(sm, 2, 64);
-      if ((c & 3) == 0) sxs[(c >> 2) * 16 + m] = sm;
+      for (int u = 0; u < kUX; ++u) {
+        const int f = f0 + u * NW * 64 + (int)threadIdx.x;
+        const int m = f / CC, c = f - m * CC;
+        xs[m * XR + c] = perm_x(v[u]);
+        float sm = dot2(v[u].x, 0x3F803F80u, 0.f);  // bf16 1.0 pairs
+        sm = dot2(v[u].y, 0x3F803F80u, sm);
+        sm = dot2(v[u].z, 0x3F803F80u, sm);
+        sm = dot2(v[u].w, 0x3F803F80u, sm);
+        sm += __shfl_xor(sm, 1, 64);
+        sm += __shfl_xor(sm, 2, 64);
+        if ((c & 3) == 0) sxs[(c >> 2) * 16 + m] = sm;
+      }
     }
-  }
+  };
+  stage(0);
   if (MR < 16) {
-    for (int i = threadIdx.x; i < (K / 32) * (16 - MR); i += NW * 64)
+    for (int i = threadIdx.x; i < (KC / 32) * (16 - MR); i += NW * 64)
       sxs[(i / (16 - MR)) * 16 + MR + i % (16 - MR)] = 0.f;
   }
   __syncthreads();
@@ -466,7 +481,13 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_stream_kernel(
 
   auto compute = [&](const MsBuf<GQ, SYM>& B, int i) {
     const int k0 = item_k0(i);
-    const int xc0 = k0 / 8, ch0 = k0 / 32;
+    const int kb = (i % IPW) / IPC * KC;  // the item's chunk
+    if (CHUNKED && i > 0 && i % IPC == 0) {  // a new chunk: every wave is done with the last one
+      __syncthreads();
+      stage(kb);
+      __syncthreads();
+    }
+    const int xc0 = (k0 - kb) / 8, ch0 = (k0 - kb) / 32;
     f32x4_t D = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int L = 0; L < 4; ++L) {
@@ -536,14 +557,18 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_stream_kernel(
 }
 
 template <int MR, int NW, bool SYM>
-hipError_t launch_ms(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
+hipError_t launch_ms(const uint16_t* x, int M, int K, int KC, const uint8_t* qw, const uint16_t* sc,
                      const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
-  const size_t lds = mfma_stream_lds_bytes(MR, NW, K);
+  const size_t lds = mfma_stream_lds_bytes(MR, NW, KC);
   const int per_cu = lds <= 80 * 1024 ? 2 : 1;
   const int grid = std::max(1, std::min((N + 15) / 16, per_cu * num_cus()));
-#define GQ_MS_LAUNCH(GQ_)                                                                          \
-  hipLaunchKernelGGL((gemv_mfma_stream_kernel<MR, NW, GQ_, SYM>), dim3(grid), dim3(NW * 64), lds, \
-                     s, x, M, K, qw, sc, zr, N, G, y)
+#define GQ_MS_LAUNCH(GQ_)                                                                      \
+  if (KC < K)                                                                                  \
+    hipLaunchKernelGGL((gemv_mfma_stream_kernel<MR, NW, GQ_, SYM, true>), dim3(grid),          \
+                       dim3(NW * 64), lds, s, x, M, K, qw, sc, zr, N, G, y, KC);               \
+  else                                                                                         \
+    hipLaunchKernelGGL((gemv_mfma_stream_kernel<MR, NW, GQ_, SYM, false>), dim3(grid),         \
+                       dim3(NW * 64), lds, s, x, M, K, qw, sc, zr, N, G, y, KC)
   switch (G) {
     case 32: GQ_MS_LAUNCH(0); break;
     case 64: GQ_MS_LAUNCH(1); break;
@@ -588,23 +613,37 @@ hipError_t launch_all(const uint16_t* x, int M, int K, const uint8_t* qw, const 
 
 }  // namespace
 
-// The streaming matrix-core GEMV: 8 or 16 staged rows; 8 waves per workgroup
-// (one workgroup per compute unit), or with 8 staged rows and more than two
-// row blocks per compute unit 4 waves (two workgroups per compute unit: more
-// row blocks in flight; measured on [28672, 4096] 25 against 31 us at M = 8,
-// while [6144, 4096] and [4096, 4096] gain 0.7 and 1.2 us from 8 waves).
-static void mfma_stream_config(int M, int64_t K, int64_t N, int* MR, int* NW) {
+// The streaming matrix-core GEMV: 8 or 16 staged rows.  With 8 staged rows,
+// more than two row blocks per compute unit and x of at most 4096 columns, 4
+// waves per workgroup and two workgroups per compute unit (more row blocks in
+// flight: [28672, 4096] 25 against 31 us at M = 8); otherwise 8 waves and one
+// workgroup per compute unit ([6144, 4096] and [4096, 4096] gain 0.7 and
+// 1.2 us), with K in chunks of KC (the largest multiple of 4096 whose x fits
+// LDS: 8192 columns of 8 rows, 4096 of 16).  Chunks only with 8 staged rows:
+// with 16 the split-K kernel is faster on [4096, 14336] (24 against 30 us at
+// M = 16; 23 against 21.5 us at M = 8).  False if K or G do not fit.
+static bool mfma_stream_config(int M, int64_t K, int64_t N, int* MR, int* NW, int* KC) {
+  if (K % kMSItem != 0 || K > ((int64_t)1 << 24)) return false;
   *MR = M <= 8 ? 8 : 16;
-  *NW = M <= 8 && ((N + 15) / 16 > 2 * (int64_t)num_cus() || K % (8 * kMSItem) != 0) ? 4 : 8;
+  const bool many = (N + 15) / 16 > 2 * (int64_t)num_cus();
+  if (*MR == 8 && K % 2048 == 0 && mfma_stream_lds_bytes(8, 4, K) <= 80 * 1024 &&
+      (many || K % 4096 != 0)) {
+    *NW = 4;
+    *KC = (int)K;
+    return true;
+  }
+  *NW = 8;
+  const int kcmax = *MR == 8 ? 8192 : 4096;
+  *KC = (int)std::min<int64_t>(kcmax, (K + 4095) / 4096 * 4096);
+  if (*MR == 16 && *KC < K) return false;
+  return mfma_stream_lds_bytes(*MR, 8, *KC) <= 156 * 1024;
 }
 
 bool gemv_mfma_stream_supported(int M, int64_t K, int64_t N, int G) {
   if (M < 4 || M > 16) return false;
   if (G % 32 != 0 || (G < 512 && 512 % G != 0) || (G >= 512 && G % 512 != 0)) return false;
-  int MR, NW;
-  mfma_stream_config(M, K, N, &MR, &NW);
-  if (K % (NW * kMSItem) != 0) return false;
-  if (mfma_stream_lds_bytes(MR, NW, K) > (NW == 4 ? 80 * 1024 : 156 * 1024)) return false;
+  int MR, NW, KC;
+  if (!mfma_stream_config(M, K, N, &MR, &NW, &KC)) return false;
   if (N * (K / 2) >= ((int64_t)1 << 31) || (int64_t)M * K * 2 >= ((int64_t)1 << 31)) return false;
   return true;
 }
@@ -612,17 +651,17 @@ bool gemv_mfma_stream_supported(int M, int64_t K, int64_t N, int G) {
 hipError_t launch_w4a16_gemv_mfma_stream(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
                                          const uint16_t* scales, const uint16_t* zeros, int64_t N,
                                          int G, int symmetric, uint16_t* y, hipStream_t s) {
-  int MR, NW;
-  mfma_stream_config(M, K, N, &MR, &NW);
+  int MR, NW, KC;
+  if (!mfma_stream_config(M, K, N, &MR, &NW, &KC)) return hipErrorInvalidValue;
   const int k = (int)K, n = (int)N;
   if (MR == 8 && NW == 4)
-    return symmetric ? launch_ms<8, 4, true>(x, M, k, qweight, scales, zeros, n, G, y, s)
-                     : launch_ms<8, 4, false>(x, M, k, qweight, scales, zeros, n, G, y, s);
+    return symmetric ? launch_ms<8, 4, true>(x, M, k, KC, qweight, scales, zeros, n, G, y, s)
+                     : launch_ms<8, 4, false>(x, M, k, KC, qweight, scales, zeros, n, G, y, s);
   if (MR == 8)
-    return symmetric ? launch_ms<8, 8, true>(x, M, k, qweight, scales, zeros, n, G, y, s)
-                     : launch_ms<8, 8, false>(x, M, k, qweight, scales, zeros, n, G, y, s);
-  return symmetric ? launch_ms<16, 8, true>(x, M, k, qweight, scales, zeros, n, G, y, s)
-                   : launch_ms<16, 8, false>(x, M, k, qweight, scales, zeros, n, G, y, s);
+    return symmetric ? launch_ms<8, 8, true>(x, M, k, KC, qweight, scales, zeros, n, G, y, s)
+                     : launch_ms<8, 8, false>(x, M, k, KC, qweight, scales, zeros, n, G, y, s);
+  return symmetric ? launch_ms<16, 8, true>(x, M, k, KC, qweight, scales, zeros, n, G, y, s)
+                   : launch_ms<16, 8, false>(x, M, k, KC, qweight, scales, zeros, n, G, y, s);
 }
 
 bool gemv_mfma_supported(int M, int64_t K, int64_t N, int G) {
