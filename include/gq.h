@@ -199,9 +199,12 @@ gq_status gq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* 
  * fused kernel multiplies BF16/FP16 activations]: the same product as
  * gq_w4a16_gemv / gq_w4a16_gemm, x [M, K] fp16 and y [M, N] fp16 (rounded to
  * nearest even; overflow gives +-inf), fp32 accumulation.  Supported shapes:
- * gq_w4a16_gemv_f16 for M = 1 (K up to 26624); gq_w4a16_gemm_f16 for K % 64
- * == 0 and group_size 64, 128 or a multiple of 256.  Other shapes return
- * UNSUPPORTED.  Errors otherwise as the bf16 entry points. */
+ * gq_w4a16_gemv_f16 wherever gq_w4a16_gemv needs no scratch (M = 1..4 with
+ * K up to 26624, 34816, 22528, 16384; M = 5..16 with K % 512 == 0, group size
+ * 32, 64, 128, 256 or a multiple of 512, and K <= 4096 when M > 8);
+ * gq_w4a16_gemm_f16 for K % 64 == 0 and group_size 64, 128 or a multiple of
+ * 256.  Other shapes return UNSUPPORTED.  Errors otherwise as the bf16 entry
+ * points. */
 gq_status gq_w4a16_gemv_f16(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
                             const uint16_t* scales, const uint16_t* zeros, int64_t N,
                             gq_qparams p, uint16_t* y, void* stream);

@@ -189,7 +189,9 @@ def test_f16_entry_point_validation(lib):
     L = lib
     args = (FAKE, 1, 4096, FAKE, FAKE, FAKE, 4096)
     # only M = 1 for the GEMV, only the 256x256 kernel's shapes for the GEMM
-    assert L.gq_w4a16_gemv_f16(FAKE, 2, 4096, FAKE, FAKE, FAKE, 4096, q(), FAKE, None) == B.GQ_ERR_UNSUPPORTED
+    # fp16 GEMV: shapes of the split-K matrix-core path (no fp16 form) are UNSUPPORTED
+    assert L.gq_w4a16_gemv_f16(FAKE, 16, 14336, FAKE, FAKE, FAKE, 4096, q(), FAKE, None) == B.GQ_ERR_UNSUPPORTED
+    assert L.gq_w4a16_gemv_f16(FAKE, 9, 4352, FAKE, FAKE, FAKE, 4096, q(), FAKE, None) == B.GQ_ERR_UNSUPPORTED
     assert L.gq_w4a16_gemv_f16(FAKE, 17, 4096, FAKE, FAKE, FAKE, 4096, q(), FAKE, None) == B.GQ_ERR_INVALID_ARG
     assert L.gq_w4a16_gemv_f16(FAKE, 1, 28672, FAKE, FAKE, FAKE, 64, q(), FAKE, None) == B.GQ_ERR_UNSUPPORTED
     assert L.gq_w4a16_gemm_f16(FAKE, 64, 4096, FAKE, FAKE, FAKE, 4096, q(g=32), FAKE, None) == B.GQ_ERR_UNSUPPORTED

@@ -35,23 +35,31 @@ def _check(y, x_bits, qw, s, z, G, sym, what):
     assert ok, (what, rel, ratio)
 
 
-@pytest.mark.parametrize("N,K,G,sym", [
-    (203, 6144, 128, False),
-    (4096, 14336, 32, True),
-    (130, 6400, 64, False),     # K not a multiple of 2048: per-lane offset tables
-    (1, 2048, 2048, True),
-    (77, 6144, 64, False),      # two lanes per group
-    (203, 4096, 64, True),
-    (9001, 2048, 256, False),   # several items per wave
+@pytest.mark.parametrize("M,N,K,G,sym", [
+    (1, 203, 6144, 128, False),
+    (1, 4096, 14336, 32, True),
+    (1, 130, 6400, 64, False),     # K not a multiple of 2048: per-lane offset tables
+    (1, 1, 2048, 2048, True),
+    (1, 77, 6144, 64, False),      # two lanes per group
+    (1, 203, 4096, 64, True),
+    (1, 9001, 2048, 256, False),   # several items per wave
+    (2, 203, 6144, 128, False),    # streaming kernel, M activation rows
+    (3, 203, 4096, 32, True),
+    (4, 4096, 14336, 32, True),    # one 8-wave workgroup per compute unit
+    (4, 16387, 4096, 128, False),  # four weight rows per item
+    (5, 203, 4096, 64, False),     # matrix-core streaming kernel
+    (8, 4096, 14336, 128, False),  # x staged in chunks
+    (12, 3001, 4096, 256, True),
+    (16, 203, 4096, 32, True),
 ])
-def test_gemv_f16(N, K, G, sym):
+def test_gemv_f16(M, N, K, G, sym):
     qw, s, z = _weights(N, K, G, sym, seed=N + K)
-    x, _ = synth.activations_f16(1, K, seed=K, n_outlier_channels=2)
+    x, _ = synth.activations_f16(M, K, seed=K + M, n_outlier_channels=2)
     y = B.gq_w4a16_gemv_f16(_f16_dev(x), torch.from_numpy(qw).to(device()), _f16_dev(s),
                             None if sym else _f16_dev(z), G, sym)
     torch.cuda.synchronize()
-    assert y.dtype == torch.float16
-    _check(y, x, qw, s, None if sym else z, G, sym, f"gemv f16 [{N},{K}] G={G} sym={sym}")
+    assert y.dtype == torch.float16 and y.shape == (M, N)
+    _check(y, x, qw, s, None if sym else z, G, sym, f"gemv f16 M={M} [{N},{K}] G={G} sym={sym}")
 
 
 @pytest.mark.parametrize("M,N,K,G,sym", [
@@ -71,6 +79,15 @@ def test_gemm_f16(M, N, K, G, sym):
 
 
 def test_f16_unsupported_shapes_raise():
+    # the split-K matrix-core GEMV has no fp16 form: 16 rows at K = 14336, or
+    # K not a multiple of 512, return UNSUPPORTED
+    for M, K in ((16, 14336), (9, 4352)):
+        qw, s, z = _weights(64, K, 128, False, seed=M)
+        x, _ = synth.activations_f16(M, K, seed=3)
+        with pytest.raises(B.GqError) as e:
+            B.gq_w4a16_gemv_f16(_f16_dev(x), torch.from_numpy(qw).to(device()), _f16_dev(s),
+                                _f16_dev(z), 128, False)
+        assert e.value.status == B.GQ_ERR_UNSUPPORTED
     qw, s, z = _weights(64, 4096, 32, False, seed=1)
     x, _ = synth.activations_f16(64, 4096, seed=2)
     with pytest.raises(RuntimeError):   # G = 32 stays on the bf16-only GEMM kernel

@@ -256,7 +256,7 @@ def gq_w4a16_gemm(x, qweight, scales, zeros, group_size: int = 128, symmetric: b
 
 def gq_w4a16_gemv_f16(x, qweight, scales, zeros, group_size: int = 128, symmetric: bool = False,
                       y=None, stream=None):
-    """Fused W4A16 GEMV with fp16 activations, x fp16 [1, K] -> y fp16 [1, N]."""
+    """Fused W4A16 GEMV with fp16 activations, x fp16 [M<=16, K] -> y fp16 [M, N]."""
     return _matmul(lib().gq_w4a16_gemv_f16, "gq_w4a16_gemv_f16", x, qweight, scales, zeros,
                    group_size, symmetric, y, stream, torch.float16)
 

@@ -507,14 +507,14 @@ hipError_t stream_m(const uint16_t* x, int K, const uint8_t* qw, const uint16_t*
   return hipSuccess;
 }
 
-template <bool SYM>
+template <bool SYM, bool XF16 = false>
 hipError_t stream_any(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
                       const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
   switch (M) {
-    case 1: return stream_m<1, SYM>(x, K, qw, sc, zr, N, G, y, s);
-    case 2: return stream_m<2, SYM>(x, K, qw, sc, zr, N, G, y, s);
-    case 3: return stream_m<3, SYM>(x, K, qw, sc, zr, N, G, y, s);
-    default: return stream_m<4, SYM>(x, K, qw, sc, zr, N, G, y, s);
+    case 1: return stream_m<1, SYM, XF16>(x, K, qw, sc, zr, N, G, y, s);
+    case 2: return stream_m<2, SYM, XF16>(x, K, qw, sc, zr, N, G, y, s);
+    case 3: return stream_m<3, SYM, XF16>(x, K, qw, sc, zr, N, G, y, s);
+    default: return stream_m<4, SYM, XF16>(x, K, qw, sc, zr, N, G, y, s);
   }
 }
 }  // namespace
@@ -524,15 +524,20 @@ bool gemv_stream_supported(int M, int64_t K) {
   return M >= 2 && M <= kSMaxM && stream_lds_bytes(M, K, true) <= kSLdsOne;
 }
 
-bool gemv_f16_supported(int M, int64_t K) {
-  return M == 1 && (K + kStepK - 1) / kStepK <= kSMaxT;
+// fp16 activations: the streaming kernel (M = 1..4) and the matrix-core
+// streaming kernel (M = 4..16) where they take the shape.
+bool gemv_f16_supported(int M, int64_t K, int64_t N, int G) {
+  return gemv_stream_supported(M, K) || gemv_mfma_stream_supported(M, K, N, G);
 }
 
-hipError_t launch_w4a16_gemv_f16(const uint16_t* x, int64_t K, const uint8_t* qweight,
+hipError_t launch_w4a16_gemv_f16(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
                                  const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
                                  int symmetric, uint16_t* y, hipStream_t s) {
-  if (symmetric) return stream_m<1, true, true>(x, (int)K, qweight, scales, zeros, (int)N, G, y, s);
-  return stream_m<1, false, true>(x, (int)K, qweight, scales, zeros, (int)N, G, y, s);
+  if (gemv_stream_supported(M, K)) {
+    if (symmetric) return stream_any<true, true>(x, M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
+    return stream_any<false, true>(x, M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
+  }
+  return launch_w4a16_gemv_mfma_stream(x, M, K, qweight, scales, zeros, N, G, symmetric, y, s, true);
 }
 
 hipError_t launch_w4a16_gemv(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,

@@ -38,6 +38,8 @@ namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -65,6 +67,15 @@ __device__ __forceinline__ uint4 perm_x(uint4 v) {
                     __builtin_amdgcn_perm(v.w, v.z, 0x05040100u),
                     __builtin_amdgcn_perm(v.y, v.x, 0x07060302u),
                     __builtin_amdgcn_perm(v.w, v.z, 0x07060302u));
+}
+
+// a + the two 16-bit values of v (bf16 pairs, or fp16 pairs if XF16)
+template <bool XF16>
+__device__ __forceinline__ float dot2x(uint32_t v, float a) {
+  if constexpr (XF16)
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, v),
+                                  __builtin_bit_cast(f16x2_t, 0x3C003C00u), a, false);
+  return dot2(v, 0x3F803F80u, a);
 }
 
 // 8 nibbles -> bf16 128 + q in the same pair order
@@ -401,7 +412,8 @@ __device__ __forceinline__ uint16_t ms_half(const uint32_t* v, int j) {
   return (uint16_t)(v[h >> 1] >> (16 * (h & 1)));
 }
 
-template <int MR, int NW, int GQ, bool SYM, bool CHUNKED>
+// XF16: fp16 activations and output (fp16 MFMA, nibbles as fp16 1024 + q).
+template <int MR, int NW, int GQ, bool SYM, bool CHUNKED, bool XF16>
 __global__ __launch_bounds__(NW * 64) void gemv_mfma_stream_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
@@ -458,10 +470,10 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_stream_kernel(
         const int f = f0 + u * NW * 64 + (int)threadIdx.x;
         const int m = f / CC, c = f - m * CC;
         xs[m * XR + c] = perm_x(v[u]);
-        float sm = dot2(v[u].x, 0x3F803F80u, 0.f);  // bf16 1.0 pairs
-        sm = dot2(v[u].y, 0x3F803F80u, sm);
-        sm = dot2(v[u].z, 0x3F803F80u, sm);
-        sm = dot2(v[u].w, 0x3F803F80u, sm);
+        float sm = dot2x<XF16>(v[u].x, 0.f);  // against 1.0 pairs
+        sm = dot2x<XF16>(v[u].y, sm);
+        sm = dot2x<XF16>(v[u].z, sm);
+        sm = dot2x<XF16>(v[u].w, sm);
         sm += __shfl_xor(sm, 1, 64);
         sm += __shfl_xor(sm, 2, 64);
         if ((c & 3) == 0) sxs[(c >> 2) * 16 + m] = sm;
@@ -475,7 +487,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_stream_kernel(
   }
   __syncthreads();
 
-  const uint32_t magic = 0x43004300u;
+  const uint32_t magic = XF16 ? 0x64006400u : 0x43004300u;  // 1024 + q or 128 + q
+  constexpr float kOff = XF16 ? 1024.f : 128.f;
   const int xrow = (n % MR) * XR;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
 
@@ -499,12 +512,16 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_stream_kernel(
         const uint4 A = xs[xrow + xc0 + 16 * L + 4 * c + g];
         const uint4 Bv = unpack8(ev[c], magic);
         const f32x4_t Cin = (c % CPG == 0) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : D;
-        D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A),
-                                                    __builtin_bit_cast(bf16x8_t, Bv), Cin, 0, 0, 0);
+        if constexpr (XF16)
+          D = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, A),
+                                                     __builtin_bit_cast(f16x8_t, Bv), Cin, 0, 0, 0);
+        else
+          D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A),
+                                                      __builtin_bit_cast(bf16x8_t, Bv), Cin, 0, 0, 0);
         if (c % CPG == CPG - 1) {
           const int j = 4 * L + c;  // last 32-chunk of the segment
           const float sc = f16_to_f32(ms_half<GQ>(B.s, j));
-          const float zc = 128.f + (SYM ? 8.f : f16_to_f32(ms_half<GQ>(B.z, j)));
+          const float zc = kOff + (SYM ? 8.f : f16_to_f32(ms_half<GQ>(B.z, j)));
           float4 sx = *(const float4*)&sxs[(ch0 + j) * 16 + 4 * g];
 #pragma unroll
           for (int q = 1; q < CPG; ++q) {
@@ -532,7 +549,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_stream_kernel(
         float v = 0.f;
         for (int u = 0; u < NW; ++u) v += red[u * 256 + src];
         const int row = rb * 16 + nn;
-        if (row < N) y[(size_t)m * N + row] = f32_to_bf16_rne(v);
+        if (row < N)
+          y[(size_t)m * N + row] = XF16 ? __builtin_bit_cast(uint16_t, (_Float16)v) : f32_to_bf16_rne(v);
       }
       __syncthreads();
     }
@@ -556,7 +574,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_stream_kernel(
   if (rest > 1) compute(buf[1], i++);
 }
 
-template <int MR, int NW, bool SYM>
+template <int MR, int NW, bool SYM, bool XF16>
 hipError_t launch_ms(const uint16_t* x, int M, int K, int KC, const uint8_t* qw, const uint16_t* sc,
                      const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
   const size_t lds = mfma_stream_lds_bytes(MR, NW, KC);
@@ -564,10 +582,10 @@ hipError_t launch_ms(const uint16_t* x, int M, int K, int KC, const uint8_t* qw,
   const int grid = std::max(1, std::min((N + 15) / 16, per_cu * num_cus()));
 #define GQ_MS_LAUNCH(GQ_)                                                                      \
   if (KC < K)                                                                                  \
-    hipLaunchKernelGGL((gemv_mfma_stream_kernel<MR, NW, GQ_, SYM, true>), dim3(grid),          \
+    hipLaunchKernelGGL((gemv_mfma_stream_kernel<MR, NW, GQ_, SYM, true, XF16>), dim3(grid),    \
                        dim3(NW * 64), lds, s, x, M, K, qw, sc, zr, N, G, y, KC);               \
   else                                                                                         \
-    hipLaunchKernelGGL((gemv_mfma_stream_kernel<MR, NW, GQ_, SYM, false>), dim3(grid),         \
+    hipLaunchKernelGGL((gemv_mfma_stream_kernel<MR, NW, GQ_, SYM, false, XF16>), dim3(grid),   \
                        dim3(NW * 64), lds, s, x, M, K, qw, sc, zr, N, G, y, KC)
   switch (G) {
     case 32: GQ_MS_LAUNCH(0); break;
@@ -650,18 +668,19 @@ bool gemv_mfma_stream_supported(int M, int64_t K, int64_t N, int G) {
 
 hipError_t launch_w4a16_gemv_mfma_stream(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
                                          const uint16_t* scales, const uint16_t* zeros, int64_t N,
-                                         int G, int symmetric, uint16_t* y, hipStream_t s) {
+                                         int G, int symmetric, uint16_t* y, hipStream_t s, bool xf16) {
   int MR, NW, KC;
   if (!mfma_stream_config(M, K, N, &MR, &NW, &KC)) return hipErrorInvalidValue;
   const int k = (int)K, n = (int)N;
-  if (MR == 8 && NW == 4)
-    return symmetric ? launch_ms<8, 4, true>(x, M, k, KC, qweight, scales, zeros, n, G, y, s)
-                     : launch_ms<8, 4, false>(x, M, k, KC, qweight, scales, zeros, n, G, y, s);
-  if (MR == 8)
-    return symmetric ? launch_ms<8, 8, true>(x, M, k, KC, qweight, scales, zeros, n, G, y, s)
-                     : launch_ms<8, 8, false>(x, M, k, KC, qweight, scales, zeros, n, G, y, s);
-  return symmetric ? launch_ms<16, 8, true>(x, M, k, KC, qweight, scales, zeros, n, G, y, s)
-                   : launch_ms<16, 8, false>(x, M, k, KC, qweight, scales, zeros, n, G, y, s);
+#define GQ_MS_ROWS(MR_, NW_)                                                                       \
+  (xf16 ? (symmetric ? launch_ms<MR_, NW_, true, true>(x, M, k, KC, qweight, scales, zeros, n, G, y, s)   \
+                     : launch_ms<MR_, NW_, false, true>(x, M, k, KC, qweight, scales, zeros, n, G, y, s)) \
+        : (symmetric ? launch_ms<MR_, NW_, true, false>(x, M, k, KC, qweight, scales, zeros, n, G, y, s)  \
+                     : launch_ms<MR_, NW_, false, false>(x, M, k, KC, qweight, scales, zeros, n, G, y, s)))
+  if (MR == 8 && NW == 4) return GQ_MS_ROWS(8, 4);
+  if (MR == 8) return GQ_MS_ROWS(8, 8);
+  return GQ_MS_ROWS(16, 8);
+#undef GQ_MS_ROWS
 }
 
 bool gemv_mfma_supported(int M, int64_t K, int64_t N, int G) {

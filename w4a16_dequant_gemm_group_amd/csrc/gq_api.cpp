@@ -259,10 +259,10 @@ gq_status gq_w4a16_gemv_f16(const uint16_t* x, int64_t M, int64_t K, const uint8
   if (M > 16) return GQ_ERR_INVALID_ARG;
   if (gq_status s = check_w4_matmul(x, M, K, qweight, scales, zeros, N, p, y)) return s;
   if (M == 0 || N == 0) return GQ_OK;
-  if (!gq::gemv_f16_supported((int)M, K)) return GQ_ERR_UNSUPPORTED;
+  if (!gq::gemv_f16_supported((int)M, K, N, p.group_size)) return GQ_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   if (gq_status st = check_device(s)) return st;
-  return from_hip(gq::launch_w4a16_gemv_f16(x, K, qweight, scales, zeros, N, p.group_size,
+  return from_hip(gq::launch_w4a16_gemv_f16(x, (int)M, K, qweight, scales, zeros, N, p.group_size,
                                             p.symmetric, y, s));
 }
 

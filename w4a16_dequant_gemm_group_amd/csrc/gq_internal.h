@@ -130,7 +130,8 @@ bool gemv_stream_supported(int M, int64_t K);
 bool gemv_mfma_stream_supported(int M, int64_t K, int64_t N, int G);
 hipError_t launch_w4a16_gemv_mfma_stream(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
                                          const uint16_t* scales, const uint16_t* zeros, int64_t N,
-                                         int G, int symmetric, uint16_t* y, hipStream_t s);
+                                         int G, int symmetric, uint16_t* y, hipStream_t s,
+                                         bool xf16 = false);
 // Small-batch GEMV on the matrix cores (4 <= M <= 16, split along K).  Sets
 // *launched = false without launching when it cannot run this call (no split
 // workspace while the stream is being captured); the caller then uses the
@@ -147,8 +148,8 @@ hipError_t launch_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const uint
                              int symmetric, uint16_t* y, hipStream_t s);
 // fp16 activations and output: the M = 1 streaming GEMV and the 256 x 256 GEMM
 // kernel (K % 64 == 0, G = 64, 128 or a multiple of 256).
-bool gemv_f16_supported(int M, int64_t K);
-hipError_t launch_w4a16_gemv_f16(const uint16_t* x, int64_t K, const uint8_t* qweight,
+bool gemv_f16_supported(int M, int64_t K, int64_t N, int G);
+hipError_t launch_w4a16_gemv_f16(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
                                  const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
                                  int symmetric, uint16_t* y, hipStream_t s);
 bool gemm_f16_supported(int64_t K, int G);
