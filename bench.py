@@ -291,7 +291,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": None if tr is None else round(tr["mean_hbm_bytes_per_launch"]),
-                "kernel": f"{GEMV_KERNEL}<1,2,256,false,false,false> (M = 1, asym; all four projections)",
+                "kernel": f"{GEMV_KERNEL}<1,2,NT,false,false,false> (M = 1, asym; all four projections; NT = 256 threads at K = 4096, 512 on down)",
                 "bytes_per_launch": bytes_per_launch, "avg_launch_us": round(avg_launch_us, 3),
                 "frac_of_measured_read_ceiling": round(achieved / ceiling["GB/s"], 4),
                 # time of pure reads of the same byte counts over the time of the GEMVs
