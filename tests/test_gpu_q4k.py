@@ -40,7 +40,7 @@ def test_quantize_other_dtypes(dtype):
 
 
 @pytest.mark.parametrize("M", [1, 2, 4, 16])
-@pytest.mark.parametrize("N,K", [(77, 2304), (64, 256), (33, 18432), (1031, 4096), (37, 28672)])
+@pytest.mark.parametrize("N,K", [(77, 2304), (64, 256), (33, 18432), (1031, 4096), (1031, 10496), (37, 28672)])
 def test_gemv_small(M, N, K):
     """M = 1 with K up to 26624 takes the streaming kernel (ragged last step at
     2304 and 256, a second x staging pass at 18432, several row pairs per wave
