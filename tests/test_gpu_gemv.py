@@ -273,3 +273,41 @@ def test_workspace_entry_point_and_graph_replays():
         torch.cuda.synchronize()
         assert torch.equal(y_g, y_lib), f"replay {rep}"
         assert other.shape == (5, N)
+
+
+@pytest.mark.parametrize("M,K,N,G,sym", [
+    (3, 4096, 1000, 32, True),      # streaming kernel, three activation rows
+    (8, 4096, 1000, 128, False),    # matrix-core streaming kernel
+    (8, 14336, 500, 64, False),     # the same with x staged in chunks
+    (16, 4096, 700, 32, True),
+])
+def test_scratch_free_paths_under_graph_capture(M, K, N, G, sym):
+    # these calls need no workspace, so a captured graph holds only the
+    # kernel launch; every replay must reproduce the eager bits, with other
+    # eager work on the stream between replays
+    assert B.gq_w4a16_gemv_workspace_size(M, K, N, G, sym) == 0
+    w, x = synth.small(N, K, M, seed=M + K + N)
+    qw, s, z = _oracle_weights(w, G, sym)
+    xd, qd, sd, zd = bf16_dev(x), u8_dev(qw), f16_dev(s), None if sym else f16_dev(z)
+    y_eager = B.gq_w4a16_gemv(xd, qd, sd, zd, G, sym)
+    torch.cuda.synchronize()
+    ref = O.w4a16_reference(x, qw, s, None if sym else z, G, sym)
+    wh = O.dequantize_packed(qw, s, None if sym else z, G, sym)
+    assert_parity(bits16(y_eager), ref, O.bf16_to_f64(x), wh, f"[{N},{K}] M={M} G={G} eager")
+    y_g = torch.empty_like(y_eager)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        B.gq_w4a16_gemv(xd, qd, sd, zd, G, sym, y=y_g)
+        with torch.cuda.graph(g, stream=stream):
+            B.gq_w4a16_gemv(xd, qd, sd, zd, G, sym, y=y_g)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        y_g.zero_()
+        g.replay()
+        other = B.gq_w4a16_gemv(xd[:1], qd, sd, zd, G, sym)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_eager), f"replay {rep}"
+        assert other.shape == (1, N)
