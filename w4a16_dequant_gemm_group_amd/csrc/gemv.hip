@@ -458,11 +458,12 @@ hipError_t launch_stream_rpw(const uint16_t* x, int K, const uint8_t* qw, const 
   const size_t lds = stream_lds_bytes(MT, K, TAB);
   const int nb = (N + RPW - 1) / RPW;
   // One workgroup of 8 waves per compute unit (x staged once per compute unit)
-  // when x needs more LDS than two workgroups can have, and at M = 1 once K
-  // spans four or more 2048-steps ([4096, 14336]: 8.6 -> 8.0 us; the K = 4096
-  // shapes are faster with two workgroups of 4 waves: qkv 4.8 against 5.3 us).
+  // when x needs more LDS than two workgroups can have, and once K spans four
+  // or more 2048-steps ([4096, 14336]: M = 1 8.6 -> 8.0 us, M = 2 13.2 ->
+  // 10.2 us; the K = 4096 shapes are faster with two workgroups of 4 waves:
+  // qkv 4.8 against 5.3 us at M = 1).
   const int T = (K + kStepK - 1) / kStepK;
-  if (MT > 1 ? lds > kSLdsMulti : T >= 4) {
+  if (lds > kSLdsMulti || T >= 4) {
     const int grid = std::max(1, std::min((nb + 7) / 8, num_cus()));
     hipLaunchKernelGGL((gemv_stream_kernel<MT, RPW, 512, SYM, TAB, XF16>), dim3(grid), dim3(512),
                        lds, s, x, K, qw, sc, zr, N, G, y, ldy);
