@@ -501,41 +501,47 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_stream_kernel(
       __syncthreads();
     }
     const int xc0 = (k0 - kb) / 8, ch0 = (k0 - kb) / 32;
-    f32x4_t D = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int L = 0; L < 4; ++L) {
       uint32_t e0 = B.w[L].x, e1 = B.w[L].y, e2 = B.w[L].z, e3 = B.w[L].w;
       transpose4(e0, e1, e2, e3);
       const uint32_t ev[4] = {e0, e1, e2, e3};
+      // the step's MFMAs first (one accumulation chain per correction
+      // segment), then the segments' corrections: with one segment per chunk
+      // (G = 32) no correction waits for the MFMA just issued
+      f32x4_t Dq[4 / CPG];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const uint4 A = xs[xrow + xc0 + 16 * L + 4 * c + g];
         const uint4 Bv = unpack8(ev[c], magic);
-        const f32x4_t Cin = (c % CPG == 0) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : D;
+        const int sg = c / CPG;
+        const f32x4_t Cin = (c % CPG == 0) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : Dq[sg];
         if constexpr (XF16)
-          D = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, A),
-                                                     __builtin_bit_cast(f16x8_t, Bv), Cin, 0, 0, 0);
+          Dq[sg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, A),
+                                                          __builtin_bit_cast(f16x8_t, Bv), Cin, 0, 0, 0);
         else
-          D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A),
-                                                      __builtin_bit_cast(bf16x8_t, Bv), Cin, 0, 0, 0);
-        if (c % CPG == CPG - 1) {
-          const int j = 4 * L + c;  // last 32-chunk of the segment
-          const float sc = f16_to_f32(ms_half<GQ>(B.s, j));
-          const float zc = kOff + (SYM ? 8.f : f16_to_f32(ms_half<GQ>(B.z, j)));
-          float4 sx = *(const float4*)&sxs[(ch0 + j) * 16 + 4 * g];
+          Dq[sg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A),
+                                                           __builtin_bit_cast(bf16x8_t, Bv), Cin, 0, 0, 0);
+      }
 #pragma unroll
-          for (int q = 1; q < CPG; ++q) {
-            const float4 t = *(const float4*)&sxs[(ch0 + j - q) * 16 + 4 * g];
-            sx.x += t.x;
-            sx.y += t.y;
-            sx.z += t.z;
-            sx.w += t.w;
-          }
-          acc[0] = fmaf(sc, fmaf(-zc, sx.x, D[0]), acc[0]);
-          acc[1] = fmaf(sc, fmaf(-zc, sx.y, D[1]), acc[1]);
-          acc[2] = fmaf(sc, fmaf(-zc, sx.z, D[2]), acc[2]);
-          acc[3] = fmaf(sc, fmaf(-zc, sx.w, D[3]), acc[3]);
+      for (int sg = 0; sg < 4 / CPG; ++sg) {
+        const f32x4_t D = Dq[sg];
+        const int j = 4 * L + sg * CPG + CPG - 1;  // last 32-chunk of the segment
+        const float sc = f16_to_f32(ms_half<GQ>(B.s, j));
+        const float zc = kOff + (SYM ? 8.f : f16_to_f32(ms_half<GQ>(B.z, j)));
+        float4 sx = *(const float4*)&sxs[(ch0 + j) * 16 + 4 * g];
+#pragma unroll
+        for (int q = 1; q < CPG; ++q) {
+          const float4 t = *(const float4*)&sxs[(ch0 + j - q) * 16 + 4 * g];
+          sx.x += t.x;
+          sx.y += t.y;
+          sx.z += t.z;
+          sx.w += t.w;
         }
+        acc[0] = fmaf(sc, fmaf(-zc, sx.x, D[0]), acc[0]);
+        acc[1] = fmaf(sc, fmaf(-zc, sx.y, D[1]), acc[1]);
+        acc[2] = fmaf(sc, fmaf(-zc, sx.z, D[2]), acc[2]);
+        acc[3] = fmaf(sc, fmaf(-zc, sx.w, D[3]), acc[3]);
       }
     }
     if (i % IPW == IPW - 1) {  // the row block is done: add the waves' tiles
