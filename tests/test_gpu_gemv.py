@@ -117,9 +117,11 @@ def test_mfma_stream_shapes(M, N, K, sym, G):
     _run(x, qw, s, z, G, sym, f"[{N},{K}] M={M} sym={sym} G={G} (matrix cores, streaming)", rows=rows)
 
 
-@pytest.mark.parametrize("M", [5, 8, 13])
-@pytest.mark.parametrize("K", [1024, 2048, 6144, 8192, 14336, 16896])
+@pytest.mark.parametrize("M", [4, 5, 8, 13])
+@pytest.mark.parametrize("K", [1024, 2048, 6144, 8192, 14336, 16896, 18432])
 def test_mfma_stream_k_extents(M, K):
+    # (M = 4 takes the dot-product streaming kernel up to K = 16384 and the
+    # matrix-core one, in chunks, beyond)
     # 8 staged rows: K = 2048 runs 4 waves with one 512-wide item each, 8192 8
     # waves with two; longer K runs in chunks of x staged one after the other, a
     # partial last chunk loading zeros (16 staged rows beyond K = 4096 take the
