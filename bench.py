@@ -54,6 +54,15 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "w4a16_gemv_stream_traffic.json")
 GEMV_KERNEL = "gemv_stream_kernel"
 CALIB_BYTES = 256 << 20          # calibration copy: reads and writes this many bytes
 G = 128
+# which kernel serves each small-batch M on the four projections (sym g32)
+SMALL_BATCH_KERNELS = {
+    1: "gemv_stream_kernel (dot products, one activation row)",
+    2: "gemv_stream_kernel (dot products, 2 activation rows in LDS)",
+    3: "gemv_stream_kernel (dot products, 3 activation rows in LDS)",
+    4: "gemv_stream_kernel (dot products, 4 activation rows in LDS)",
+    5: "gemv_mfma_stream_kernel (matrix cores, no scratch) on qkv/o/gate_up and on down up to "
+       "M = 8; split-K gemv_mfma_tile_kernel + finalize on down above M = 8",
+}
 
 
 def log(msg):
@@ -603,8 +612,11 @@ def run_extras(torch, B, synth, to_dev, dev, stream, shapes, W, X, gate, fused_s
         sb_step(0)
         us = graph_time(torch, stream, sb_step, 4 * Rs)
         tot_b = sum(gemv_bytes(n, k, 32, m, True) for _, n, k in shapes)
-        sb[f"M={m}"] = {"us_per_step": round(us, 2), "GB/s": round(tot_b / (us * 1e-6) / 1e9, 1),
-                        "TFLOP/s": round(2.0 * m * sum(n * k for _, n, k in shapes) / (us * 1e-6) / 1e12, 2)}
+        gbps = tot_b / (us * 1e-6) / 1e9
+        sb[f"M={m}"] = {"us_per_step": round(us, 2), "GB/s": round(gbps, 1),
+                        "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                        "TFLOP/s": round(2.0 * m * sum(n * k for _, n, k in shapes) / (us * 1e-6) / 1e12, 2),
+                        "kernels": SMALL_BATCH_KERNELS[min(m, 5)]}
     del sym_copies, sym_w, gate_w
     ex["small_batch_sym_g32"] = sb
     log(f"small batch {sb}")
