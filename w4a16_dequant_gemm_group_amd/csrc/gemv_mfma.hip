@@ -1,4 +1,7 @@
-// Small-batch W4A16 GEMV (4 <= M <= 16) on bf16 MFMA, split along K.
+// Small-batch W4A16 GEMV (4 <= M <= 16) on the matrix cores: a streaming
+// kernel without scratch (every activation row in LDS, K split over the waves
+// of a workgroup; bf16 or fp16 activations) where x fits, and a tile kernel
+// split along K with partial sums in scratch otherwise.
 //
 // Same product as the streaming GEMV ("vLLM 量化与推测解码" section 2, fused
 // W4A16 paragraph; "量化" page, "工作原理" figure right panel):
@@ -21,8 +24,8 @@
 //  * per group segment, the offset and zero point are removed with the chunk
 //    sums of x and the scale applied in fp32:
 //      acc[m][n] += S * (D[m][n] - (128 + z) * sum_{k in segment} x[m][k]).
-// A workgroup (4 waves, 64 rows) covers a 1024-wide slice of K and writes fp32
-// partial sums.  With library scratch, the last workgroup of a 64-row group to
+// Tile kernel: a workgroup (4 waves, 64 rows) covers a 1024-wide slice of K
+// and writes fp32 partial sums.  With library scratch, the last workgroup of a 64-row group to
 // finish (a per-group counter) adds the slices; with a caller's workspace (no
 // counters that are known to be zero) a second kernel does.  Either way the
 // slices are added in slice order (so the result does not depend on
@@ -346,7 +349,8 @@ __global__ __launch_bounds__(256) void gemv_split_finalize_kernel(const float* _
 // multiplies.  The operands, MFMAs and per-segment corrections are those of the
 // tile kernel above.  At the end of a row block each wave writes its 16 x 16
 // partial tile to LDS and, after a barrier, 16 M threads add the NW tiles in
-// wave order (deterministic) and store y rounded once to bf16.
+// wave order (deterministic) and store y rounded once to bf16 (fp16 when the
+// activations are fp16).
 //
 // When x is too long for LDS, K runs in chunks of KC (a multiple of NW 512):
 // the workgroup stages x[:, chunk] before each chunk's items (a barrier on
