@@ -448,43 +448,54 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_stream_kernel(
     return (j / IPC) * KC + w * kw + (j % IPC) * kMSItem;
   };
 
+  // stage x[:, kb .. kb + KC) (rows >= M, k >= K and the chunk sums of rows
+  // >= MR are zero) in batches of eight 16-byte loads per thread, all in flight
+  // before any is used; MR KC / 8 is a multiple of 8 NW 64, so every lane runs
+  // every batch (the quad shuffles)
+  constexpr int kUX = 8;
+  const int CC = KC / 8;  // 16-byte chunks per row
+  auto stage_load = [&](int kb, int f0, uint4 (&v)[kUX]) {
+#pragma unroll
+    for (int u = 0; u < kUX; ++u) {
+      const int f = f0 + u * NW * 64 + (int)threadIdx.x;
+      const int m = f / CC, c = f - m * CC;
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (m < M && kb + c * 8 < K) v[u] = *(const uint4*)(x + (size_t)m * K + (size_t)(kb + c * 8));
+    }
+  };
+  auto stage_store = [&](int f0, const uint4 (&v)[kUX]) {
+#pragma unroll
+    for (int u = 0; u < kUX; ++u) {
+      const int f = f0 + u * NW * 64 + (int)threadIdx.x;
+      const int m = f / CC, c = f - m * CC;
+      xs[m * XR + c] = perm_x(v[u]);
+      float sm = dot2x<XF16>(v[u].x, 0.f);  // against 1.0 pairs
+      sm = dot2x<XF16>(v[u].y, sm);
+      sm = dot2x<XF16>(v[u].z, sm);
+      sm = dot2x<XF16>(v[u].w, sm);
+      sm += __shfl_xor(sm, 1, 64);
+      sm += __shfl_xor(sm, 2, 64);
+      if ((c & 3) == 0) sxs[(c >> 2) * 16 + m] = sm;
+    }
+  };
+  auto stage = [&](int kb, int from) {
+    for (int f0 = from; f0 < MR * CC; f0 += kUX * NW * 64) {
+      uint4 v[kUX];
+      stage_load(kb, f0, v);
+      stage_store(f0, v);
+    }
+  };
+
+  // the first x batch is issued before the weight prefetch, so staging it
+  // does not wait for the weights (loads retire in order)
+  uint4 xv0[kUX];
+  stage_load(0, 0, xv0);
   MsBuf<GQ, SYM> buf[3];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
     if (j < items) ms_load<GQ, SYM>(buf[j], item_rb(j), item_k0(j), n, g, N, K, G, rw, rs, rz);
-
-  // stage x[:, kb .. kb + KC) (rows >= M, k >= K and the chunk sums of rows
-  // >= MR are zero), eight 16-byte loads per thread in flight before any is
-  // used; MR KC / 8 is a multiple of 8 NW 64, so every lane runs every batch
-  // (the quad shuffles)
-  auto stage = [&](int kb) {
-    constexpr int kUX = 8;
-    const int CC = KC / 8;  // 16-byte chunks per row
-    for (int f0 = 0; f0 < MR * CC; f0 += kUX * NW * 64) {
-      uint4 v[kUX];
-#pragma unroll
-      for (int u = 0; u < kUX; ++u) {
-        const int f = f0 + u * NW * 64 + (int)threadIdx.x;
-        const int m = f / CC, c = f - m * CC;
-        v[u] = make_uint4(0, 0, 0, 0);
-        if (m < M && kb + c * 8 < K) v[u] = *(const uint4*)(x + (size_t)m * K + (size_t)(kb + c * 8));
-      }
-#pragma unroll
-      for (int u = 0; u < kUX; ++u) {
-        const int f = f0 + u * NW * 64 + (int)threadIdx.x;
-        const int m = f / CC, c = f - m * CC;
-        xs[m * XR + c] = perm_x(v[u]);
-        float sm = dot2x<XF16>(v[u].x, 0.f);  // against 1.0 pairs
-        sm = dot2x<XF16>(v[u].y, sm);
-        sm = dot2x<XF16>(v[u].z, sm);
-        sm = dot2x<XF16>(v[u].w, sm);
-        sm += __shfl_xor(sm, 1, 64);
-        sm += __shfl_xor(sm, 2, 64);
-        if ((c & 3) == 0) sxs[(c >> 2) * 16 + m] = sm;
-      }
-    }
-  };
-  stage(0);
+  stage_store(0, xv0);
+  stage(0, kUX * NW * 64);
   if (MR < 16) {
     for (int i = threadIdx.x; i < (KC / 32) * (16 - MR); i += NW * 64)
       sxs[(i / (16 - MR)) * 16 + MR + i % (16 - MR)] = 0.f;
@@ -501,7 +512,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_stream_kernel(
     const int kb = (i % IPW) / IPC * KC;  // the item's chunk
     if (CHUNKED && i > 0 && i % IPC == 0) {  // a new chunk: every wave is done with the last one
       __syncthreads();
-      stage(kb);
+      stage(kb, 0);
       __syncthreads();
     }
     const int xc0 = (k0 - kb) / 8, ch0 = (k0 - kb) / 32;
