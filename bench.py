@@ -197,6 +197,10 @@ def main():
             _, xb = synth.prefill_case(nm)
             qw, s, z = W[nm]
             B.gq_w4a16_gemm(to_dev(xb), qw, s, z, G, False)
+        for nm, n, k in shapes:   # one small-batch GEMV per projection (M = 8, matrix cores)
+            qw, s, z = W[nm]
+            x8, _ = synth.activations(8, k, seed=2000 + synth.SHAPE_ORDER.index(nm))
+            B.gq_w4a16_gemv(to_dev(x8), qw, s, z, G, False)
         a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
         torch.neg(a, out=b)

@@ -359,11 +359,15 @@ __global__ __launch_bounds__(256) void gemv_split_finalize_kernel(const float* _
 //
 // GQ: group size 32 << GQ (GQ = 4: 512 or any multiple of 512).  MR: staged
 // activation rows (8 or 16, >= M).  Requires K % 512 == 0, KC % (NW * 512) ==
-// 0 and the LDS of mfma_stream_lds_bytes(MR, NW, KC).
+// 0 and the LDS of mfma_stream_lds_bytes(MR, NW, KC, chunked).
 constexpr int kMSItem = 512;  // k per item
 
-size_t mfma_stream_lds_bytes(int MR, int NW, int64_t K) {
-  return (size_t)MR * (size_t)(K / 8 + 1) * 16 + (size_t)(K / 32) * 16 * 4 + (size_t)NW * 64 * 16;
+// Chunk sums are stored for the MR staged rows plus a zeroed slot read by the
+// lanes of rows >= MR; the chunked form keeps 16 rows per chunk (rows >= MR
+// zero), which measured faster there.
+size_t mfma_stream_lds_bytes(int MR, int NW, int64_t KC, bool chunked) {
+  const size_t sums = chunked ? (size_t)(KC / 32) * 16 * 4 : (size_t)(KC / 32) * MR * 4 + 16;
+  return (size_t)MR * (size_t)(KC / 8 + 1) * 16 + sums + (size_t)NW * 64 * 16;
 }
 
 template <int GQ, bool SYM>
@@ -417,8 +421,10 @@ __device__ __forceinline__ uint16_t ms_half(const uint32_t* v, int j) {
 }
 
 // XF16: fp16 activations and output (fp16 MFMA, nibbles as fp16 1024 + q).
+// Two workgroups per compute unit with 8 staged rows and 8 waves: the launch
+// bounds ask for four waves per SIMD (at most 128 registers).
 template <int MR, int NW, int GQ, bool SYM, bool CHUNKED, bool XF16>
-__global__ __launch_bounds__(NW * 64) void gemv_mfma_stream_kernel(
+__global__ __launch_bounds__(NW * 64, MR == 8 && NW == 8 && !CHUNKED ? 4 : 1) void gemv_mfma_stream_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
     uint16_t* __restrict__ y, int KC) {
@@ -426,8 +432,10 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_stream_kernel(
   extern __shared__ uint4 lds4[];
   const int XR = KC / 8 + 1;                     // uint4 per staged x row (+1: no bank conflicts)
   uint4* xs = lds4;                              // [MR][XR] permuted pairs of the chunk
-  float* sxs = (float*)(xs + MR * XR);           // [KC / 32][16] chunk sums (0 for m >= MR)
-  float* red = sxs + (KC / 32) * 16;             // [NW][64][4] partial tiles
+  constexpr int SXW = CHUNKED ? 16 : MR;         // chunk-sum rows stored per 32-chunk
+  float* sxs = (float*)(xs + MR * XR);           // [KC / 32][SXW] chunk sums (+ 4 zeros)
+  const int zslot = (KC / 32) * SXW;             // the zero slot (SXW == MR)
+  float* red = sxs + zslot + (CHUNKED ? 0 : 4);  // [NW][64][4] partial tiles
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int NB = (N + 15) / 16;
@@ -475,7 +483,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_stream_kernel(
       sm = dot2x<XF16>(v[u].w, sm);
       sm += __shfl_xor(sm, 1, 64);
       sm += __shfl_xor(sm, 2, 64);
-      if ((c & 3) == 0) sxs[(c >> 2) * 16 + m] = sm;
+      if ((c & 3) == 0) sxs[(c >> 2) * SXW + m] = sm;
     }
   };
   auto stage = [&](int kb, int from) {
@@ -496,7 +504,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_stream_kernel(
     if (j < items) ms_load<GQ, SYM>(buf[j], item_rb(j), item_k0(j), n, g, N, K, G, rw, rs, rz);
   stage_store(0, xv0);
   stage(0, kUX * NW * 64);
-  if (MR < 16) {
+  if (SXW == MR) {
+    if (threadIdx.x < 4) sxs[zslot + threadIdx.x] = 0.f;
+  } else {
     for (int i = threadIdx.x; i < (KC / 32) * (16 - MR); i += NW * 64)
       sxs[(i / (16 - MR)) * 16 + MR + i % (16 - MR)] = 0.f;
   }
@@ -544,10 +554,13 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_stream_kernel(
         const int j = 4 * L + sg * CPG + CPG - 1;  // last 32-chunk of the segment
         const float sc = f16_to_f32(ms_half<GQ>(B.s, j));
         const float zc = kOff + (SYM ? 8.f : f16_to_f32(ms_half<GQ>(B.z, j)));
-        float4 sx = *(const float4*)&sxs[(ch0 + j) * 16 + 4 * g];
+        // rows 4 g .. 4 g + 3; lanes whose rows are >= MR (no activations)
+        // read a zeroed slot
+        float4 sx = *(const float4*)&sxs[SXW == 16 || 4 * g < MR ? (ch0 + j) * SXW + 4 * g : zslot];
 #pragma unroll
         for (int q = 1; q < CPG; ++q) {
-          const float4 t = *(const float4*)&sxs[(ch0 + j - q) * 16 + 4 * g];
+          const float4 t =
+              *(const float4*)&sxs[SXW == 16 || 4 * g < MR ? (ch0 + j - q) * SXW + 4 * g : zslot];
           sx.x += t.x;
           sx.y += t.y;
           sx.z += t.z;
@@ -598,7 +611,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_stream_kernel(
 template <int MR, int NW, bool SYM, bool XF16>
 hipError_t launch_ms(const uint16_t* x, int M, int K, int KC, const uint8_t* qw, const uint16_t* sc,
                      const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
-  const size_t lds = mfma_stream_lds_bytes(MR, NW, KC);
+  const size_t lds = mfma_stream_lds_bytes(MR, NW, KC, KC < K);
   const int per_cu = lds <= 80 * 1024 ? 2 : 1;
   const int grid = std::max(1, std::min((N + 15) / 16, per_cu * num_cus()));
 #define GQ_MS_LAUNCH(GQ_)                                                                      \
@@ -652,21 +665,21 @@ hipError_t launch_all(const uint16_t* x, int M, int K, const uint8_t* qw, const 
 
 }  // namespace
 
-// The streaming matrix-core GEMV: 8 or 16 staged rows.  With 8 staged rows,
-// more than two row blocks per compute unit and x of at most 4096 columns, 4
-// waves per workgroup and two workgroups per compute unit (more row blocks in
-// flight: [28672, 4096] 25 against 31 us at M = 8); otherwise 8 waves and one
-// workgroup per compute unit ([6144, 4096] and [4096, 4096] gain 0.7 and
-// 1.2 us), with K in chunks of KC (the largest multiple of 4096 whose x fits
-// LDS: 8192 columns of 8 rows, 4096 of 16).  Chunks only with 8 staged rows:
-// with 16 the split-K kernel is faster on [4096, 14336] (24 against 30 us at
-// M = 16; 23 against 21.5 us at M = 8).  False if K or G do not fit.
+// The streaming matrix-core GEMV: 8 or 16 staged rows and 8 waves per
+// workgroup (two workgroups per compute unit when x fits 80 KiB of LDS: 8 rows
+// of 4096 columns; the launch bounds then hold each wave to 128 registers),
+// or with 8 staged rows and K = 2048 4 waves (one 512-wide item each).  K
+// runs in chunks of KC (the largest multiple of 4096 whose x fits LDS: 8192
+// columns of 8 rows, 4096 of 16); chunks only with 8 staged rows: with 16 the
+// split-K kernel is faster on [4096, 14336] (24 against 30 us at M = 16).
+// Measured at M = 8 against 4-wave workgroups: qkv 10.75 -> 10.3 us, gate_up
+// 24.8 -> 23.9 us.  False if K or G do not fit.
 static bool mfma_stream_config(int M, int64_t K, int64_t N, int* MR, int* NW, int* KC) {
+  (void)N;
   if (K % kMSItem != 0 || K > ((int64_t)1 << 24)) return false;
   *MR = M <= 8 ? 8 : 16;
-  const bool many = (N + 15) / 16 > 2 * (int64_t)num_cus();
-  if (*MR == 8 && K % 2048 == 0 && mfma_stream_lds_bytes(8, 4, K) <= 80 * 1024 &&
-      (many || K % 4096 != 0)) {
+  if (*MR == 8 && K % 4096 != 0 && K % 2048 == 0 &&
+      mfma_stream_lds_bytes(8, 4, K, false) <= 80 * 1024) {
     *NW = 4;
     *KC = (int)K;
     return true;
@@ -675,7 +688,7 @@ static bool mfma_stream_config(int M, int64_t K, int64_t N, int* MR, int* NW, in
   const int kcmax = *MR == 8 ? 8192 : 4096;
   *KC = (int)std::min<int64_t>(kcmax, (K + 4095) / 4096 * 4096);
   if (*MR == 16 && *KC < K) return false;
-  return mfma_stream_lds_bytes(*MR, 8, *KC) <= 156 * 1024;
+  return mfma_stream_lds_bytes(*MR, 8, *KC, *KC < K) <= 156 * 1024;
 }
 
 bool gemv_mfma_stream_supported(int M, int64_t K, int64_t N, int G) {
