@@ -313,3 +313,13 @@ def test_scratch_free_paths_under_graph_capture(M, K, N, G, sym):
         torch.cuda.synchronize()
         assert torch.equal(y_g, y_eager), f"replay {rep}"
         assert other.shape == (1, N)
+
+
+@pytest.mark.parametrize("M", [5, 8, 16])
+@pytest.mark.parametrize("N", [1, 15, 17])
+def test_mfma_stream_tiny_row_counts(M, N):
+    # one output row, one row short of a 16-row block, one row past it
+    K, G = 4096, 64
+    w, x = synth.small(N, K, M, seed=N * 31 + M)
+    qw, s, z = _oracle_weights(w, G, False)
+    _run(x, qw, s, z, G, False, f"[{N},{K}] M={M} asym G={G} (matrix cores, streaming)")
