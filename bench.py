@@ -52,6 +52,7 @@ GEMV_SOURCES = [os.path.join(ROOT, "w4a16_dequant_gemm_group_amd", "csrc", f)
                 for f in ("gemv.hip", "stream_util.h")]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "w4a16_gemv_stream_traffic.json")
 GEMV_KERNEL = "gemv_stream_kernel"
+GEMV_KERNEL_M1 = "gemv_stream_kernel<1,"  # the one-row instantiation (trace names)
 CALIB_BYTES = 256 << 20          # calibration copy: reads and writes this many bytes
 G = 128
 # which kernel serves each small-batch M on the four projections (sym g32)
@@ -104,7 +105,7 @@ def summarize_traffic(fetch_dir, write_dir):
         rows = [r for r in _counter_rows(d) if r["Counter_Name"] == cname]
         rows.sort(key=lambda r: int(r["Dispatch_Id"]))
         calib = [float(r["Counter_Value"]) for r in rows if "neg" in r["Kernel_Name"]]
-        gemv = [float(r["Counter_Value"]) for r in rows if GEMV_KERNEL in r["Kernel_Name"]]
+        gemv = [float(r["Counter_Value"]) for r in rows if GEMV_KERNEL_M1 in r["Kernel_Name"]]
         if not calib or not gemv or len(gemv) % len(shapes):
             raise SystemExit(f"{cname}: expected calibration and {len(shapes)}*k GEMV dispatches, "
                              f"found {len(calib)} / {len(gemv)}")
@@ -197,10 +198,13 @@ def main():
             _, xb = synth.prefill_case(nm)
             qw, s, z = W[nm]
             B.gq_w4a16_gemm(to_dev(xb), qw, s, z, G, False)
-        for nm, n, k in shapes:   # one small-batch GEMV per projection (M = 8, matrix cores)
-            qw, s, z = W[nm]
-            x8, _ = synth.activations(8, k, seed=2000 + synth.SHAPE_ORDER.index(nm))
-            B.gq_w4a16_gemv(to_dev(x8), qw, s, z, G, False)
+        # one small-batch GEMV per projection and row count: M = 2, 3, 4 run the
+        # multi-row streaming kernel, M = 8 and 16 the matrix-core kernels
+        for m in (2, 3, 4, 8, 16):
+            for nm, n, k in shapes:
+                qw, s, z = W[nm]
+                xm, _ = synth.activations(m, k, seed=2000 + 10 * m + synth.SHAPE_ORDER.index(nm))
+                B.gq_w4a16_gemv(to_dev(xm), qw, s, z, G, False)
         a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
         torch.neg(a, out=b)
