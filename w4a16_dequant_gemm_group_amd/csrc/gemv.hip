@@ -319,15 +319,35 @@ __device__ __forceinline__ void stream_compute(const StreamBuf<RPW>& B, Cursor c
     }
   }
   if (c.p == T - 1) {
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
+    if constexpr (MT == 1) {
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
-        const float v = wave_sum_to_lane63(acc[m][r]);
+        const float v = wave_sum_to_lane63(acc[0][r]);
         const int row = c.b * RPW + r;
-        if (lane == 63 && row < N)
-          y[(size_t)m * ldy + row] = XF16 ? f32_to_f16_rne(v) : f32_to_bf16_rne(v);
+        if (lane == 63 && row < N) y[row] = XF16 ? f32_to_f16_rne(v) : f32_to_bf16_rne(v);
       }
+    } else {
+      // all (m, r) sums together, four per register (padded with zeros); the
+      // last lane of each 16-lane row stores the one its row holds
+      constexpr int V = MT * RPW;
+      constexpr int VP = V <= 4 ? 4 : V <= 8 ? 8 : 16;
+      static_assert(V <= 16, "at most sixteen sums per row block");
+      float v[VP], u[VP / 4];
+#pragma unroll
+      for (int i = 0; i < VP; ++i) v[i] = i < V ? acc[i / RPW][i % RPW] : 0.f;
+      wave_sums_by_row<VP>(v, u);
+      const int q = lane >> 4;
+      const int qi = (q & 1) * 2 + (q >> 1);
+      if ((lane & 15) == 15) {
+#pragma unroll
+        for (int j = 0; j < VP / 4; ++j) {
+          const int idx = 4 * j + qi;
+          const int m = idx / RPW, row = c.b * RPW + idx % RPW;
+          if (idx < V && row < N)
+            y[(size_t)m * ldy + row] = XF16 ? f32_to_f16_rne(u[j]) : f32_to_bf16_rne(u[j]);
+        }
+      }
+    }
   }
 }
 
