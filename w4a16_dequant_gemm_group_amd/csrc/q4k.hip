@@ -228,7 +228,8 @@ struct QBuf {
   uint4 h[kQRpw], w[kQRpw];
 };
 
-__global__ __launch_bounds__(kThreads) void q4k_stream_kernel(const uint16_t* __restrict__ x, int K,
+template <int NT>
+__global__ __launch_bounds__(NT) void q4k_stream_kernel(const uint16_t* __restrict__ x, int K,
                                                               const uint8_t* __restrict__ blocks,
                                                               int N, uint16_t* __restrict__ y) {
   namespace su = stream_util;
@@ -239,7 +240,8 @@ __global__ __launch_bounds__(kThreads) void q4k_stream_kernel(const uint16_t* __
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nb = (N + kQRpw - 1) / kQRpw;
-  const int W = gridDim.x * kWaves;
+  constexpr int NW = NT / 64;  // waves per workgroup
+  const int W = gridDim.x * NW;
   const uint32_t row_bytes = (uint32_t)(K / 256) * kBlockBytes;
   const su::rsrc_t rb = su::make_rsrc(blocks, (uint32_t)N * row_bytes);
   const uint32_t hoff = (uint32_t)(lane >> 3) * kBlockBytes;
@@ -266,13 +268,13 @@ __global__ __launch_bounds__(kThreads) void q4k_stream_kernel(const uint16_t* __
   uint4 xv[kXr];
 #pragma unroll
   for (int i = 0; i < kXr; ++i) {
-    const int c = threadIdx.x + kThreads * i;
+    const int c = threadIdx.x + NT * i;
     xv[i] = make_uint4(0, 0, 0, 0);
-    if (i < T && c * 8 < K) xv[i] = *(const uint4*)(x + c * 8);
+    if (c < T * 256 && c * 8 < K) xv[i] = *(const uint4*)(x + c * 8);
   }
   QBuf buf[kQNbuf];
   float acc[kQRpw] = {0.f, 0.f};
-  int lb = (int)blockIdx.x * kWaves + wave, lt = 0;  // next item to load
+  int lb = (int)blockIdx.x * NW + wave, lt = 0;  // next item to load
   int cb = lb, ct = 0;                               // next item to compute
   auto advance = [&](int& b, int& t) {
     if (++t == T) {
@@ -286,13 +288,13 @@ __global__ __launch_bounds__(kThreads) void q4k_stream_kernel(const uint16_t* __
     __builtin_amdgcn_sched_barrier(0);  // keep the loads in item order: the loop's waits assume it
     advance(lb, lt);
   }
-  for (int c0 = 0; c0 < T * 256; c0 += kXr * kThreads) {
+  for (int c0 = 0; c0 < T * 256; c0 += kXr * NT) {
 #pragma unroll
     for (int i = 0; i < kXr; ++i) {
-      const int c = c0 + threadIdx.x + kThreads * i;
+      const int c = c0 + threadIdx.x + NT * i;
       // every load issued here is consumed here: a load left in flight on
       // some path would make the main loop wait for all loads at its head
-      if (c0 + kThreads * i < T * 256) {  // uniform over the block
+      if (c < T * 256) {  // uniform over each wave (T * 256 is a multiple of 64)
         uint4 v = xv[i];
         if (c0 > 0) {
           v = make_uint4(0, 0, 0, 0);
@@ -344,7 +346,7 @@ __global__ __launch_bounds__(kThreads) void q4k_stream_kernel(const uint16_t* __
   // Whole buffer rounds in the loop, the last 0-2 items (already loaded) after
   // it: with its only exit at the bottom, the loop head waits for exactly the
   // item it multiplies, and no item is computed twice or padded.
-  const int b0 = (int)blockIdx.x * kWaves + wave;
+  const int b0 = (int)blockIdx.x * NW + wave;
   const int items = b0 < nb ? ((nb - 1 - b0) / W + 1) * T : 0;
   const int rounds = items / kQNbuf, rest = items % kQNbuf;
   for (int it = 0; it < rounds; ++it) {
@@ -397,9 +399,17 @@ hipError_t launch_q4k_gemv(const uint16_t* x, int M, int64_t K, const uint8_t* b
     for (int64_t n0 = 0; n0 < N; n0 += cap) {
       const int nn = (int)std::min<int64_t>(cap, N - n0);
       const int nb = (nn + kQRpw - 1) / kQRpw;
-      const int grid = std::max(1, std::min((nb + kWaves - 1) / kWaves, 2 * num_cus()));
-      hipLaunchKernelGGL(q4k_stream_kernel, dim3(grid), dim3(kThreads), lds, s, x, k,
-                         blocks + n0 * row_bytes, nn, y + n0);
+      // one workgroup of 8 waves per compute unit once K spans four or more
+      // 2048-steps (x staged once per compute unit), else two of 4 waves
+      if (steps >= 4) {
+        const int grid = std::max(1, std::min((nb + 7) / 8, num_cus()));
+        hipLaunchKernelGGL(q4k_stream_kernel<512>, dim3(grid), dim3(512), lds, s, x, k,
+                           blocks + n0 * row_bytes, nn, y + n0);
+      } else {
+        const int grid = std::max(1, std::min((nb + kWaves - 1) / kWaves, 2 * num_cus()));
+        hipLaunchKernelGGL(q4k_stream_kernel<kThreads>, dim3(grid), dim3(kThreads), lds, s, x, k,
+                           blocks + n0 * row_bytes, nn, y + n0);
+      }
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
