@@ -319,7 +319,12 @@ __device__ __forceinline__ void stream_compute(const StreamBuf<RPW>& B, Cursor c
     }
   }
   if (c.p == T - 1) {
-    if constexpr (MT == 1) {
+    if constexpr (MT == 1 && RPW == 2) {
+      // both rows' sums together: row 0's in lane 31, row 1's in lane 63
+      const float v = wave_sums_pair(acc[0][0], acc[0][1]);
+      const int row = c.b * 2 + (lane >> 5);
+      if ((lane & 31) == 31 && row < N) y[row] = XF16 ? f32_to_f16_rne(v) : f32_to_bf16_rne(v);
+    } else if constexpr (MT == 1) {
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
         const float v = wave_sum_to_lane63(acc[0][r]);

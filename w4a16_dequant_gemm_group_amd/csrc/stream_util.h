@@ -152,6 +152,23 @@ __device__ __forceinline__ void wave_sums_by_row(const float (&v)[VP], float (&u
   }
 }
 
+// Sums over the 64 lanes of two values: a's lands in lane 31, b's in lane 63.
+// One permlane32_swap and add halve both, four row-local DPP adds give every
+// row its 16-lane sum, and a row_bcast:15 into rows 1 and 3 adds rows 0 and 2
+// to them (8 instructions, against 8 per value for wave_sum_to_lane63).
+__device__ __forceinline__ float wave_sums_pair(float a, float b) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a),
+                                                  __builtin_bit_cast(uint32_t, b), false, false);
+  const uint32_t lo = p[0], hi = p[1];  // bit-casting p[1] in place reads p[0]
+  float t = __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
+  t += dpp_f32<0xB1, 0xF>(t);   // quad_perm [1,0,3,2]
+  t += dpp_f32<0x4E, 0xF>(t);   // quad_perm [2,3,0,1]
+  t += dpp_f32<0x124, 0xF>(t);  // row_ror:4
+  t += dpp_f32<0x128, 0xF>(t);  // row_ror:8
+  t += dpp_f32<0x142, 0xA>(t);  // row_bcast:15 into rows 1 and 3
+  return t;
+}
+
 // Sum over the 64 lanes; the total lands in lane 63.
 __device__ __forceinline__ float wave_sum_to_lane63(float v) {
   v += dpp_f32<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
