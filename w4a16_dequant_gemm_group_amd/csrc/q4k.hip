@@ -335,12 +335,11 @@ __global__ __launch_bounds__(NT) void q4k_stream_kernel(const uint16_t* __restri
       acc[r] = fmaf(S, a, fmaf(-Mn, sx, acc[r]));
     }
     if (t == T - 1) {
-#pragma unroll
-      for (int r = 0; r < kQRpw; ++r) {
-        const float v = su::wave_sum_to_lane63(acc[r]);
-        const int row = b * kQRpw + r;
-        if (lane == 63 && row < N) y[row] = f32_to_bf16_rne(v);
-      }
+      // both rows' sums together: row 0's in lane 31, row 1's in lane 63
+      static_assert(kQRpw == 2, "the paired reduction takes two rows");
+      const float v = su::wave_sums_pair(acc[0], acc[1]);
+      const int row = b * kQRpw + (lane >> 5);
+      if ((lane & 31) == 31 && row < N) y[row] = f32_to_bf16_rne(v);
     }
   };
   // Whole buffer rounds in the loop, the last 0-2 items (already loaded) after
