@@ -42,7 +42,9 @@ R6  Packing: qweight is [N, K/2] bytes, byte j of row n holds code k=2j in
 R7  The super-block format's own quantizer (the pages give only its sizes):
     per 32-wide sub-block an unsigned 4-bit code with a zero-inclusive min,
     x^ = d*sc*q - dmin*mn, 6-bit sc/mn by round-to-nearest against fp16 d/dmin
-    taken from the block maxima / 63.
+    taken from the block maxima / 63.  A zero d or dmin is stored as +0
+    (bits 0x0000): the sub-block min is m_j = 0 - lo_j, which is +0 when lo_j
+    is 0, and a zero scale rounds to +0.
 """
 from __future__ import annotations
 
@@ -268,7 +270,7 @@ def q4k_quantize(w: np.ndarray):
     lo = np.minimum(sub.min(axis=3), 0.0)
     hi = np.maximum(sub.max(axis=3), 0.0)
     s = np.where(hi != lo, (hi - lo) / 15.0, 0.0)      # sub-block step
-    m = 0.0 - lo                                        # sub-block min (>= +0)
+    m = 0.0 - lo                                        # sub-block min, +0 (never -0) when lo = 0
     d = scale_to_f16(s.max(axis=2) / 63.0)              # fp16 scale of scales
     dmin = scale_to_f16(m.max(axis=2) / 63.0)           # fp16 min of mins
     with np.errstate(divide="ignore", invalid="ignore"):
@@ -358,6 +360,9 @@ def rel_frobenius(y, y_ref) -> float:
 
 
 def max_err_bound(x64, w_hat64) -> float:
+    """1e-2 * max|x| * max|w^| * sqrt(K) / 64: element-wise maxima over the
+    whole activation [M, K] and the whole dequantized weight; K the reduction
+    length."""
     K = x64.shape[1]
     return 1e-2 * float(np.abs(x64).max()) * float(np.abs(w_hat64).max()) * np.sqrt(K) / 64.0
 
@@ -371,15 +376,26 @@ def bf16_half_ulp(v) -> np.ndarray:
     return np.where(a > 0, 2.0 ** (e - 8), 2.0 ** -134)
 
 
-def within_parity(y, y_ref, x64, w_hat):
+def f16_half_ulp(v) -> np.ndarray:
+    """Half the spacing of binary16 values at |v|: 11 significant bits, so
+    2^(e-11) in [2^e, 2^(e+1)); the subnormal spacing 2^-24 below 2^-14."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -14.0)
+    return np.where(a > 0, 2.0 ** (e - 11), 2.0 ** -25)
+
+
+def within_parity(y, y_ref, x64, w_hat, out: str = "bf16"):
     """The matmul parity bar: relative Frobenius error <= 2e-3 and, element-wise,
-    |y - y_ref| <= 1e-2 ||x||_inf ||w^||_inf sqrt(K)/64 plus half a bf16 ulp of
-    the output (the result is stored as bf16, whose rounding alone may exceed the
-    first term when K is small).  Returns (ok, rel_f, max_excess_ratio)."""
+    |y - y_ref| <= 1e-2 ||x||_inf ||w^||_inf sqrt(K)/64 plus half an ulp of the
+    output format (``out`` = "bf16" or "f16"; the result is stored in that
+    format, whose rounding alone may exceed the first term when K is small).
+    Returns (ok, rel_f, max_excess_ratio)."""
     y = np.asarray(y, dtype=np.float64)
     y_ref = np.asarray(y_ref, dtype=np.float64)
     rel = rel_frobenius(y, y_ref)
-    allow = max_err_bound(x64, w_hat) + bf16_half_ulp(np.maximum(np.abs(y), np.abs(y_ref)))
+    half_ulp = {"bf16": bf16_half_ulp, "f16": f16_half_ulp}[out]
+    allow = max_err_bound(x64, w_hat) + half_ulp(np.maximum(np.abs(y), np.abs(y_ref)))
     ratio = float((np.abs(y - y_ref) / allow).max()) if y.size else 0.0
     return (rel <= 2e-3 and ratio <= 1.0), rel, ratio
 

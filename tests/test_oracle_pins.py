@@ -475,3 +475,111 @@ def test_group_major_ingest_preserves_the_product():
     assert np.array_equal(O.unpack_int4(qw, True)[3, 32:64], codes[1, :, 3])
     canon = O.w4a16_reference(x, qw, sc, None, g, True)
     assert np.allclose(canon, page, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# the element-wise half of the parity bar
+# ---------------------------------------------------------------------------
+
+def test_max_err_bound_closed_form():
+    """1e-2 * max|x| * max|w^| * sqrt(K) / 64 with max|x| = 2, max|w^| = 3 and
+    K = 4096 is 1e-2 * 2 * 3 * 64 / 64 = 0.06; the maxima are of absolute values
+    and K is the reduction length (the number of columns of x)."""
+    x = np.zeros((2, 4096)); x[1, 17] = -2.0; x[0, 3] = 1.5
+    w = np.zeros((5, 4096)); w[4, 100] = -3.0; w[2, 7] = 2.9
+    assert abs(O.max_err_bound(x, w) - 0.06) < 1e-15
+    # K from x's columns: a quarter of the length halves the bound
+    assert abs(O.max_err_bound(x[:, :1024], w[:, :1024]) - 0.03) < 1e-15
+
+
+def test_f16_half_ulp_closed_form():
+    # binary16 keeps 11 significant bits: spacing 2^(e-10) in [2^e, 2^(e+1)),
+    # subnormal spacing 2^-24 below 2^-14
+    for v, want in ((1.0, 2.0 ** -11), (1.99, 2.0 ** -11), (2.0, 2.0 ** -10), (10.0, 2.0 ** -8),
+                    (-0.3, 2.0 ** -13), (2.0 ** -14, 2.0 ** -25), (1e-6, 2.0 ** -25),
+                    (0.0, 2.0 ** -25)):
+        assert float(O.f16_half_ulp(np.array([v]))[0]) == want
+    rng = np.random.default_rng(4)
+    v = rng.normal(0, 10, 5000)
+    r = v.astype(np.float16).astype(np.float64)
+    assert np.all(np.abs(r - v) <= O.f16_half_ulp(v))
+
+
+def test_element_bound_rejects_what_frobenius_accepts():
+    """An error on a single output that the relative Frobenius half cannot see
+    (20000 outputs of 10) must still be rejected once it exceeds the element
+    bound 0.06 plus half an output ulp, and accepted just below it; the bound of
+    fp16 outputs uses fp16's half ulp (2^-8 at 10), bf16's uses 2^-5."""
+    x = np.zeros((1, 4096)); x[0, 9] = 2.0
+    w = np.zeros((3, 4096)); w[1, 11] = -3.0
+    ref = np.full((1, 20000), 10.0)
+    for out, half in (("bf16", 2.0 ** -5), ("f16", 2.0 ** -8)):
+        allow = 0.06 + half
+        y = ref.copy(); y[0, 123] += 1.04 * allow
+        ok, rel, ratio = O.within_parity(y, ref, x, w, out=out)
+        assert rel < 2e-3 and not ok and 1.0 < ratio < 1.05, (out, rel, ratio)
+        y = ref.copy(); y[0, 123] -= 0.96 * allow
+        ok, rel, ratio = O.within_parity(y, ref, x, w, out=out)
+        assert ok and 0.95 < ratio < 1.0, (out, rel, ratio)
+    # the Frobenius half on its own: a uniform relative error of 3e-3 fails
+    y = ref * (1 + 3e-3)
+    ok, rel, _ = O.within_parity(y, ref, x * 1e3, w, out="bf16")
+    assert not ok and abs(rel - 3e-3) < 1e-9
+
+
+# ---------------------------------------------------------------------------
+# super-block format: scale-of-mins, byte layout, signed zero
+# ---------------------------------------------------------------------------
+
+def test_q4k_dmin_is_nearest_fp16_of_max_min_over_63():
+    """dmin is the fp16 nearest to the exact max_j(0 - lo_j) / 63, as d is the
+    fp16 nearest to max_j (hi_j - lo_j) / (15 * 63)."""
+    w = synth.weights(6, 1024, seed=21)[0]
+    wf = O.bf16_to_f64(w)
+    f = O.q4k_quantize(wf)
+    sub = wf.reshape(6, 4, 8, 32)
+    checked = 0
+    for n in range(6):
+        for b in range(4):
+            m = np.array([-min(v.min(), 0.0) for v in sub[n, b]])
+            assert m.max() > 0
+            j = int(np.argmax(m))
+            want = _exact_scale(min(sub[n, b, j].min(), 0.0), 0.0, 63)
+            assert f["dmin"][n, b] == want, (n, b)
+            checked += 1
+    assert checked == 24
+
+
+def test_q4k_hand_built_block_bytes():
+    """Encode and decode of a block whose fields were chosen by hand, against
+    the literal bytes derived in the fixture (d, dmin, sc, mn at offsets 0, 2,
+    4, 10; nibbles from 16)."""
+    gd = read_golden("q4k_block_layout.txt")
+    f = {"d": np.array([[float(gd["d"])]]), "dmin": np.array([[float(gd["dmin"])]]),
+         "sc": np.array([[[int(v) for v in gd["sc"].split()]]]),
+         "mn": np.array([[[int(v) for v in gd["mn"].split()]]]),
+         "q": (np.arange(256) % 16)[None, :].astype(np.int64)}
+    want = np.array([int(v, 16) for v in gd["header_hex"].split()]
+                    + [int(v, 16) for v in gd["nibble_hex"].split()] * 16, dtype=np.uint8)
+    assert want.size == 144
+    blk = O.q4k_encode(f)
+    assert blk.shape == (1, 1, 144)
+    assert np.array_equal(blk[0, 0], want)
+    g = O.q4k_decode(want.reshape(1, 1, 144))
+    for key in ("d", "dmin", "sc", "mn", "q"):
+        assert np.array_equal(np.asarray(g[key]), np.asarray(f[key])), key
+    wh = O.q4k_dequantize_fields(g)
+    assert wh[0, 5] == float(gd["xhat_k5"]) and wh[0, 255] == float(gd["xhat_k255"])
+
+
+def test_q4k_zero_min_is_positive_zero():
+    """A block with no negative weight has every sub-block min 0 - 0 = +0, so
+    dmin is stored as +0 (0x0000) and every mn field is 0; an all-zero block
+    stores d = +0 as well."""
+    w = np.abs(O.bf16_to_f64(synth.weights(2, 512, seed=5)[0]))
+    w[1, 256:] = 0.0
+    blocks = O.q4k_encode(O.q4k_quantize(w))
+    hdr = blocks[..., 0:4].copy().view(np.uint16)       # [N, nb, 2]: d, dmin
+    assert np.all(hdr[..., 1] == 0x0000)                 # dmin = +0, not 0x8000
+    assert np.all(blocks[..., 10:16] == 0)               # mn fields
+    assert hdr[1, 1, 0] == 0x0000 and hdr[0, 0, 0] != 0
