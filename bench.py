@@ -300,7 +300,10 @@ def main():
     log(f"stream read ceiling {ceiling['GB/s']:.0f} GB/s; same-size pure reads {ceiling['per_shape_us']}")
 
     # Every launch of the step is the same streaming GEMV kernel: its algorithmic
-    # bytes per launch over its average launch duration in the timed region.
+    # bytes per launch over its average launch duration in the timed region,
+    # i.e. the event-timed region divided by its launches (gaps between the
+    # back-to-back launches of the graph included; the kernel trace of the same
+    # command gives the durations alone).
     bytes_per_launch = step_bytes / len(shapes)
     avg_launch_us = ms_per_step * 1e3 / len(shapes)
     achieved = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
@@ -309,7 +312,10 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": None if tr is None else round(tr["mean_hbm_bytes_per_launch"]),
                 "kernel": f"{GEMV_KERNEL}<1,2,NT,false,false,false> (M = 1, asym; all four projections; NT = 256 threads at K = 4096, 512 on down)",
-                "bytes_per_launch": bytes_per_launch, "avg_launch_us": round(avg_launch_us, 3),
+                "bytes_per_launch": bytes_per_launch,
+                "event_us_per_launch": round(avg_launch_us, 3),
+                "event_us_per_launch_is": "HIP-event time of the timed graph replays / launches "
+                                          "(launch gaps included)",
                 "frac_of_measured_read_ceiling": round(achieved / ceiling["GB/s"], 4),
                 # time of pure reads of the same byte counts over the time of the GEMVs
                 "frac_of_same_size_reads": round(sum(ceiling["per_shape_us"].values())
@@ -438,14 +444,19 @@ def run_extras(torch, B, synth, to_dev, dev, stream, shapes, W, X, gate, fused_s
         xd = to_dev(xb)
         qw, s, z = W[name]
         y = torch.empty((2048, n), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(B.gq_w4a16_gemm_workspace_size(2048, k, n, G), dtype=torch.uint8, device=dev)
         for _ in range(3):
-            B.gq_w4a16_gemm(xd, qw, s, z, G, False, y=y, stream=stream)
-        us = time_launches(torch, stream, lambda i: B.gq_w4a16_gemm(xd, qw, s, z, G, False, y=y, stream=stream), 10)
+            B.gq_w4a16_gemm(xd, qw, s, z, G, False, y=y, stream=stream, workspace=ws)
+        torch.cuda.synchronize()
+        # a graph of 10 launches replayed 3 times: GPU time only (an eager loop
+        # would add the host's per-call time whenever it exceeds the kernel's)
+        us = graph_time(torch, stream, lambda i: B.gq_w4a16_gemm(xd, qw, s, z, G, False, y=y,
+                                                                  workspace=ws), 10, reps=3)
         fl = 2.0 * 2048 * n * k
         gemm[name] = {"us": round(us, 2), "TFLOP/s": round(fl / (us * 1e-6) / 1e12, 1)}
         tot_flop += fl
         tot_us += us
-        del xd, y
+        del xd, y, ws
     agg = tot_flop / (tot_us * 1e-6) / 1e12
     ex["gemm_m2048"] = {"per_shape": gemm, "aggregate_TFLOPs": round(agg, 1),
                         "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS, "frac": round(agg / MFMA_BF16_PEAK_TFLOPS, 4)}
@@ -546,11 +557,19 @@ def run_extras(torch, B, synth, to_dev, dev, stream, shapes, W, X, gate, fused_s
             unf(i)
             plain(i)
         torch.cuda.synchronize()
-        t_u = float(np.median([time_launches(torch, stream, unf, 5) for _ in range(3)]))
-        t_p = float(np.median([time_launches(torch, stream, plain, 5) for _ in range(3)]))
+        try:   # graphs, as for the fused GEMM: GPU time only
+            t_u = graph_time(torch, stream, unf, 5, reps=3)
+            t_p = graph_time(torch, stream, plain, 5, reps=3)
+            how = "HIP graph"
+        except Exception as e:  # a library call that cannot be captured is timed eagerly
+            log(f"M=2048 comparator not capturable ({type(e).__name__}); timing eager launches")
+            torch.cuda.synchronize()
+            t_u = float(np.median([time_launches(torch, stream, unf, 5) for _ in range(3)]))
+            t_p = float(np.median([time_launches(torch, stream, plain, 5) for _ in range(3)]))
+            how = "eager launches"
         fl = 2.0 * 2048 * n * k
         unf_pf[name] = {"unfused_us": round(t_u, 2), "bf16_gemm_us": round(t_p, 2),
-                        "fused_us": gemm[name]["us"],
+                        "fused_us": gemm[name]["us"], "timing": how,
                         "bf16_gemm_TFLOP/s": round(fl / (t_p * 1e-6) / 1e12, 1)}
         del xd, wb1, yp
     ex["unfused_and_bf16_m2048"] = unf_pf

@@ -21,14 +21,12 @@
  *
  * Conventions for every entry point
  *   - Pointers are device pointers (HIP global memory) unless marked "host".
- *     The caller owns every buffer.  libgq keeps a per-device architecture
- *     check and allocates nothing, with two exceptions, both per (device,
- *     stream), grown on demand, held until the process ends and never handed
- *     out while the stream is being captured (the call then runs unsplit
- *     kernels): gq_w4a16_gemv on its split-K matrix-core path (below) keeps split-K
- *     partial sums (gq_w4a16_gemv_ws takes them from the caller instead), and
- *     gq_w4a16_gemm keeps split-K partial sums and per-tile counters when its
- *     output tiles fill at most half of the GPU.
+ *     The caller owns every buffer.  libgq allocates nothing, never
+ *     synchronizes and keeps no state beyond a per-device architecture and
+ *     compute-unit check and a per-process launch-id counter.  Scratch that a
+ *     faster kernel can use (split-K partial sums) is passed in by the caller
+ *     through the *_ws entry points, sized by the *_workspace_size queries;
+ *     the entry points without a workspace run kernels that need none.
  *   - All matrices are dense, row-major, contiguous.  W is [N, K] = out x in,
  *     so Y = X W^T [P1 sec.2]; groups run along K (the reduction axis).
  *   - fp16 / bf16 values are passed as uint16_t bit patterns.
@@ -38,7 +36,10 @@
  *     enqueued asynchronously and the call returns GQ_OK; kernel faults surface
  *     on the stream as usual.  A failed launch returns GQ_ERR_HIP and leaves the
  *     outputs undefined.
- *   - Calls are thread-safe; calls on one stream run in order.
+ *   - Calls are thread-safe; calls on one stream run in order.  A workspace
+ *     belongs to one call at a time: calls whose kernels may overlap (on
+ *     different streams, or replayed graphs on different streams) must not
+ *     share one.
  *   - Only gfx950 devices are accepted (GQ_ERR_UNSUPPORTED otherwise).
  *
  * Storage contract (the readings of the pages used throughout)
@@ -156,30 +157,30 @@ gq_status gq_w4a16_gemv(const uint16_t* x, int64_t M, int64_t K, const uint8_t* 
                         const uint16_t* scales, const uint16_t* zeros, int64_t N, gq_qparams p,
                         uint16_t* y, void* stream);
 
-/* Scratch (bytes) that gq_w4a16_gemv_ws needs for these arguments, 0 when the
- * call runs without any.  1 <= M <= 4 runs a streaming kernel that needs none
+/* Scratch (bytes) that gq_w4a16_gemv_ws can use for these arguments; 0 when no
+ * kernel for them would use any.  1 <= M <= 4 runs a streaming kernel that needs none
  * while x fits its LDS stage (K <= 26624, 34816, 22528, 16384 for M = 1, 2,
  * 3, 4).  5 <= M <= 16 (and M = 4 beyond that K) runs a matrix-core kernel
- * that needs none either when the group size is 32,
- * 64, 128, 256 or a multiple of 512 and K is a multiple of 512: any such K
- * for M <= 8 (x staged in chunks of up to 8192 columns), K <= 4096 for M > 8.
- * Otherwise, with 4 <= M <= 16, group_size 32, 64 or a multiple of 128
- * and K % 256 == 0, the GEMV runs on the matrix cores split along K into
- * 1024-wide slices and keeps fp32 partial sums per slice:
- * ceil(K / 1024) * M * N * 4 bytes.  Errors: those of gq_w4a16_gemv's argument
- * checks; INVALID_ARG for a NULL `bytes`. */
+ * that needs none either when the group size is 32, 64, 128, 256 or a
+ * multiple of 512 and K is a multiple of 512: any such K for M <= 8 (x staged
+ * in chunks of up to 8192 columns), K <= 4096 for M > 8.  Otherwise, with
+ * 4 <= M <= 16, group_size 32, 64 or a multiple of 128 and K % 256 == 0, a
+ * workspace lets the GEMV run on the matrix cores split along K into
+ * 1024-wide slices with fp32 partial sums per slice: ceil(K / 1024) * M * N * 4
+ * bytes (without one it runs a slower per-row dot-product kernel).  The same
+ * size serves gq_w4a16_gemv_f16_ws.  Host only.  Errors: INVALID_ARG (M
+ * outside 0..16, shapes, group_size, a NULL `bytes`), UNSUPPORTED (bits != 4). */
 gq_status gq_w4a16_gemv_workspace_size(int64_t M, int64_t K, int64_t N, gq_qparams p,
                                        size_t* bytes);
 
-/* gq_w4a16_gemv with caller-provided scratch, for callers that manage device
- * memory themselves (e.g. under stream capture).  workspace: device memory of
- * at least gq_w4a16_gemv_workspace_size() bytes, 16-byte aligned (NULL allowed
- * when that size is 0); it is written by this call's kernels on `stream` and
- * must not be touched by other work until they complete.  The plain
- * gq_w4a16_gemv keeps such scratch per (device, stream) inside the library and,
- * while its stream is being captured and none is available, runs the
- * dot-product kernel instead.  Errors: those of gq_w4a16_gemv, and
- * INVALID_ARG when a needed workspace is NULL or smaller than required. */
+/* gq_w4a16_gemv with caller-provided scratch (also usable under stream
+ * capture: the call allocates nothing).  workspace: device memory of at least
+ * gq_w4a16_gemv_workspace_size() bytes, 16-byte aligned (NULL allowed when
+ * that size is 0); this call's kernels on `stream` write it, and nothing else
+ * may use it until they complete.  Same result bits as gq_w4a16_gemv up to the
+ * summation order of the kernel that runs.  Errors: those of gq_w4a16_gemv,
+ * and INVALID_ARG / MISALIGNED for a needed workspace that is NULL, smaller
+ * than required or not 16-byte aligned. */
 gq_status gq_w4a16_gemv_ws(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
                            const uint16_t* scales, const uint16_t* zeros, int64_t N,
                            gq_qparams p, uint16_t* y, void* workspace, size_t workspace_bytes,
@@ -190,33 +191,69 @@ gq_status gq_w4a16_gemv_ws(const uint16_t* x, int64_t M, int64_t K, const uint8_
  * FLOPs; prefill is compute-bound)].  Same arithmetic, arguments, layout and
  * errors as gq_w4a16_gemv except the M range; additionally UNSUPPORTED for
  * K > 2^22.  The dequantized weight enters the bf16 MFMA as the exact integer
- * q - z and the group scale is applied in fp32, so no weight is rounded. */
+ * q - z and the group scale is applied in fp32, so no weight is rounded.
+ * Without a workspace every output tile is computed by one workgroup. */
 gq_status gq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
                         const uint16_t* scales, const uint16_t* zeros, int64_t N, gq_qparams p,
                         uint16_t* y, void* stream);
 
+/* Scratch (bytes) that gq_w4a16_gemm_ws can use: when the 256 x 256 output
+ * tiles of the last round fill at most half of the GPU's compute units (all
+ * tiles when there are at most half as many tiles as compute units), each of
+ * those tiles is split along K over two workgroups (each half keeps whole
+ * groups and at least two of them), which hand fp32 partial sums over through
+ * the workspace: per split tile 16 bytes of handshake words plus a 256 x 256
+ * fp32 tile (262144 bytes), the words first and padded to 256 bytes.  0 when
+ * nothing would be split (and for K % 64 != 0 or group sizes other than 64,
+ * 128 and multiples of 256).  Queries the current device's compute-unit count
+ * when a device is present (256 otherwise).  The same size serves
+ * gq_w4a16_gemm_f16_ws.  Errors: INVALID_ARG (shapes, group_size, a NULL
+ * `bytes`), UNSUPPORTED (bits != 4, K > 2^22). */
+gq_status gq_w4a16_gemm_workspace_size(int64_t M, int64_t K, int64_t N, gq_qparams p,
+                                       size_t* bytes);
+
+/* gq_w4a16_gemm with caller-provided scratch for the split tiles above.  The
+ * workspace needs no initial content (the two workgroups of a split tile tell
+ * this call's handshake words from stale ones by a per-call 64-bit id, and the
+ * second clears them); it must not be used by other work until this call's
+ * kernels complete.  The sum of a split tile does not depend on which half
+ * finishes first.  Should a tile's second half wait for the first beyond a
+ * bound (about a second; only a lost workgroup could cause it), that tile is
+ * written as NaN rather than left wrong.  Errors: those of gq_w4a16_gemm, and
+ * INVALID_ARG / MISALIGNED for a needed workspace that is NULL, smaller than
+ * gq_w4a16_gemm_workspace_size() or not 16-byte aligned. */
+gq_status gq_w4a16_gemm_ws(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                           const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                           gq_qparams p, uint16_t* y, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* The fused matmuls with fp16 activations and fp16 output [P1 sec.2: the
  * fused kernel multiplies BF16/FP16 activations]: the same product as
  * gq_w4a16_gemv / gq_w4a16_gemm, x [M, K] fp16 and y [M, N] fp16 (rounded to
- * nearest even; overflow gives +-inf), fp32 accumulation.  Supported shapes:
- * gq_w4a16_gemv_f16 wherever gq_w4a16_gemv needs no scratch (M = 1..4 with
- * K up to 26624, 34816, 22528, 16384; M = 5..16 with K % 512 == 0, group size
- * 32, 64, 128, 256 or a multiple of 512, and K <= 4096 when M > 8);
- * gq_w4a16_gemm_f16 for K % 64 == 0 and group_size 64, 128 or a multiple of
- * 256.  Other shapes return UNSUPPORTED.  Errors otherwise as the bf16 entry
- * points. */
+ * nearest even; overflow gives +-inf), fp32 accumulation, with the same
+ * shapes, kernels (fp16 MFMA and fp16 dot products, the nibble taken as the
+ * exact fp16 1024 + q), workspaces and errors as the bf16 entry points. */
 gq_status gq_w4a16_gemv_f16(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
                             const uint16_t* scales, const uint16_t* zeros, int64_t N,
                             gq_qparams p, uint16_t* y, void* stream);
+gq_status gq_w4a16_gemv_f16_ws(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                               const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                               gq_qparams p, uint16_t* y, void* workspace, size_t workspace_bytes,
+                               void* stream);
 gq_status gq_w4a16_gemm_f16(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
                             const uint16_t* scales, const uint16_t* zeros, int64_t N,
                             gq_qparams p, uint16_t* y, void* stream);
+gq_status gq_w4a16_gemm_f16_ws(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                               const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                               gq_qparams p, uint16_t* y, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /* Nested 4-bit super-block format [P2 "工作原理" figure, middle panel: 256
  * weights = 8 sub-blocks of 32, 6-bit scale and 6-bit min per sub-block, fp16
  * scale-of-scales d and min-of-mins dmin per super-block, 4.5 bits/weight].
  * Per sub-block j: lo = min(min,0), hi = max(max,0), s_j = (hi-lo)/15 (0 if
- * equal), m_j = -lo; d = fp16(max_j s_j / 63), dmin = fp16(max_j m_j / 63);
+ * equal), m_j = 0 - lo (+0 when lo = 0); d = fp16(max_j s_j / 63),
+ * dmin = fp16(max_j m_j / 63), a zero d or dmin stored as +0 (0x0000);
  * sc_j = clamp(round(s_j/d), 0, 63), mn_j = clamp(round(m_j/dmin), 0, 63)
  * (0 when d or dmin is 0); q = clamp(round((x + dmin mn_j)/(d sc_j)), 0, 15)
  * (0 when d sc_j = 0); x^ = d sc_j q - dmin mn_j.  All in binary64.

@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 15
+    assert len(names) == 19
     assert set(names) == set(B.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -134,6 +134,7 @@ def test_gemv_workspace_size_and_validation(lib):
     assert B.gq_w4a16_gemv_workspace_size(1, 4096, 4096, 128) == 0
     assert B.gq_w4a16_gemv_workspace_size(8, 6528, 203, 128) == 0   # K % 256 != 0
     assert B.gq_w4a16_gemv_workspace_size(8, 6528, 203, 96) == 0    # G outside 32, 64, 128k
+    assert B.gq_w4a16_gemv_workspace_size(0, 4352, 4096, 128) == 0
     nbytes = ctypes.c_size_t()
     assert lib.gq_w4a16_gemv_workspace_size(17, 4096, 64, q(), ctypes.byref(nbytes)) == B.GQ_ERR_INVALID_ARG
     assert lib.gq_w4a16_gemv_workspace_size(8, 4096, 64, q(g=48), ctypes.byref(nbytes)) == B.GQ_ERR_INVALID_ARG
@@ -187,15 +188,90 @@ def test_ingest_validation(lib):
 
 def test_f16_entry_point_validation(lib):
     L = lib
-    args = (FAKE, 1, 4096, FAKE, FAKE, FAKE, 4096)
-    # only M = 1 for the GEMV, only the 256x256 kernel's shapes for the GEMM
-    # fp16 GEMV: shapes of the split-K matrix-core path (no fp16 form) are UNSUPPORTED
-    assert L.gq_w4a16_gemv_f16(FAKE, 16, 14336, FAKE, FAKE, FAKE, 4096, q(), FAKE, None) == B.GQ_ERR_UNSUPPORTED
-    assert L.gq_w4a16_gemv_f16(FAKE, 9, 4352, FAKE, FAKE, FAKE, 4096, q(), FAKE, None) == B.GQ_ERR_UNSUPPORTED
+    # the fp16 entry points validate like the bf16 ones (every shape is supported)
     assert L.gq_w4a16_gemv_f16(FAKE, 17, 4096, FAKE, FAKE, FAKE, 4096, q(), FAKE, None) == B.GQ_ERR_INVALID_ARG
-    assert L.gq_w4a16_gemv_f16(FAKE, 1, 28672, FAKE, FAKE, FAKE, 64, q(), FAKE, None) == B.GQ_ERR_UNSUPPORTED
-    assert L.gq_w4a16_gemm_f16(FAKE, 64, 4096, FAKE, FAKE, FAKE, 4096, q(g=32), FAKE, None) == B.GQ_ERR_UNSUPPORTED
-    assert L.gq_w4a16_gemm_f16(FAKE, 64, 4128, FAKE, FAKE, FAKE, 4096, q(g=96), FAKE, None) == B.GQ_ERR_UNSUPPORTED
+    assert L.gq_w4a16_gemv_f16(FAKE_MIS, 1, 4096, FAKE, FAKE, FAKE, 64, q(), FAKE, None) == B.GQ_ERR_MISALIGNED
     assert L.gq_w4a16_gemm_f16(FAKE_MIS, 64, 4096, FAKE, FAKE, FAKE, 4096, q(), FAKE, None) == B.GQ_ERR_MISALIGNED
     assert L.gq_w4a16_gemm_f16(FAKE, 64, 4096, FAKE, FAKE, None, 4096, q(), FAKE, None) == B.GQ_ERR_INVALID_ARG
-    del args
+    assert L.gq_w4a16_gemm_f16(FAKE, 64, 4096, FAKE, FAKE, FAKE, 4096, q(bits=8), FAKE, None) == B.GQ_ERR_UNSUPPORTED
+    need = B.gq_w4a16_gemv_workspace_size(16, 14336, 4096, 128)
+    assert need > 0
+    args = (FAKE, 16, 14336, FAKE, FAKE, FAKE, 4096, q(), FAKE)
+    assert L.gq_w4a16_gemv_f16_ws(*args, None, need, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_w4a16_gemv_f16_ws(*args, FAKE_MIS, need, None) == B.GQ_ERR_MISALIGNED
+
+
+def test_gemm_workspace_size_and_validation(lib):
+    """The split covers the last round of 256 x 256 tiles when it fills at most
+    half of the compute units (256 when no device is present): 16 bytes of
+    handshake words per split tile (padded to 256) plus a 256 x 256 fp32 tile."""
+    def ws(M, K, N, G=128, sym=False):
+        return B.gq_w4a16_gemm_workspace_size(M, K, N, G, sym)
+    tile = 256 * 256 * 4
+
+    def split(t):  # handshake words padded to 256 bytes, then the partial tiles
+        return -(-16 * t // 256) * 256 + t * tile
+    assert ws(2048, 4096, 4096) == split(128) == 2048 + 128 * tile   # o: 128 tiles, all split
+    assert ws(2048, 14336, 4096) == split(128)                      # down
+    assert ws(2048, 4096, 6144) == 0                                # qkv: 192 tiles > 128
+    assert ws(2048, 4096, 28672) == split(128)                      # gate_up: 896 = 3 x 256 + 128
+    assert ws(512, 2048, 512) == split(4) == 256 + 4 * tile
+    assert ws(256, 256, 256) == 0                            # halves too short to split
+    assert ws(2048, 4096, 4096, 32) == 0                     # group 32: the generic kernel
+    assert ws(300, 4128, 200, 96, True) == 0                 # K % 64 == 32
+    assert ws(0, 4096, 4096) == 0
+    nbytes = ctypes.c_size_t()
+    assert lib.gq_w4a16_gemm_workspace_size(64, 4096, 64, q(g=48), ctypes.byref(nbytes)) == B.GQ_ERR_INVALID_ARG
+    assert lib.gq_w4a16_gemm_workspace_size(64, 4096, 64, q(), None) == B.GQ_ERR_INVALID_ARG
+    assert lib.gq_w4a16_gemm_workspace_size(64, 1 << 23, 64, q(), ctypes.byref(nbytes)) == B.GQ_ERR_UNSUPPORTED
+    need = ws(2048, 4096, 4096)
+    args = (FAKE, 2048, 4096, FAKE, FAKE, FAKE, 4096, q(), FAKE)
+    for fn in (lib.gq_w4a16_gemm_ws, lib.gq_w4a16_gemm_f16_ws):
+        assert fn(*args, None, need, None) == B.GQ_ERR_INVALID_ARG
+        assert fn(*args, FAKE, need - 16, None) == B.GQ_ERR_INVALID_ARG
+        assert fn(*args, FAKE_MIS, need, None) == B.GQ_ERR_MISALIGNED
+
+
+def test_binding_checks_tensors_before_any_call():
+    """The binding rejects wrong shapes, dtypes and devices of inputs and of
+    caller-supplied outputs before it calls the library (CPU tensors here: the
+    shape and dtype checks come first, the device check last)."""
+    import torch
+    N, K, G = 64, 512, 128
+    x = torch.zeros((2, K), dtype=torch.bfloat16)
+    qw = torch.zeros((N, K // 2), dtype=torch.uint8)
+    sc = torch.zeros((N, K // G), dtype=torch.float16)
+    zr = torch.zeros((N, K // G), dtype=torch.float16)
+    cases = [
+        (dict(y=torch.zeros((2, N - 1), dtype=torch.bfloat16)), ValueError, "y has shape"),
+        (dict(y=torch.zeros((2, N), dtype=torch.float16)), TypeError, "y: dtype"),
+        (dict(scales=torch.zeros((N, K // G - 1), dtype=torch.float16)), ValueError, "scales has shape"),
+        (dict(zeros=torch.zeros((N + 1, K // G), dtype=torch.float16)), ValueError, "zeros has shape"),
+        (dict(zeros=None), ValueError, "need zeros"),
+        (dict(qweight=torch.zeros((N, K // 4), dtype=torch.uint8)), ValueError, "does not match K"),
+        (dict(x=torch.zeros((17, K), dtype=torch.bfloat16)), ValueError, "M <= 16"),
+        (dict(group_size=96), ValueError, "group_size"),
+        (dict(workspace=torch.zeros(16, dtype=torch.int32)), TypeError, "workspace: dtype"),
+        (dict(), ValueError, "must be a GPU tensor"),
+    ]
+    for over, exc, msg in cases:
+        a = dict(x=x, qweight=qw, scales=sc, zeros=zr, group_size=G, y=None, workspace=None)
+        a.update(over)
+        with pytest.raises(exc, match=msg):
+            B.gq_w4a16_gemv(a["x"], a["qweight"], a["scales"], a["zeros"], a["group_size"], False,
+                            y=a["y"], workspace=a["workspace"])
+    with pytest.raises(ValueError, match="y has shape"):
+        B.gq_w4a16_gemm(x, qw, sc, zr, G, False, y=torch.zeros((3, N), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="blocks has shape"):
+        B.gq_q4k_gemv(x, torch.zeros((N, 1, 144), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="y has shape"):
+        B.gq_q4k_gemv(x, torch.zeros((N, 2, 144), dtype=torch.uint8), y=torch.zeros((2, 7), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="out has shape"):
+        B.gq_dequantize(qw, sc, zr, G, False, out=torch.zeros((N, K - 2), dtype=torch.float32))
+    with pytest.raises(ValueError, match="codes has shape"):
+        B.gq_quantize_groups(torch.zeros((N, K), dtype=torch.bfloat16), 4, G, False,
+                             codes=torch.zeros((N, K - 1), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="qweight has shape"):
+        B.gq_pack_int4(torch.zeros((N, K), dtype=torch.uint8), qweight=torch.zeros((N, K), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="blocks has shape"):
+        B.gq_q4k_quantize(torch.zeros((N, K), dtype=torch.float32), blocks=torch.zeros((N, 3, 144), dtype=torch.uint8))

@@ -1,7 +1,8 @@
 """GPU parity of the fused matmuls with fp16 activations and fp16 output
-(gq_w4a16_gemv_f16 at M = 1, gq_w4a16_gemm_f16) against the oracle's float64
-group-by-group product of the same fp16 activations and exact dequantized
-weight, to the matmul parity bar."""
+(gq_w4a16_gemv_f16 / _ws, gq_w4a16_gemm_f16 / _ws) against the oracle's
+float64 group-by-group product of the same fp16 activations and exact
+dequantized weight, to the matmul parity bar with the output's rounding taken
+as half an fp16 ulp."""
 import numpy as np
 import pytest
 import torch
@@ -30,8 +31,9 @@ def _check(y, x_bits, qw, s, z, G, sym, what):
     wh = O.dequantize_packed(qw, s, z, G, sym)
     ref = O.matmul_groupwise(x64, wh, G)
     yv = O.f16_to_f64(y.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
-    ok, rel, ratio = O.within_parity(yv, ref, x64, wh)
-    announce(f"{what}: relF={rel:.3e} max/allowed={ratio:.3f}")
+    assert np.all(np.isfinite(yv)), what
+    ok, rel, ratio = O.within_parity(yv, ref, x64, wh, out="f16")
+    announce(f"{what}: relF={rel:.3e} max/allowed={ratio:.3f} (fp16 half-ulp bar)")
     assert ok, (what, rel, ratio)
 
 
@@ -78,17 +80,35 @@ def test_gemm_f16(M, N, K, G, sym):
     _check(y, x, qw, s, None if sym else z, G, sym, f"gemm f16 M={M} [{N},{K}] G={G} sym={sym}")
 
 
-def test_f16_unsupported_shapes_raise():
-    # the split-K matrix-core GEMV has no fp16 form: 16 rows at K = 14336, or
-    # K not a multiple of 512, return UNSUPPORTED
-    for M, K in ((16, 14336), (9, 4352)):
-        qw, s, z = _weights(64, K, 128, False, seed=M)
-        x, _ = synth.activations_f16(M, K, seed=3)
-        with pytest.raises(B.GqError) as e:
-            B.gq_w4a16_gemv_f16(_f16_dev(x), torch.from_numpy(qw).to(device()), _f16_dev(s),
-                                _f16_dev(z), 128, False)
-        assert e.value.status == B.GQ_ERR_UNSUPPORTED
-    qw, s, z = _weights(64, 4096, 32, False, seed=1)
-    x, _ = synth.activations_f16(64, 4096, seed=2)
-    with pytest.raises(RuntimeError):   # G = 32 stays on the bf16-only GEMM kernel
-        B.gq_w4a16_gemm_f16(_f16_dev(x), torch.from_numpy(qw).to(device()), _f16_dev(s), _f16_dev(z), 32, False)
+@pytest.mark.parametrize("M,K,G,ws", [
+    (16, 14336, 128, True),     # split-K matrix-core kernel (workspace), 16 rows
+    (9, 4352, 128, True),       # K not a multiple of 512
+    (16, 14336, 32, True),      # group 32 through the split kernel
+    (9, 4352, 128, False),      # no workspace: the per-row dot-product kernel
+    (6, 4160, 64, False),
+])
+def test_gemv_f16_split_and_dot_product_shapes(M, K, G, ws):
+    qw, s, z = _weights(203, K, G, False, seed=M + K)
+    x, _ = synth.activations_f16(M, K, seed=K - M, n_outlier_channels=2)
+    args = (_f16_dev(x), torch.from_numpy(qw).to(device()), _f16_dev(s), _f16_dev(z), G, False)
+    need = B.gq_w4a16_gemv_workspace_size(M, K, 203, G)
+    if ws:
+        assert need > 0
+        y = B.gq_w4a16_gemv_f16(*args)
+    else:
+        y = B.gq_w4a16_plain("gq_w4a16_gemv_f16", *args)
+    torch.cuda.synchronize()
+    _check(y, x, qw, s, z, G, False, f"gemv f16 M={M} [203,{K}] G={G} workspace={ws and need > 0}")
+
+
+@pytest.mark.parametrize("M,N,K,G,sym", [
+    (300, 260, 4096, 32, False),   # group 32: the generic kernel
+    (130, 200, 4128, 96, True),    # K % 64 == 32, group 96
+])
+def test_gemm_f16_generic_kernel(M, N, K, G, sym):
+    qw, s, z = _weights(N, K, G, sym, seed=M + K)
+    x, _ = synth.activations_f16(M, K, seed=M, n_outlier_channels=4)
+    y = B.gq_w4a16_gemm_f16(_f16_dev(x), torch.from_numpy(qw).to(device()), _f16_dev(s),
+                            None if sym else _f16_dev(z), G, sym)
+    torch.cuda.synchronize()
+    _check(y, x, qw, s, None if sym else z, G, sym, f"gemm f16 generic M={M} [{N},{K}] G={G}")

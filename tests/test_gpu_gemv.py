@@ -147,21 +147,37 @@ def test_group_equals_k_and_outlier_blowup():
     assert errs[512] > 1.5 * errs[128]
 
 
+def full_rows_parity(y_bits, w, x, qw_dev, G, sym, what, chunk=4096):
+    """Every output row against the oracle: the weight is quantized by the
+    oracle in row chunks (bytes compared with the GPU's packed weight), the
+    float64 product computed chunk by chunk, and the parity bar applied to the
+    whole output with the whole dequantized weight's max |w^|."""
+    N = w.shape[0]
+    ref = np.empty((x.shape[0], N))
+    wmax = 0.0
+    qw_all = qw_dev.cpu().numpy()
+    for r0 in range(0, N, chunk):
+        r1 = min(N, r0 + chunk)
+        qw_ref, s_ref, z_ref = _oracle_weights(w[r0:r1], G, sym)
+        assert np.array_equal(qw_all[r0:r1], qw_ref), (what, r0)
+        wh = O.dequantize_packed(qw_ref, s_ref, z_ref, G, sym)
+        wmax = max(wmax, float(np.abs(wh).max()))
+        ref[:, r0:r1] = O.matmul_groupwise(O.bf16_to_f64(x), wh, G)
+    assert_parity(y_bits, ref, O.bf16_to_f64(x), np.array([[wmax]]), what)
+
+
 @pytest.mark.parametrize("name", synth.SHAPE_ORDER)
 def test_decode_shapes_full_size(name):
-    """Llama-3-8B decode GEMV at full size (M=1, asym g128), sampled rows."""
+    """Llama-3-8B decode GEMV at full size (M=1, asym g128), in the bench's
+    launch configuration: every output row against the oracle."""
     w, x = synth.decode_case(name)
-    rows = np.sort(np.random.default_rng(3).choice(w.shape[0], 384, replace=False))
-    wd = bf16_dev(w)
-    codes, scales, zeros = B.gq_quantize_groups(wd, 4, 128, False)
+    announce(f"decode {name} {w.shape} M=1, all rows")
+    codes, scales, zeros = B.gq_quantize_groups(bf16_dev(w), 4, 128, False)
     qw = B.gq_pack_int4(codes)
+    del codes
     y = B.gq_w4a16_gemv(bf16_dev(x), qw, scales, zeros, 128, False)
     torch.cuda.synchronize()
-    qw_ref, s_ref, z_ref = _oracle_weights(w[rows], 128, False)
-    assert np.array_equal(qw.cpu().numpy()[rows], qw_ref)
-    ref = O.w4a16_reference(x, qw_ref, s_ref, z_ref, 128, False)
-    wh = O.dequantize_packed(qw_ref, s_ref, z_ref, 128, False)
-    assert_parity(bits16(y)[:, rows], ref, O.bf16_to_f64(x), wh, f"{name} {w.shape} M=1 full, sampled")
+    full_rows_parity(bits16(y), w, x, qw, 128, False, f"{name} {w.shape} M=1 full, all rows")
 
 
 @pytest.mark.parametrize("name,M", [("down", 2), ("down", 4), ("down", 8), ("down", 16),
@@ -208,57 +224,60 @@ def test_misaligned_pointer_rejected():
     assert e.value.status == B.GQ_ERR_MISALIGNED
 
 
-def test_slice_reduction_counters_reused():
-    """With library scratch and a grid of at most two rounds, the last
-    workgroup of each 64-row group adds the K slices (per-group counters reset
-    after use); larger grids and a caller's workspace use a second kernel.
-    Calls of falling and rising N and M on one stream must match the workspace
-    path bit for bit, and the oracle on sampled rows."""
+def test_split_slices_and_plain_entry_point():
+    """Shapes that only the split-K matrix-core kernel takes fast: with a
+    workspace (the binding's default) repeated calls of falling and rising N
+    and M agree bit for bit; gq_w4a16_gemv without a workspace runs the per-row
+    dot-product kernel.  Both meet the oracle on sampled rows."""
     K, G = 4352, 128  # not a multiple of 512: the split-K matrix-core path
     for M, N, seed in ((8, 3000, 90), (5, 64, 91), (16, 1000, 92), (8, 20000, 94), (8, 3000, 93)):
-        announce(f"small-batch slice reduction M={M} N={N} K={K}")
+        announce(f"small-batch split slices M={M} N={N} K={K}")
         w, x = synth.small(N, K, M, seed=seed)
         codes, sd, zd = B.gq_quantize_groups(bf16_dev(w), 4, G, False)
         qd = B.gq_pack_int4(codes)
         xd = bf16_dev(x)
-        y_lib = B.gq_w4a16_gemv(xd, qd, sd, zd, G, False)
-        y_lib2 = B.gq_w4a16_gemv(xd, qd, sd, zd, G, False)
-        ws = torch.empty(B.gq_w4a16_gemv_workspace_size(M, K, N, G, False), dtype=torch.uint8,
-                         device=xd.device)
-        y_ws = B.gq_w4a16_gemv(xd, qd, sd, zd, G, False, workspace=ws)
+        assert B.gq_w4a16_gemv_workspace_size(M, K, N, G, False) > 0
+        y_ws = B.gq_w4a16_gemv(xd, qd, sd, zd, G, False)
+        y_ws2 = B.gq_w4a16_gemv(xd, qd, sd, zd, G, False)
+        y_plain = B.gq_w4a16_plain("gq_w4a16_gemv", xd, qd, sd, zd, G, False)
         torch.cuda.synchronize()
-        assert torch.equal(y_lib, y_ws) and torch.equal(y_lib, y_lib2)
+        assert torch.equal(y_ws, y_ws2)
         rows = np.sort(np.random.default_rng(seed).choice(N, min(N, 256), replace=False))
         qw, s, z = _oracle_weights(w[rows], G, False)
         assert np.array_equal(qd.cpu().numpy()[rows], qw)
         ref = O.w4a16_reference(x, qw, s, z, G, False)
         wh = O.dequantize_packed(qw, s, z, G, False)
-        assert_parity(bits16(y_lib)[:, rows], ref, O.bf16_to_f64(x), wh,
-                      f"[{N},{K}] M={M} slice reduction, sampled")
+        assert_parity(bits16(y_ws)[:, rows], ref, O.bf16_to_f64(x), wh,
+                      f"[{N},{K}] M={M} split slices, sampled")
+        assert_parity(bits16(y_plain)[:, rows], ref, O.bf16_to_f64(x), wh,
+                      f"[{N},{K}] M={M} no workspace (dot products), sampled")
 
 
 def test_workspace_entry_point_and_graph_replays():
-    # gq_w4a16_gemv_ws (caller scratch) and gq_w4a16_gemv (library scratch) run
-    # the same kernels: identical bits.  Captured into a graph, the call gets its
-    # scratch from torch's allocator and every replay must reproduce the eager
-    # result, with other eager work on the stream between replays.
-    # (K = 4352, not a multiple of 512, keeps the call on the split-K matrix-core path)
+    # gq_w4a16_gemv_ws with a caller's buffer and with one the binding takes
+    # from torch run the same kernels: identical bits.  Captured into a graph,
+    # the call gets its scratch from the graph's pool and every replay must
+    # reproduce the eager result, with other eager work on the stream between
+    # replays.  (K = 4352, not a multiple of 512, keeps the call on the split-K
+    # matrix-core path.)
     M, K, N, G = 12, 4352, 1000, 32
     w, x = synth.small(N, K, M, seed=77)
     qw, s, _ = _oracle_weights(w, G, True)
     xd, qd, sd = bf16_dev(x), u8_dev(qw), f16_dev(s)
     need = B.gq_w4a16_gemv_workspace_size(M, K, N, G, True)
     assert need == 5 * M * N * 4
-    y_lib = B.gq_w4a16_gemv(xd, qd, sd, None, G, True)
-    ws = torch.zeros(need + 64, dtype=torch.uint8, device=xd.device)
+    y_auto = B.gq_w4a16_gemv(xd, qd, sd, None, G, True)
+    ws = torch.full((need + 64,), 0xA5, dtype=torch.uint8, device=xd.device)
     y_ws = B.gq_w4a16_gemv(xd, qd, sd, None, G, True, workspace=ws)
     torch.cuda.synchronize()
-    assert torch.equal(y_lib, y_ws)
+    assert torch.equal(y_auto, y_ws)
     ref = O.w4a16_reference(x, qw, s, None, G, True)
     wh = O.dequantize_packed(qw, s, None, G, True)
     assert_parity(bits16(y_ws), ref, O.bf16_to_f64(x), wh, f"[{N},{K}] M={M} sym g32 via workspace")
+    with pytest.raises(ValueError):
+        B.gq_w4a16_gemv(xd, qd, sd, None, G, True, workspace=ws[:need - 16])
 
-    y_g = torch.empty_like(y_lib)
+    y_g = torch.empty_like(y_auto)
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
@@ -273,7 +292,7 @@ def test_workspace_entry_point_and_graph_replays():
         g.replay()
         other = B.gq_w4a16_gemv(xd[:5], qd, sd, None, G, True)  # eager work between replays
         torch.cuda.synchronize()
-        assert torch.equal(y_g, y_lib), f"replay {rep}"
+        assert torch.equal(y_g, y_auto), f"replay {rep}"
         assert other.shape == (5, N)
 
 

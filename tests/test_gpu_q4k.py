@@ -56,13 +56,23 @@ def test_gemv_small(M, N, K):
 
 @pytest.mark.parametrize("name", ["down", "gate_up"])
 def test_full_size(name):
+    """Full-size super-block quantize + GEMV at M = 1: every block's 144 bytes
+    and every output row against the oracle, in row chunks."""
     w, x = synth.q4k_case(name)
-    rows = np.sort(np.random.default_rng(6).choice(w.shape[0], 256, replace=False))
+    announce(f"q4k {name} {w.shape} M=1, all rows")
     blocks = B.gq_q4k_quantize(bf16_dev(w))
     y = B.gq_q4k_gemv(bf16_dev(x), blocks)
     torch.cuda.synchronize()
-    ref_blocks = O.q4k_encode(O.q4k_quantize(O.bf16_to_f64(w[rows])))
-    assert np.array_equal(blocks.cpu().numpy()[rows], ref_blocks)
-    ref = O.q4k_reference(x, ref_blocks)
-    wh = O.q4k_dequantize_fields(O.q4k_decode(ref_blocks))
-    assert_parity(bits16(y)[:, rows], ref, O.bf16_to_f64(x), wh, f"q4k {name} {w.shape} M=1 full, sampled")
+    got = blocks.cpu().numpy()
+    N = w.shape[0]
+    ref = np.empty((1, N))
+    wmax = 0.0
+    for r0 in range(0, N, 2048):
+        r1 = min(N, r0 + 2048)
+        ref_blocks = O.q4k_encode(O.q4k_quantize(O.bf16_to_f64(w[r0:r1])))
+        assert np.array_equal(got[r0:r1], ref_blocks), r0
+        wh = O.q4k_dequantize_fields(O.q4k_decode(ref_blocks))
+        wmax = max(wmax, float(np.abs(wh).max()))
+        ref[:, r0:r1] = O.matmul_groupwise(O.bf16_to_f64(x), wh, O.Q4K_SUB)
+    assert_parity(bits16(y), ref, O.bf16_to_f64(x), np.array([[wmax]]),
+                  f"q4k {name} {w.shape} M=1 full, all rows")

@@ -50,6 +50,7 @@
 // In both, workgroups are dealt round-robin to the 8 XCDs with the M tile
 // varying fastest, so each XCD keeps the same activation rows in its L2.
 #include <algorithm>
+#include <cstdlib>
 #include <type_traits>
 
 #include "gq_internal.h"
@@ -109,17 +110,46 @@ __device__ __forceinline__ float ubyte_f32(uint32_t x) {
   return r;
 }
 
-// 8 nibbles (k = 0..7 at bits 4p) -> 8 bf16 values q - z in k order (4 dwords).
+// two fp32 holding small integers -> packed fp16 pair (exact)
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
+// 8 nibbles (k = 0..7 at bits 4p) -> 8 bf16 (XF16: fp16) values q - z in k
+// order (4 dwords); |q - z| <= 15 is exact in both.
+template <bool XF16>
 __device__ __forceinline__ uint4 expand8(uint32_t d, float z) {
   const uint32_t e = d & 0x0F0F0F0Fu, o = (d >> 4) & 0x0F0F0F0Fu;
   const float q0 = ubyte_f32<0>(e) - z, q2 = ubyte_f32<1>(e) - z;
   const float q4 = ubyte_f32<2>(e) - z, q6 = ubyte_f32<3>(e) - z;
   const float q1 = ubyte_f32<0>(o) - z, q3 = ubyte_f32<1>(o) - z;
   const float q5 = ubyte_f32<2>(o) - z, q7 = ubyte_f32<3>(o) - z;
+  if (XF16) return make_uint4(pack_f16(q0, q1), pack_f16(q2, q3), pack_f16(q4, q5), pack_f16(q6, q7));
   return make_uint4(pack_bf16(q0, q1), pack_bf16(q2, q3), pack_bf16(q4, q5), pack_bf16(q6, q7));
 }
 
-template <int WM, bool SYM, bool TAIL>
+// 32 x 32 x 16 MFMA on 8-element operand registers of bf16 or fp16
+template <bool XF16>
+using opnd8_t = typename std::conditional<XF16, f16x8_t, bf16x8_t>::type;
+
+template <bool XF16>
+__device__ __forceinline__ f32x16_t mfma32(const opnd8_t<XF16>& a, const opnd8_t<XF16>& b,
+                                           const f32x16_t& c) {
+  if constexpr (XF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// The output element: bf16 (XF16: fp16), nearest-even.
+template <bool XF16>
+__device__ __forceinline__ uint16_t out16(float v) {
+  if constexpr (XF16) return __builtin_bit_cast(uint16_t, (_Float16)v);
+  else return f32_to_bf16_rne(v);
+}
+
+// XF16: fp16 activations, fp16 MFMA and fp16 output; otherwise bf16.
+template <int WM, bool SYM, bool TAIL, bool XF16 = false>
 __global__ __launch_bounds__(256 * WM, 2) void w4a16_gemm_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
@@ -227,8 +257,8 @@ __global__ __launch_bounds__(256 * WM, 2) void w4a16_gemm_kernel(
       const int col = id >> 1, half = id & 1;
       uint16_t* bs = Bs + (buf * kBN + col) * kLdsRow + half * 32;
       const float zf = SYM ? 8.f : h2f(S.z[h]);
-      uint4 e0 = expand8(S.b[h].x, zf), e1 = expand8(S.b[h].y, zf);
-      uint4 e2 = expand8(S.b[h].z, zf), e3 = expand8(S.b[h].w, zf);
+      uint4 e0 = expand8<XF16>(S.b[h].x, zf), e1 = expand8<XF16>(S.b[h].y, zf);
+      uint4 e2 = expand8<XF16>(S.b[h].z, zf), e3 = expand8<XF16>(S.b[h].w, zf);
       if ((S.s[h] & 0x7FFF) == 0) e0 = e1 = e2 = e3 = make_uint4(0, 0, 0, 0);  // S = 0: no contribution
       *(uint4*)(bs + 0) = e0;
       *(uint4*)(bs + 8) = e1;
@@ -271,18 +301,18 @@ __global__ __launch_bounds__(256 * WM, 2) void w4a16_gemm_kernel(
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       const int kk = ks * 16 + 8 * (lane >> 5);
-      bf16x8_t a[4], b[2];
+      opnd8_t<XF16> a[4], b[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        a[i] = __builtin_bit_cast(bf16x8_t, *(const uint4*)&as[i * 32 * kLdsRow + kk]);
+        a[i] = __builtin_bit_cast(opnd8_t<XF16>, *(const uint4*)&as[i * 32 * kLdsRow + kk]);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        b[j] = __builtin_bit_cast(bf16x8_t, *(const uint4*)&bs[j * 32 * kLdsRow + kk]);
+        b[j] = __builtin_bit_cast(opnd8_t<XF16>, *(const uint4*)&bs[j * 32 * kLdsRow + kk]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = mfma32<XF16>(a[i], b[j], acc[i][j]);
       const int kend = k0 + (ks + 1) * 16;
       if ((ks == 1 || ks == 3) && kend % G == 0 && kend < K) {
         float s[2];
@@ -328,7 +358,7 @@ __global__ __launch_bounds__(256 * WM, 2) void w4a16_gemm_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int gm = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (gm < M && gn < N) y[(size_t)gm * N + gn] = f32_to_bf16_rne(acc[i][j][v] * cref[j]);
+        if (gm < M && gn < N) y[(size_t)gm * N + gn] = out16<XF16>(acc[i][j][v] * cref[j]);
       }
     }
 }
@@ -348,11 +378,6 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// two fp32 holding small integers -> packed fp16 pair (exact)
-__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-}
-
 // 8 nibbles (k = 0..7 at bits 4p) -> 8 exact bf16 (or, XF16, fp16) values
 // m (q - z) in k order, with nz = -z m and m = 1, or m = 0 for a group whose
 // scale is 0.
@@ -365,19 +390,6 @@ __device__ __forceinline__ uint4 expand8m(uint32_t d, float m, float nz) {
   const float q5 = fmaf(ubyte_f32<2>(o), m, nz), q7 = fmaf(ubyte_f32<3>(o), m, nz);
   if (XF16) return make_uint4(pack_f16(q0, q1), pack_f16(q2, q3), pack_f16(q4, q5), pack_f16(q6, q7));
   return make_uint4(pack_bf16(q0, q1), pack_bf16(q2, q3), pack_bf16(q4, q5), pack_bf16(q6, q7));
-}
-
-// 32 x 32 x 16 MFMA on 8-element operand registers of bf16 or fp16
-template <bool XF16>
-using opnd8_t = typename std::conditional<XF16, f16x8_t, bf16x8_t>::type;
-
-template <bool XF16>
-__device__ __forceinline__ f32x16_t mfma32(const opnd8_t<XF16>& a, const opnd8_t<XF16>& b,
-                                           const f32x16_t& c) {
-  if constexpr (XF16)
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // Activation LDS tile: 16-byte chunk c of row r sits at position c ^ swz(r) of
@@ -400,15 +412,19 @@ struct WStage {
 // groups).  Each converts its running sum to the true scale; the first to finish
 // publishes it in `part` and raises the tile's flag, the second adds it to its
 // own (a sum of two terms, so the result does not depend on which finishes
-// first), writes Y and clears the tile's counter and flag for the next launch.
-// `sync` holds (counter, flag) per tile, zero between launches.
+// first) and writes Y.  `sync` holds two 64-bit words per tile (arrival,
+// flag) in caller memory of unknown content: each workgroup swaps the launch's
+// id into the arrival word, and the one that gets the id back is second (an id
+// is unique per call and random per process, so stale words never match it);
+// the second clears both words, so a graph that replays the same id finds
+// them clear.
 // XF16: fp16 activations and output (fp16 MFMA), otherwise bf16.
 template <bool SYM, int MODE, bool SPLIT, bool XF16 = false>
 __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
-    uint16_t* __restrict__ y, uint32_t* __restrict__ sync, float* __restrict__ part, int tsplit,
-    int tile0, int nt) {
+    uint16_t* __restrict__ y, uint64_t* __restrict__ sync, float* __restrict__ part, int tsplit,
+    int tile0, int nt, uint64_t launch_id, int poll_limit) {
   __shared__ uint4 sA0[kLM * 8], sA1[kLM * 8];                        // 2 x 32 KiB
   __shared__ uint4 sB0[kLN * kLBRow / 8], sB1[kLN * kLBRow / 8];      // 2 x 36 KiB
   __shared__ float sC0[2 * kLN], sC1[2 * kLN];                        // scales per column half
@@ -614,13 +630,35 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
     // and read as relaxed agent-scope atomics: those are coherent across the
     // XCDs' L2 caches without the whole-cache write-back and invalidation that
     // release/acquire fences would cost every other workgroup on the XCD.  The
-    // writer drains its stores before raising the flag; the reader loads the
-    // partials only after it has seen the flag.
+    // writer drains its stores (vmcnt 0: acknowledged by the coherent level)
+    // before any thread raises the flag; the reader issues its loads only after
+    // it has seen the flag (the loads are issued after the poll's value
+    // returned, and they bypass the non-coherent caches).
     float* slot = part + ((size_t)lt * 8 + wave) * 128 * 64 + lane;
-    __shared__ uint32_t s_first;
-    if (tid == 0) s_first = atomicAdd(&sync[2 * lt], 1u) == 0;
+    uint64_t* arrive = sync + 2 * lt;
+    uint64_t* flag = arrive + 1;
+    // 1: first to arrive; 2: second, the partner's sums are published;
+    // 3: second, the partner never published them (the poll bound expired)
+    __shared__ uint32_t s_role;
+    if (tid == 0) {
+      uint32_t role = 1;
+      if (__hip_atomic_exchange(arrive, launch_id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == launch_id) {
+        // the partner has swapped its id in, so it is running and publishes
+        // after its stores; the bound only guards against a lost workgroup
+        role = 3;
+        for (int n = 0; n < poll_limit; ++n) {
+          if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == launch_id) {
+            role = 2;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      s_role = role;
+    }
     __syncthreads();
-    if (s_first) {
+    const uint32_t role = s_role;
+    if (role == 1) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -631,38 +669,41 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       wait_vm<0>();
       __syncthreads();
-      if (tid == 0) __hip_atomic_store(&sync[2 * lt + 1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) __hip_atomic_store(flag, launch_id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
-    // The other workgroup has already counted itself, so it is running and
-    // raises the flag after its stores; the bound only guards against a
-    // corrupted flag word.
-    if (tid == 0) {
-      for (int n = 0; n < (1 << 24); ++n) {
-        if (__hip_atomic_load(&sync[2 * lt + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
-        __builtin_amdgcn_s_sleep(2);
-      }
-    }
-    __syncthreads();
-    {
+    if (role == 2) {
 #pragma clang fp contract(off)
+      // one accumulator tile (16 values) at a time: hoisting all 128 loads
+      // above their adds would need 128 more registers
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float o[16];
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            o[v] = __hip_atomic_load(&slot[((i * 2 + j) * 16 + v) * 64], __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+          // round(a c) + round(a' c'): each half's product is rounded on its own
+          // (contraction off), so the sum does not depend on which half came first
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[i][j][v] = acc[i][j][v] * cref[j] + o[v];
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+      // never silently wrong: a tile whose other half never arrived is NaN
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            // round(a c) + round(a' c'): each half's product is rounded on its own
-            // (contraction off), so the sum does not depend on which half came first
-            const float o = __hip_atomic_load(&slot[((i * 2 + j) * 16 + v) * 64], __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-            acc[i][j][v] = acc[i][j][v] * cref[j] + o;
-          }
+          for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_nanf("");
     }
     cref[0] = cref[1] = 1.f;  // acc now holds the true sum
     if (tid == 0) {
-      sync[2 * lt] = 0;
-      sync[2 * lt + 1] = 0;
+      __hip_atomic_store(arrive, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(flag, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
@@ -677,7 +718,7 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
         const int gm = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (gm < M && gn < N) {
           const float v_ = acc[i][j][v] * cref[j];
-          y[(size_t)gm * N + gn] = XF16 ? __builtin_bit_cast(uint16_t, (_Float16)v_) : f32_to_bf16_rne(v_);
+          y[(size_t)gm * N + gn] = out16<XF16>(v_);
         }
       }
     }
@@ -687,39 +728,59 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
 // compute units: all tiles when there are at most half as many as compute
 // units, else the last partial round (launched after the full rounds, so its
 // 2r half-tile workgroups run side by side).  Each half keeps at least two
-// groups' worth of 64-k tiles; the partial sums and the per-tile (counter,
-// flag) words live in two library scratch slots (not available while the
-// stream is captured: the tiles then run unsplit).
-template <bool SYM, int MODE, bool XF16 = false>
-hipError_t launch_lds(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
-                      const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
+// groups' worth of 64-k tiles.  Returns the number of split tiles (0: no split).
+int64_t split_tail(int M, int K, int N, int G, int64_t cus, int* tsplit) {
   const int64_t tiles = (int64_t)((M + kLM - 1) / kLM) * ((N + kLN - 1) / kLN);
   const int T = K / kBK;
   const int tpg = G >= kBK ? G / kBK : 1;  // 64-k tiles per group
-  const int tsplit = (T / 2) / std::max(tpg, 2) * std::max(tpg, 2);
-  const int64_t cus = num_cus();
+  *tsplit = (T / 2) / std::max(tpg, 2) * std::max(tpg, 2);
   const int64_t tail = tiles <= cus ? tiles : tiles % cus;  // tiles of the last round
-  if (tail > 0 && 2 * tail <= cus && tsplit >= 2 * tpg && T - tsplit >= 2 * tpg) {
-    const size_t sync_bytes = (size_t)tail * 8;
-    uint32_t* sync = (uint32_t*)stream_scratch(kScratchGemmSync, sync_bytes, sync_bytes, s);
-    float* part = (float*)stream_scratch(kScratchGemm, (size_t)tail * kLM * kLN * 4, 0, s);
-    if (sync && part) {
-      const int64_t full = tiles - tail;  // a multiple of the CU count: whole rounds
-      if (full > 0) {
-        hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE, false, XF16>), dim3((unsigned)full),
-                           dim3(kLT), 0, s, x, M, K, qw, sc, zr, N, G, y, nullptr, nullptr, 0, 0,
-                           (int)full);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-      }
-      hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE, true, XF16>), dim3((unsigned)(2 * tail)),
-                         dim3(kLT), 0, s, x, M, K, qw, sc, zr, N, G, y, sync, part, tsplit,
-                         (int)full, (int)tail);
-      return hipGetLastError();
+  if (tail > 0 && 2 * tail <= cus && *tsplit >= 2 * tpg && T - *tsplit >= 2 * tpg) return tail;
+  return 0;
+}
+
+// Scratch of a split: per split tile two 64-bit words (padded to 256 bytes
+// in all), then a 256 x 256 fp32 partial tile.
+size_t split_sync_bytes(int64_t tail) { return ((size_t)tail * 16 + 255) / 256 * 256; }
+size_t split_bytes(int64_t tail) { return tail ? split_sync_bytes(tail) + (size_t)tail * kLM * kLN * 4 : 0; }
+
+// Polls of the second half of a split tile before it gives up on the first
+// and writes NaN: 2^24 (each poll sleeps about 128 cycles, so about a second),
+// or GQ_SPLIT_POLL_LIMIT from the environment (a test sets 0 to take the
+// timeout path on purpose; every workgroup still exits normally).
+int split_poll_limit() {
+  const char* e = std::getenv("GQ_SPLIT_POLL_LIMIT");
+  if (!e || !*e) return 1 << 24;
+  const long v = std::strtol(e, nullptr, 10);
+  return (int)std::min<long>(std::max<long>(v, 0), 1 << 24);
+}
+
+// ws: scratch of at least split_bytes(split_tail(...)) bytes, or NULL: the
+// tiles then all run unsplit.
+template <bool SYM, int MODE, bool XF16 = false>
+hipError_t launch_lds(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
+                      const uint16_t* zr, int N, int G, uint16_t* y, void* ws, hipStream_t s) {
+  const int64_t tiles = (int64_t)((M + kLM - 1) / kLM) * ((N + kLN - 1) / kLN);
+  int tsplit = 0;
+  const int64_t tail = ws ? split_tail(M, K, N, G, num_cus(), &tsplit) : 0;
+  if (tail > 0) {
+    uint64_t* sync = (uint64_t*)ws;
+    float* part = (float*)((char*)ws + split_sync_bytes(tail));
+    const int64_t full = tiles - tail;  // a multiple of the CU count: whole rounds
+    if (full > 0) {
+      hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE, false, XF16>), dim3((unsigned)full),
+                         dim3(kLT), 0, s, x, M, K, qw, sc, zr, N, G, y, nullptr, nullptr, 0, 0,
+                         (int)full, (uint64_t)0, 0);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
     }
+    hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE, true, XF16>), dim3((unsigned)(2 * tail)),
+                       dim3(kLT), 0, s, x, M, K, qw, sc, zr, N, G, y, sync, part, tsplit,
+                       (int)full, (int)tail, next_launch_id(), split_poll_limit());
+    return hipGetLastError();
   }
   hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE, false, XF16>), dim3((unsigned)tiles), dim3(kLT), 0,
-                     s, x, M, K, qw, sc, zr, N, G, y, nullptr, nullptr, 0, 0, (int)tiles);
+                     s, x, M, K, qw, sc, zr, N, G, y, nullptr, nullptr, 0, 0, (int)tiles, (uint64_t)0, 0);
   return hipGetLastError();
 }
 
@@ -733,28 +794,28 @@ int lds_mode(int K, int G) {
   return -1;
 }
 
-template <int WM, bool SYM>
+template <int WM, bool SYM, bool XF16>
 hipError_t launch_t(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
                     const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
   constexpr int BM = 128 * WM;
   const int64_t grid = (int64_t)((M + BM - 1) / BM) * ((N + kBN - 1) / kBN);
   const size_t lds = (size_t)2 * (BM + kBN) * kLdsRow * 2 + (size_t)2 * 2 * kBN * 4;
   if (K % kBK == 0)
-    hipLaunchKernelGGL((w4a16_gemm_kernel<WM, SYM, false>), dim3((unsigned)grid), dim3(256 * WM), lds,
-                       s, x, M, K, qw, sc, zr, N, G, y);
+    hipLaunchKernelGGL((w4a16_gemm_kernel<WM, SYM, false, XF16>), dim3((unsigned)grid), dim3(256 * WM),
+                       lds, s, x, M, K, qw, sc, zr, N, G, y);
   else
-    hipLaunchKernelGGL((w4a16_gemm_kernel<WM, SYM, true>), dim3((unsigned)grid), dim3(256 * WM), lds,
-                       s, x, M, K, qw, sc, zr, N, G, y);
+    hipLaunchKernelGGL((w4a16_gemm_kernel<WM, SYM, true, XF16>), dim3((unsigned)grid), dim3(256 * WM),
+                       lds, s, x, M, K, qw, sc, zr, N, G, y);
   return hipGetLastError();
 }
 
-template <bool SYM>
+template <bool SYM, bool XF16>
 hipError_t dispatch(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
-                    const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
+                    const uint16_t* zr, int N, int G, uint16_t* y, void* ws, hipStream_t s) {
   switch (lds_mode(K, G)) {
-    case 1: return launch_lds<SYM, 1>(x, M, K, qw, sc, zr, N, G, y, s);
-    case 2: return launch_lds<SYM, 2>(x, M, K, qw, sc, zr, N, G, y, s);
-    case 3: return launch_lds<SYM, 3>(x, M, K, qw, sc, zr, N, G, y, s);
+    case 1: return launch_lds<SYM, 1, XF16>(x, M, K, qw, sc, zr, N, G, y, ws, s);
+    case 2: return launch_lds<SYM, 2, XF16>(x, M, K, qw, sc, zr, N, G, y, ws, s);
+    case 3: return launch_lds<SYM, 3, XF16>(x, M, K, qw, sc, zr, N, G, y, ws, s);
     default: break;
   }
   // 256-row tiles run two waves per SIMD and are faster per compute unit; the
@@ -763,39 +824,27 @@ hipError_t dispatch(const uint16_t* x, int M, int K, const uint8_t* qw, const ui
   // 2048 x 4096 x 4096 and 2048 x 4096 x 14336: +11 %).
   const int64_t tiles256 = (int64_t)((M + 255) / 256) * ((N + kBN - 1) / kBN);
   if (tiles256 < num_cus() && 2 * tiles256 <= num_cus())
-    return launch_t<1, SYM>(x, M, K, qw, sc, zr, N, G, y, s);
-  return launch_t<2, SYM>(x, M, K, qw, sc, zr, N, G, y, s);
+    return launch_t<1, SYM, XF16>(x, M, K, qw, sc, zr, N, G, y, s);
+  return launch_t<2, SYM, XF16>(x, M, K, qw, sc, zr, N, G, y, s);
 }
 
 }  // namespace
 
-bool gemm_f16_supported(int64_t K, int G) { return lds_mode((int)K, G) >= 0; }
-
-template <bool SYM>
-hipError_t dispatch_f16(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
-                        const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
-  switch (lds_mode(K, G)) {
-    case 1: return launch_lds<SYM, 1, true>(x, M, K, qw, sc, zr, N, G, y, s);
-    case 2: return launch_lds<SYM, 2, true>(x, M, K, qw, sc, zr, N, G, y, s);
-    case 3: return launch_lds<SYM, 3, true>(x, M, K, qw, sc, zr, N, G, y, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-hipError_t launch_w4a16_gemm_f16(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
-                                 const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
-                                 int symmetric, uint16_t* y, hipStream_t s) {
-  if (symmetric)
-    return dispatch_f16<true>(x, (int)M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
-  return dispatch_f16<false>(x, (int)M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
+size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, int G) {
+  if (lds_mode((int)K, G) < 0) return 0;
+  int tsplit = 0;
+  return split_bytes(split_tail((int)M, (int)K, (int)N, G, num_cus(), &tsplit));
 }
 
 hipError_t launch_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
                              const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
-                             int symmetric, uint16_t* y, hipStream_t s) {
-  if (symmetric)
-    return dispatch<true>(x, (int)M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
-  return dispatch<false>(x, (int)M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
+                             int symmetric, uint16_t* y, void* workspace, bool xf16, hipStream_t s) {
+  const int m = (int)M, k = (int)K, n = (int)N;
+  if (xf16)
+    return symmetric ? dispatch<true, true>(x, m, k, qweight, scales, zeros, n, G, y, workspace, s)
+                     : dispatch<false, true>(x, m, k, qweight, scales, zeros, n, G, y, workspace, s);
+  return symmetric ? dispatch<true, false>(x, m, k, qweight, scales, zeros, n, G, y, workspace, s)
+                   : dispatch<false, false>(x, m, k, qweight, scales, zeros, n, G, y, workspace, s);
 }
 
 }  // namespace gq

@@ -47,9 +47,17 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kStepK = 2048;   // k covered by one wave load (64 lanes x 32)
 
 // 8 nibbles of one dword (k offsets 0..7 at bits 4p) against the permuted
-// activation dwords (x0,x4) (x1,x5) (x2,x6) (x3,x7).
+// activation dwords (x0,x4) (x1,x5) (x2,x6) (x3,x7): bf16 128 + q, or (XF16)
+// fp16 1024 + q against fp16 activations.
+template <bool XF16>
 __device__ __forceinline__ float dot8(uint32_t d, const uint4& xp, float a) {
-  constexpr uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
+  constexpr uint32_t kMask = 0x000F000Fu, kMagic = XF16 ? 0x64006400u : 0x43004300u;
+  if (XF16) {
+    a = dot2h((d & kMask) | kMagic, xp.x, a);
+    a = dot2h(((d >> 4) & kMask) | kMagic, xp.y, a);
+    a = dot2h(((d >> 8) & kMask) | kMagic, xp.z, a);
+    return dot2h(((d >> 12) & kMask) | kMagic, xp.w, a);
+  }
   a = dot2((d & kMask) | kMagic, xp.x, a);
   a = dot2(((d >> 4) & kMask) | kMagic, xp.y, a);
   a = dot2(((d >> 8) & kMask) | kMagic, xp.z, a);
@@ -63,8 +71,9 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Stage x[:, kc0 : kc0 + KC) into LDS as permuted pairs plus 32-chunk sums.
-template <int MT, int KC>
+// Stage x[:, kc0 : kc0 + KC) into LDS as permuted pairs plus 32-chunk sums
+// (XF16: fp16 activations).
+template <int MT, int KC, bool XF16>
 __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, int M, int K, int kc0,
                                         uint4 (*xs)[KC / 8], float (*sx)[KC / 32]) {
   static_assert((KC / 8) % kThreads == 0, "chunk must be a multiple of 2048");
@@ -80,10 +89,7 @@ __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, int M, i
     p.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);  // (x2, x6)
     p.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);  // (x3, x7)
     xs[m][c] = p;
-    float s = bf16_to_f32(v.x & 0xFFFFu) + bf16_to_f32(v.x >> 16);
-    s += bf16_to_f32(v.y & 0xFFFFu) + bf16_to_f32(v.y >> 16);
-    s += bf16_to_f32(v.z & 0xFFFFu) + bf16_to_f32(v.z >> 16);
-    s += bf16_to_f32(v.w & 0xFFFFu) + bf16_to_f32(v.w >> 16);
+    float s = XF16 ? sum_f16x8(v) : sum_bf16x8(v);
     s += __shfl_xor(s, 1, 64);
     s += __shfl_xor(s, 2, 64);
     if ((c & 3) == 0) sx[m][c >> 2] = s;
@@ -91,8 +97,9 @@ __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, int M, i
 }
 
 // MT: activation rows handled together (M <= MT), RPW: weight rows per wave,
-// T: 2048-wide steps per LDS chunk.  Each workgroup owns 4*RPW rows.
-template <int MT, int RPW, int T, bool SYM>
+// T: 2048-wide steps per LDS chunk.  Each workgroup owns 4*RPW rows.  XF16:
+// fp16 activations and output.
+template <int MT, int RPW, int T, bool SYM, bool XF16>
 __global__ __launch_bounds__(kThreads) void gemv_chunked_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
@@ -115,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void gemv_chunked_kernel(
 
   for (int kc0 = 0; kc0 < K; kc0 += KC) {
     if (kc0) __syncthreads();
-    stage_x<MT, KC>(x, M, K, kc0, xs, sx);
+    stage_x<MT, KC, XF16>(x, M, K, kc0, xs, sx);
     __syncthreads();
 
     // Phase 1: issue every weight/scale load of this chunk.
@@ -134,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void gemv_chunked_kernel(
           wv[t][r] = load_nt16(qw + row * row_bytes + k / 2);
           const int gi = row * ng + k / G;
           sc[t][r] = f16_to_f32(scales[gi]);
-          zo[t][r] = SYM ? 136.f : 128.f + f16_to_f32(zeros[gi]);
+          zo[t][r] = (XF16 ? 1024.f : 128.f) + (SYM ? 8.f : f16_to_f32(zeros[gi]));
         }
       }
     }
@@ -149,10 +156,10 @@ __global__ __launch_bounds__(kThreads) void gemv_chunked_kernel(
         const float sxm = sx[m][kl / 32];
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
-          float a = dot8(wv[t][r].x, x0, 0.f);
-          a = dot8(wv[t][r].y, x1, a);
-          a = dot8(wv[t][r].z, x2, a);
-          a = dot8(wv[t][r].w, x3, a);
+          float a = dot8<XF16>(wv[t][r].x, x0, 0.f);
+          a = dot8<XF16>(wv[t][r].y, x1, a);
+          a = dot8<XF16>(wv[t][r].z, x2, a);
+          a = dot8<XF16>(wv[t][r].w, x3, a);
           acc[m][r] = fmaf(sc[t][r], fmaf(-zo[t][r], sxm, a), acc[m][r]);
         }
       }
@@ -165,40 +172,41 @@ __global__ __launch_bounds__(kThreads) void gemv_chunked_kernel(
     for (int r = 0; r < RPW; ++r) {
       const float v = wave_sum(acc[m][r]);
       const int row = row0 + r;
-      if (lane == 0 && m < M && row < N) y[(size_t)m * N + row] = f32_to_bf16_rne(v);
+      if (lane == 0 && m < M && row < N)
+        y[(size_t)m * N + row] = XF16 ? f32_to_f16_rne(v) : f32_to_bf16_rne(v);
     }
 }
 
-template <int MT, int RPW, int T, bool SYM>
+template <int MT, int RPW, int T, bool SYM, bool XF16>
 hipError_t launch_t(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
                     const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
   const int rows_per_block = kWaves * RPW;
   const unsigned grid = (unsigned)((N + rows_per_block - 1) / rows_per_block);
-  hipLaunchKernelGGL((gemv_chunked_kernel<MT, RPW, T, SYM>), dim3(grid), dim3(kThreads), 0, s, x,
-                     M, K, qw, sc, zr, N, G, y);
+  hipLaunchKernelGGL((gemv_chunked_kernel<MT, RPW, T, SYM, XF16>), dim3(grid), dim3(kThreads), 0, s,
+                     x, M, K, qw, sc, zr, N, G, y);
   return hipGetLastError();
 }
 
-template <bool SYM>
+template <bool SYM, bool XF16>
 hipError_t dispatch(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
                     const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
   const int steps = (K + kStepK - 1) / kStepK;
   if (M == 1) {
     switch (steps) {
-      case 1: return launch_t<1, 2, 1, SYM>(x, M, K, qw, sc, zr, N, G, y, s);
-      case 2: return launch_t<1, 2, 2, SYM>(x, M, K, qw, sc, zr, N, G, y, s);
-      case 3: return launch_t<1, 2, 3, SYM>(x, M, K, qw, sc, zr, N, G, y, s);
-      case 4: return launch_t<1, 2, 4, SYM>(x, M, K, qw, sc, zr, N, G, y, s);
-      case 5: return launch_t<1, 2, 5, SYM>(x, M, K, qw, sc, zr, N, G, y, s);
-      case 6: return launch_t<1, 2, 6, SYM>(x, M, K, qw, sc, zr, N, G, y, s);
-      case 7: return launch_t<1, 2, 7, SYM>(x, M, K, qw, sc, zr, N, G, y, s);
-      default: return launch_t<1, 2, 8, SYM>(x, M, K, qw, sc, zr, N, G, y, s);
+      case 1: return launch_t<1, 2, 1, SYM, XF16>(x, M, K, qw, sc, zr, N, G, y, s);
+      case 2: return launch_t<1, 2, 2, SYM, XF16>(x, M, K, qw, sc, zr, N, G, y, s);
+      case 3: return launch_t<1, 2, 3, SYM, XF16>(x, M, K, qw, sc, zr, N, G, y, s);
+      case 4: return launch_t<1, 2, 4, SYM, XF16>(x, M, K, qw, sc, zr, N, G, y, s);
+      case 5: return launch_t<1, 2, 5, SYM, XF16>(x, M, K, qw, sc, zr, N, G, y, s);
+      case 6: return launch_t<1, 2, 6, SYM, XF16>(x, M, K, qw, sc, zr, N, G, y, s);
+      case 7: return launch_t<1, 2, 7, SYM, XF16>(x, M, K, qw, sc, zr, N, G, y, s);
+      default: return launch_t<1, 2, 8, SYM, XF16>(x, M, K, qw, sc, zr, N, G, y, s);
     }
   }
-  if (M == 2) return launch_t<2, 2, 2, SYM>(x, M, K, qw, sc, zr, N, G, y, s);
-  if (M <= 4) return launch_t<4, 2, 1, SYM>(x, M, K, qw, sc, zr, N, G, y, s);
-  if (M <= 8) return launch_t<8, 2, 1, SYM>(x, M, K, qw, sc, zr, N, G, y, s);
-  return launch_t<16, 2, 1, SYM>(x, M, K, qw, sc, zr, N, G, y, s);
+  if (M == 2) return launch_t<2, 2, 2, SYM, XF16>(x, M, K, qw, sc, zr, N, G, y, s);
+  if (M <= 4) return launch_t<4, 2, 1, SYM, XF16>(x, M, K, qw, sc, zr, N, G, y, s);
+  if (M <= 8) return launch_t<8, 2, 1, SYM, XF16>(x, M, K, qw, sc, zr, N, G, y, s);
+  return launch_t<16, 2, 1, SYM, XF16>(x, M, K, qw, sc, zr, N, G, y, s);
 }
 
 
@@ -553,41 +561,30 @@ bool gemv_stream_supported(int M, int64_t K) {
   return M >= 2 && M <= kSMaxM && stream_lds_bytes(M, K, true) <= kSLdsOne;
 }
 
-// fp16 activations: the streaming kernel (M = 1..4) and the matrix-core
-// streaming kernel (M = 4..16) where they take the shape.
-bool gemv_f16_supported(int M, int64_t K, int64_t N, int G) {
-  return gemv_stream_supported(M, K) || gemv_mfma_stream_supported(M, K, N, G);
-}
-
-hipError_t launch_w4a16_gemv_f16(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
-                                 const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
-                                 int symmetric, uint16_t* y, hipStream_t s) {
-  if (gemv_stream_supported(M, K)) {
-    if (symmetric) return stream_any<true, true>(x, M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
-    return stream_any<false, true>(x, M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
-  }
-  return launch_w4a16_gemv_mfma_stream(x, M, K, qweight, scales, zeros, N, G, symmetric, y, s, true);
-}
-
+// Kernel choice: the streaming kernel (M = 1..4 while x fits its LDS stage),
+// the matrix-core streaming kernel (M = 4..16 where it takes the shape), the
+// split-K matrix-core kernel when the caller gives a workspace for it, and the
+// per-row dot-product kernel for everything else; none of them allocates.
 hipError_t launch_w4a16_gemv(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
                              const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
-                             int symmetric, uint16_t* y, void* workspace, size_t ws_bytes,
-                             hipStream_t s) {
+                             int symmetric, uint16_t* y, void* workspace, bool xf16, hipStream_t s) {
+  const int k = (int)K, n = (int)N;
   if (gemv_stream_supported(M, K)) {
-    if (symmetric) return stream_any<true>(x, M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
-    return stream_any<false>(x, M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
+    if (xf16)
+      return symmetric ? stream_any<true, true>(x, M, k, qweight, scales, zeros, n, G, y, s)
+                       : stream_any<false, true>(x, M, k, qweight, scales, zeros, n, G, y, s);
+    return symmetric ? stream_any<true>(x, M, k, qweight, scales, zeros, n, G, y, s)
+                     : stream_any<false>(x, M, k, qweight, scales, zeros, n, G, y, s);
   }
   if (gemv_mfma_stream_supported(M, K, N, G))
-    return launch_w4a16_gemv_mfma_stream(x, M, K, qweight, scales, zeros, N, G, symmetric, y, s);
-  if (gemv_mfma_supported(M, K, N, G)) {
-    (void)ws_bytes;  // checked against gemv_workspace_bytes by the caller
-    bool launched = false;
-    const hipError_t e = launch_w4a16_gemv_mfma(x, M, K, qweight, scales, zeros, N, G, symmetric,
-                                                y, workspace, s, &launched);
-    if (e != hipSuccess || launched) return e;
-  }
-  if (symmetric) return dispatch<true>(x, M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
-  return dispatch<false>(x, M, (int)K, qweight, scales, zeros, (int)N, G, y, s);
+    return launch_w4a16_gemv_mfma_stream(x, M, K, qweight, scales, zeros, N, G, symmetric, y, s, xf16);
+  if (workspace && gemv_workspace_bytes(M, K, N, G) > 0)
+    return launch_w4a16_gemv_mfma(x, M, K, qweight, scales, zeros, N, G, symmetric, y, workspace, xf16, s);
+  if (xf16)
+    return symmetric ? dispatch<true, true>(x, M, k, qweight, scales, zeros, n, G, y, s)
+                     : dispatch<false, true>(x, M, k, qweight, scales, zeros, n, G, y, s);
+  return symmetric ? dispatch<true, false>(x, M, k, qweight, scales, zeros, n, G, y, s)
+                   : dispatch<false, false>(x, M, k, qweight, scales, zeros, n, G, y, s);
 }
 
 }  // namespace gq

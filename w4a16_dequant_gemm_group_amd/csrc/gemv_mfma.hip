@@ -25,12 +25,9 @@
 //    sums of x and the scale applied in fp32:
 //      acc[m][n] += S * (D[m][n] - (128 + z) * sum_{k in segment} x[m][k]).
 // Tile kernel: a workgroup (4 waves, 64 rows) covers a 1024-wide slice of K
-// and writes fp32 partial sums.  With library scratch, the last workgroup of a 64-row group to
-// finish (a per-group counter) adds the slices; with a caller's workspace (no
-// counters that are known to be zero) a second kernel does.  Either way the
-// slices are added in slice order (so the result does not depend on
-// scheduling, and both ways agree bit for bit) and rounded once to bf16
-// (nearest-even).
+// and writes fp32 partial sums to the caller's workspace; a second kernel adds
+// the slices in slice order (so the result does not depend on scheduling) and
+// rounds once to bf16 (fp16 for fp16 activations), nearest-even.
 #include <algorithm>
 #include <utility>
 
@@ -106,15 +103,12 @@ __device__ __forceinline__ void transpose4(uint32_t& d0, uint32_t& d1, uint32_t&
 // multiple of 128).  MR: activation rows staged (>= M; 4, 8 or 16).  Requires
 // N * K / 2 and M * K * 2 below 2^31 (byte offsets of the buffer loads).
 // G = 32 needs about 400 registers per lane without spilling: one wave per SIMD.
-// FUSE: partial sums are written as relaxed agent-scope atomics (coherent
-// across the XCDs' L2 caches), drained, and counted in cnt[row group]; the
-// workgroup that counts last reads every slice back in slice order, writes y
-// and resets the counter (zero between launches).
-template <int CPG, bool SYM, int MR, bool FUSE>
+// XF16: fp16 activations (nibbles as fp16 1024 + q, fp16 MFMA).
+template <int CPG, bool SYM, int MR, bool XF16>
 __global__ __launch_bounds__(256, CPG == 1 ? 1 : 2) void gemv_mfma_tile_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
-    float* __restrict__ part, uint32_t* __restrict__ cnt, uint16_t* __restrict__ y) {
+    float* __restrict__ part) {
   __shared__ uint4 xs[MR * kXRow];     // x[m][k0 .. k0 + 1024) as permuted 8-chunks
   __shared__ float sxs[kKC / 32][16];  // per 32-chunk and row m: sum of x (0 for m >= MR)
   // G = 32: per wave, scale | zero << 16 of its 16 rows x 32 groups (registers would spill)
@@ -192,10 +186,10 @@ __global__ __launch_bounds__(256, CPG == 1 ? 1 : 2) void gemv_mfma_tile_kernel(
     const int m = id >> 7, c = id & 127;
     const uint4 v = xv[j];
     xs[m * kXRow + c] = perm_x(v);
-    float s = dot2(v.x, 0x3F803F80u, 0.f);  // bf16 1.0 pairs
-    s = dot2(v.y, 0x3F803F80u, s);
-    s = dot2(v.z, 0x3F803F80u, s);
-    s = dot2(v.w, 0x3F803F80u, s);
+    float s = dot2x<XF16>(v.x, 0.f);  // against 1.0 pairs
+    s = dot2x<XF16>(v.y, s);
+    s = dot2x<XF16>(v.z, s);
+    s = dot2x<XF16>(v.w, s);
     s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0xB1,
                                                                0xF, 0xF, true));
     s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x4E,
@@ -221,7 +215,8 @@ __global__ __launch_bounds__(256, CPG == 1 ? 1 : 2) void gemv_mfma_tile_kernel(
   __syncthreads();
 
   // 5. MFMAs and per-segment corrections; lane (n, g) accumulates rows m = 4g + r
-  const uint32_t magic = 0x43004300u;
+  const uint32_t magic = XF16 ? 0x64006400u : 0x43004300u;  // 1024 + q (fp16) / 128 + q (bf16)
+  constexpr float kOff = XF16 ? 1024.f : 128.f;
   const int xrow = (n % MR) * kXRow;  // A row of this lane (rows >= M are dropped at the end)
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   f32x4_t D = {0.f, 0.f, 0.f, 0.f};
@@ -235,8 +230,12 @@ __global__ __launch_bounds__(256, CPG == 1 ? 1 : 2) void gemv_mfma_tile_kernel(
       const uint4 A = xs[xrow + 16 * L + 4 * c + g];
       const uint4 B = unpack8(ev[c], magic);
       const f32x4_t Cin = (c % CPG == 0) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : D;
-      D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A),
-                                                  __builtin_bit_cast(bf16x8_t, B), Cin, 0, 0, 0);
+      if constexpr (XF16)
+        D = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, A),
+                                                   __builtin_bit_cast(f16x8_t, B), Cin, 0, 0, 0);
+      else
+        D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A),
+                                                    __builtin_bit_cast(bf16x8_t, B), Cin, 0, 0, 0);
       if (c % CPG == CPG - 1) {
         uint32_t sb, zb;
         if (GPS == 1) {
@@ -250,7 +249,7 @@ __global__ __launch_bounds__(256, CPG == 1 ? 1 : 2) void gemv_mfma_tile_kernel(
           zb = sb >> 16;
         }
         const float s = f16_to_f32((uint16_t)sb);
-        const float zc = 128.f + (SYM ? 8.f : f16_to_f32((uint16_t)zb));
+        const float zc = kOff + (SYM ? 8.f : f16_to_f32((uint16_t)zb));
         const int ch = 4 * L + c;  // last 32-chunk of the segment
         float4 sx = *(const float4*)&sxs[ch][4 * g];
 #pragma unroll
@@ -269,63 +268,15 @@ __global__ __launch_bounds__(256, CPG == 1 ? 1 : 2) void gemv_mfma_tile_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);  // keep each step's fragments short-lived
   }
-  if constexpr (!FUSE) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 4 * g + r;
-      if (m < M && rin) part[((size_t)split * M + m) * N + row] = acc[r];
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 4 * g + r;
-      if (m < M && rin)
-        __hip_atomic_store(&part[((size_t)split * M + m) * N + row], acc[r], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // the stores are done before the count says so
-    __shared__ uint32_t s_last;
-    __syncthreads();
-    if (threadIdx.x == 0)
-      s_last = __hip_atomic_fetch_add(&cnt[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               gridDim.y - 1;
-    __syncthreads();
-    if (!s_last) return;
-    // every other slice of this row group has counted itself after its stores.
-    // Thread t adds outputs t + 256 q (q < 4: M * 64 <= 1024), eight slices'
-    // loads of all its outputs in flight at a time, each output's slices added
-    // in slice order
-    const int splits = (int)gridDim.y;
-    float t[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < splits; j0 += 8) {
-      float v[4][8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int i = threadIdx.x + 256 * q, m = i >> 6, r = blockIdx.x * 64 + (i & 63);
-        const bool ok = m < M && r < N;
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          v[q][u] = ok && j0 + u < splits
-                        ? __hip_atomic_load(&part[((size_t)(j0 + u) * M + m) * N + r],
-                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                        : 0.f;
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (j0 + u < splits) t[q] += v[q][u];
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = threadIdx.x + 256 * q, m = i >> 6, r = blockIdx.x * 64 + (i & 63);
-      if (m < M && r < N) y[(size_t)m * N + r] = f32_to_bf16_rne(t[q]);
-    }
-    if (threadIdx.x == 0) __hip_atomic_store(&cnt[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * g + r;
+    if (m < M && rin) part[((size_t)split * M + m) * N + row] = acc[r];
   }
 }
 
-// y = bf16(sum of the K slices, in slice order)
+// y = bf16 (XF16: fp16) of the sum of the K slices, in slice order
+template <bool XF16>
 __global__ __launch_bounds__(256) void gemv_split_finalize_kernel(const float* __restrict__ part,
                                                                   int splits, int64_t MN,
                                                                   uint16_t* __restrict__ y) {
@@ -333,7 +284,7 @@ __global__ __launch_bounds__(256) void gemv_split_finalize_kernel(const float* _
   if (i >= MN) return;
   float s = 0.f;
   for (int j = 0; j < splits; ++j) s += part[(size_t)j * MN + i];
-  y[i] = f32_to_bf16_rne(s);
+  y[i] = XF16 ? __builtin_bit_cast(uint16_t, (_Float16)s) : f32_to_bf16_rne(s);
 }
 
 
@@ -632,35 +583,28 @@ hipError_t launch_ms(const uint16_t* x, int M, int K, int KC, const uint8_t* qw,
   return hipGetLastError();
 }
 
-template <int CPG, bool SYM, bool FUSE>
+template <int CPG, bool SYM, bool XF16>
 hipError_t launch_cpg(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
-                      const uint16_t* zr, int N, int G, float* part, int splits, uint32_t* cnt,
-                      uint16_t* y, hipStream_t s) {
+                      const uint16_t* zr, int N, int G, float* part, int splits, hipStream_t s) {
   const dim3 grid((unsigned)((N + 63) / 64), (unsigned)splits);
   if (M <= 4)
-    hipLaunchKernelGGL((gemv_mfma_tile_kernel<CPG, SYM, 4, FUSE>), grid, dim3(256), 0, s, x, M, K, qw,
-                       sc, zr, N, G, part, cnt, y);
+    hipLaunchKernelGGL((gemv_mfma_tile_kernel<CPG, SYM, 4, XF16>), grid, dim3(256), 0, s, x, M, K, qw,
+                       sc, zr, N, G, part);
   else if (M <= 8)
-    hipLaunchKernelGGL((gemv_mfma_tile_kernel<CPG, SYM, 8, FUSE>), grid, dim3(256), 0, s, x, M, K, qw,
-                       sc, zr, N, G, part, cnt, y);
+    hipLaunchKernelGGL((gemv_mfma_tile_kernel<CPG, SYM, 8, XF16>), grid, dim3(256), 0, s, x, M, K, qw,
+                       sc, zr, N, G, part);
   else
-    hipLaunchKernelGGL((gemv_mfma_tile_kernel<CPG, SYM, 16, FUSE>), grid, dim3(256), 0, s, x, M, K, qw,
-                       sc, zr, N, G, part, cnt, y);
+    hipLaunchKernelGGL((gemv_mfma_tile_kernel<CPG, SYM, 16, XF16>), grid, dim3(256), 0, s, x, M, K, qw,
+                       sc, zr, N, G, part);
   return hipGetLastError();
 }
 
-template <bool FUSE>
+template <bool SYM, bool XF16>
 hipError_t launch_all(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
-                      const uint16_t* zr, int N, int G, int symmetric, float* part, int splits,
-                      uint32_t* cnt, uint16_t* y, hipStream_t s) {
-  if (symmetric) {
-    if (G == 32) return launch_cpg<1, true, FUSE>(x, M, K, qw, sc, zr, N, G, part, splits, cnt, y, s);
-    if (G == 64) return launch_cpg<2, true, FUSE>(x, M, K, qw, sc, zr, N, G, part, splits, cnt, y, s);
-    return launch_cpg<4, true, FUSE>(x, M, K, qw, sc, zr, N, G, part, splits, cnt, y, s);
-  }
-  if (G == 32) return launch_cpg<1, false, FUSE>(x, M, K, qw, sc, zr, N, G, part, splits, cnt, y, s);
-  if (G == 64) return launch_cpg<2, false, FUSE>(x, M, K, qw, sc, zr, N, G, part, splits, cnt, y, s);
-  return launch_cpg<4, false, FUSE>(x, M, K, qw, sc, zr, N, G, part, splits, cnt, y, s);
+                      const uint16_t* zr, int N, int G, float* part, int splits, hipStream_t s) {
+  if (G == 32) return launch_cpg<1, SYM, XF16>(x, M, K, qw, sc, zr, N, G, part, splits, s);
+  if (G == 64) return launch_cpg<2, SYM, XF16>(x, M, K, qw, sc, zr, N, G, part, splits, s);
+  return launch_cpg<4, SYM, XF16>(x, M, K, qw, sc, zr, N, G, part, splits, s);
 }
 
 }  // namespace
@@ -735,41 +679,27 @@ size_t gemv_workspace_bytes(int M, int64_t K, int64_t N, int G) {
 
 hipError_t launch_w4a16_gemv_mfma(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
                                   const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
-                                  int symmetric, uint16_t* y, void* workspace, hipStream_t s,
-                                  bool* launched) {
-  *launched = false;
+                                  int symmetric, uint16_t* y, void* workspace, bool xf16,
+                                  hipStream_t s) {
   const int splits = (int)((K + kKC - 1) / kKC);
   const int k = (int)K, n = (int)N;
-  hipError_t e;
   float* part = (float*)workspace;
-  if (!part) {
-    part = (float*)stream_scratch(kScratchGemv, gemv_workspace_bytes(M, K, N, G), 0, s);
-    if (!part) return hipSuccess;  // no scratch (graph capture): the caller falls back
-    // The last workgroup of a row group adds the slices when the grid runs in
-    // at most two rounds; with more rounds every workgroup's drain-and-count
-    // tail costs more than the second launch it saves (gate_up, M = 4..16:
-    // 35 us fused against 30 us).  Counters: one per 64-row group, in a slot of
-    // their own (cleared when allocated, reset by the workgroup that used them).
-    const int64_t groups = (N + 63) / 64;
-    const int64_t per_round = (int64_t)num_cus() * (G == 32 ? 1 : 2);  // resident workgroups
-    if (groups * splits <= 2 * per_round) {
-      uint32_t* cnt = (uint32_t*)stream_scratch(kScratchGemvSync, (size_t)groups * 4, (size_t)groups * 4, s);
-      if (cnt) {
-        e = launch_all<true>(x, M, k, qweight, scales, zeros, n, G, symmetric, part, splits, cnt, y, s);
-        if (e == hipSuccess) *launched = true;
-        return e;
-      }
-    }
-  }
-  e = launch_all<false>(x, M, k, qweight, scales, zeros, n, G, symmetric, part, splits, nullptr, nullptr,
-                        s);
+  hipError_t e;
+  if (xf16)
+    e = symmetric ? launch_all<true, true>(x, M, k, qweight, scales, zeros, n, G, part, splits, s)
+                  : launch_all<false, true>(x, M, k, qweight, scales, zeros, n, G, part, splits, s);
+  else
+    e = symmetric ? launch_all<true, false>(x, M, k, qweight, scales, zeros, n, G, part, splits, s)
+                  : launch_all<false, false>(x, M, k, qweight, scales, zeros, n, G, part, splits, s);
   if (e != hipSuccess) return e;
   const int64_t mn = (int64_t)M * N;
-  hipLaunchKernelGGL(gemv_split_finalize_kernel, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, s,
-                     (const float*)part, splits, mn, y);
-  e = hipGetLastError();
-  if (e == hipSuccess) *launched = true;
-  return e;
+  if (xf16)
+    hipLaunchKernelGGL(gemv_split_finalize_kernel<true>, dim3((unsigned)((mn + 255) / 256)), dim3(256),
+                       0, s, (const float*)part, splits, mn, y);
+  else
+    hipLaunchKernelGGL(gemv_split_finalize_kernel<false>, dim3((unsigned)((mn + 255) / 256)), dim3(256),
+                       0, s, (const float*)part, splits, mn, y);
+  return hipGetLastError();
 }
 
 }  // namespace gq

@@ -3,10 +3,9 @@
 // invalid call never touches the device (and can be exercised without one).
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <cstring>
-#include <map>
-#include <mutex>
-#include <tuple>
+#include <random>
 
 #include "gq_internal.h"
 
@@ -72,36 +71,14 @@ gq_status check_w4_matmul(const uint16_t* x, int64_t M, int64_t K, const uint8_t
 
 namespace gq {
 
-// Library scratch: one buffer per (device, stream, slot), grown on demand and
-// kept for the life of the process.  Calls on one stream are ordered; different
-// streams get different buffers.  A new buffer's first zero_bytes are cleared
-// (on s) before first use.  While s is being captured into a graph nullptr is
-// returned, even when a buffer exists (the caller takes another path): a graph
-// must not hold a buffer that a later, larger call on the stream would free.
-void* stream_scratch(int slot, size_t bytes, size_t zero_bytes, hipStream_t s) {
-  static std::mutex mu;
-  static std::map<std::tuple<int, hipStream_t, int>, std::pair<void*, size_t>> bufs;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
-  std::lock_guard<std::mutex> lock(mu);
-  auto& b = bufs[{dev, s, slot}];
-  if (b.second >= bytes) return b.first;
-  if (b.first) {
-    // the old buffer may still be used by work queued on s
-    if (hipStreamSynchronize(s) != hipSuccess) return nullptr;
-    hipFree(b.first);
-    b = {nullptr, 0};
-  }
-  void* p = nullptr;
-  if (hipMalloc(&p, bytes) != hipSuccess) return nullptr;
-  if (zero_bytes && hipMemsetAsync(p, 0, std::min(zero_bytes, bytes), s) != hipSuccess) {
-    hipFree(p);
-    return nullptr;
-  }
-  b = {p, bytes};
-  return p;
+uint64_t next_launch_id() {
+  static std::atomic<uint64_t> seq{[] {
+    std::random_device rd;
+    uint64_t v = ((uint64_t)rd() << 32) ^ (uint64_t)rd();
+    v ^= (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() * 0x9E3779B97F4A7C15ull;
+    return v;
+  }()};
+  return seq.fetch_add(2, std::memory_order_relaxed) | 1ull;
 }
 
 int num_cus() {
@@ -198,27 +175,86 @@ gq_status gq_ingest_group_major(const int8_t* codes, const uint16_t* scales, int
                                                 scales_out, s));
 }
 
-gq_status gq_w4a16_gemv(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
-                        const uint16_t* scales, const uint16_t* zeros, int64_t N, gq_qparams p,
-                        uint16_t* y, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The GEMV entry points: validation, then the launch with the caller's
+// workspace (or none) and the activation type.
+gq_status gemv_call(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                    const uint16_t* scales, const uint16_t* zeros, int64_t N, gq_qparams p,
+                    uint16_t* y, void* workspace, size_t workspace_bytes, bool has_ws, bool xf16,
+                    void* stream) {
   if (M > 16) return GQ_ERR_INVALID_ARG;
   if (gq_status s = check_w4_matmul(x, M, K, qweight, scales, zeros, N, p, y)) return s;
   if (M == 0 || N == 0) return GQ_OK;
+  const size_t need = has_ws ? gq::gemv_workspace_bytes((int)M, K, N, p.group_size) : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GQ_ERR_INVALID_ARG;
+  if (need > 0 && !aligned16(workspace)) return GQ_ERR_MISALIGNED;
   hipStream_t s = (hipStream_t)stream;
   if (gq_status st = check_device(s)) return st;
   return from_hip(gq::launch_w4a16_gemv(x, (int)M, K, qweight, scales, zeros, N, p.group_size,
-                                        p.symmetric, y, nullptr, 0, s));
+                                        p.symmetric, y, need ? workspace : nullptr, xf16, s));
+}
+
+// Limits of the GEMM launches: 32-bit tile counts and activation offsets.
+gq_status check_gemm(int64_t M, int64_t K, int64_t N) {
+  if (K > kMaxGemmK || M > kMaxDim / 2) return GQ_ERR_UNSUPPORTED;
+  if (((M + 127) / 128) * ((N + 255) / 256) > INT32_MAX / 2) return GQ_ERR_UNSUPPORTED;
+  return GQ_OK;
+}
+
+// The CU count the split decision uses: the device's when one is present.
+void probe_device() {
+  int n = 0;
+  if (hipGetDeviceCount(&n) == hipSuccess && n > 0) (void)check_device(nullptr);
+}
+
+gq_status gemm_call(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                    const uint16_t* scales, const uint16_t* zeros, int64_t N, gq_qparams p,
+                    uint16_t* y, void* workspace, size_t workspace_bytes, bool has_ws, bool xf16,
+                    void* stream) {
+  if (gq_status s = check_w4_matmul(x, M, K, qweight, scales, zeros, N, p, y)) return s;
+  if (gq_status s = check_gemm(M, K, N)) return s;
+  if (M == 0 || N == 0) return GQ_OK;
+  size_t need = 0;
+  if (has_ws) {
+    probe_device();  // the split depends on the device's compute-unit count
+    need = gq::gemm_workspace_bytes(M, K, N, p.group_size);
+  }
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GQ_ERR_INVALID_ARG;
+  if (need > 0 && !aligned16(workspace)) return GQ_ERR_MISALIGNED;
+  hipStream_t s = (hipStream_t)stream;
+  if (gq_status st = check_device(s)) return st;
+  return from_hip(gq::launch_w4a16_gemm(x, M, K, qweight, scales, zeros, N, p.group_size,
+                                        p.symmetric, y, need ? workspace : nullptr, xf16, s));
+}
+
+gq_status matmul_params(int64_t M, int64_t K, int64_t N, gq_qparams p) {
+  if (M < 0 || M > kMaxDim) return GQ_ERR_INVALID_ARG;
+  if (gq_status s = check_groups(N, K, p.group_size)) return s;
+  if (p.symmetric != 0 && p.symmetric != 1) return GQ_ERR_INVALID_ARG;
+  if (p.bits < 2 || p.bits > 8) return GQ_ERR_INVALID_ARG;
+  if (p.bits != 4) return GQ_ERR_UNSUPPORTED;
+  return GQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gq_status gq_w4a16_gemv(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                        const uint16_t* scales, const uint16_t* zeros, int64_t N, gq_qparams p,
+                        uint16_t* y, void* stream) {
+  return gemv_call(x, M, K, qweight, scales, zeros, N, p, y, nullptr, 0, false, false, stream);
 }
 
 gq_status gq_w4a16_gemv_workspace_size(int64_t M, int64_t K, int64_t N, gq_qparams p,
                                        size_t* bytes) {
   if (!bytes) return GQ_ERR_INVALID_ARG;
   *bytes = 0;
-  if (M < 0 || M > 16) return GQ_ERR_INVALID_ARG;
-  if (gq_status s = check_groups(N, K, p.group_size)) return s;
-  if (p.symmetric != 0 && p.symmetric != 1) return GQ_ERR_INVALID_ARG;
-  if (p.bits < 2 || p.bits > 8) return GQ_ERR_INVALID_ARG;
-  if (p.bits != 4) return GQ_ERR_UNSUPPORTED;
+  if (M > 16) return GQ_ERR_INVALID_ARG;
+  if (gq_status s = matmul_params(M, K, N, p)) return s;
   *bytes = gq::gemv_workspace_bytes((int)M, K, N, p.group_size);
   return GQ_OK;
 }
@@ -227,57 +263,62 @@ gq_status gq_w4a16_gemv_ws(const uint16_t* x, int64_t M, int64_t K, const uint8_
                            const uint16_t* scales, const uint16_t* zeros, int64_t N,
                            gq_qparams p, uint16_t* y, void* workspace, size_t workspace_bytes,
                            void* stream) {
-  if (M > 16) return GQ_ERR_INVALID_ARG;
-  if (gq_status s = check_w4_matmul(x, M, K, qweight, scales, zeros, N, p, y)) return s;
-  if (M == 0 || N == 0) return GQ_OK;
-  const size_t need = gq::gemv_workspace_bytes((int)M, K, N, p.group_size);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return GQ_ERR_INVALID_ARG;
-  if (workspace && !aligned16(workspace)) return GQ_ERR_MISALIGNED;
-  hipStream_t s = (hipStream_t)stream;
-  if (gq_status st = check_device(s)) return st;
-  return from_hip(gq::launch_w4a16_gemv(x, (int)M, K, qweight, scales, zeros, N, p.group_size,
-                                        p.symmetric, y, need ? workspace : nullptr, need, s));
-}
-
-gq_status gq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
-                        const uint16_t* scales, const uint16_t* zeros, int64_t N, gq_qparams p,
-                        uint16_t* y, void* stream) {
-  if (gq_status s = check_w4_matmul(x, M, K, qweight, scales, zeros, N, p, y)) return s;
-  if (K > kMaxGemmK || M > kMaxDim / 2) return GQ_ERR_UNSUPPORTED;
-  // one workgroup per output tile (128 or 256 rows x 256 columns)
-  if (((M + 127) / 128) * ((N + 255) / 256) > INT32_MAX) return GQ_ERR_UNSUPPORTED;
-  if (M == 0 || N == 0) return GQ_OK;
-  hipStream_t s = (hipStream_t)stream;
-  if (gq_status st = check_device(s)) return st;
-  return from_hip(gq::launch_w4a16_gemm(x, M, K, qweight, scales, zeros, N, p.group_size,
-                                        p.symmetric, y, s));
+  return gemv_call(x, M, K, qweight, scales, zeros, N, p, y, workspace, workspace_bytes, true, false,
+                   stream);
 }
 
 gq_status gq_w4a16_gemv_f16(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
                             const uint16_t* scales, const uint16_t* zeros, int64_t N,
                             gq_qparams p, uint16_t* y, void* stream) {
-  if (M > 16) return GQ_ERR_INVALID_ARG;
-  if (gq_status s = check_w4_matmul(x, M, K, qweight, scales, zeros, N, p, y)) return s;
+  return gemv_call(x, M, K, qweight, scales, zeros, N, p, y, nullptr, 0, false, true, stream);
+}
+
+gq_status gq_w4a16_gemv_f16_ws(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                               const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                               gq_qparams p, uint16_t* y, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return gemv_call(x, M, K, qweight, scales, zeros, N, p, y, workspace, workspace_bytes, true, true,
+                   stream);
+}
+
+gq_status gq_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                        const uint16_t* scales, const uint16_t* zeros, int64_t N, gq_qparams p,
+                        uint16_t* y, void* stream) {
+  return gemm_call(x, M, K, qweight, scales, zeros, N, p, y, nullptr, 0, false, false, stream);
+}
+
+gq_status gq_w4a16_gemm_workspace_size(int64_t M, int64_t K, int64_t N, gq_qparams p,
+                                       size_t* bytes) {
+  if (!bytes) return GQ_ERR_INVALID_ARG;
+  *bytes = 0;
+  if (gq_status s = matmul_params(M, K, N, p)) return s;
+  if (gq_status s = check_gemm(M, K, N)) return s;
   if (M == 0 || N == 0) return GQ_OK;
-  if (!gq::gemv_f16_supported((int)M, K, N, p.group_size)) return GQ_ERR_UNSUPPORTED;
-  hipStream_t s = (hipStream_t)stream;
-  if (gq_status st = check_device(s)) return st;
-  return from_hip(gq::launch_w4a16_gemv_f16(x, (int)M, K, qweight, scales, zeros, N, p.group_size,
-                                            p.symmetric, y, s));
+  probe_device();
+  *bytes = gq::gemm_workspace_bytes(M, K, N, p.group_size);
+  return GQ_OK;
+}
+
+gq_status gq_w4a16_gemm_ws(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                           const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                           gq_qparams p, uint16_t* y, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return gemm_call(x, M, K, qweight, scales, zeros, N, p, y, workspace, workspace_bytes, true, false,
+                   stream);
 }
 
 gq_status gq_w4a16_gemm_f16(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
                             const uint16_t* scales, const uint16_t* zeros, int64_t N,
                             gq_qparams p, uint16_t* y, void* stream) {
-  if (gq_status s = check_w4_matmul(x, M, K, qweight, scales, zeros, N, p, y)) return s;
-  if (K > kMaxGemmK || M > kMaxDim / 2) return GQ_ERR_UNSUPPORTED;
-  if (((M + 255) / 256) * ((N + 255) / 256) > INT32_MAX / 2) return GQ_ERR_UNSUPPORTED;
-  if (M == 0 || N == 0) return GQ_OK;
-  if (!gq::gemm_f16_supported(K, p.group_size)) return GQ_ERR_UNSUPPORTED;
-  hipStream_t s = (hipStream_t)stream;
-  if (gq_status st = check_device(s)) return st;
-  return from_hip(gq::launch_w4a16_gemm_f16(x, M, K, qweight, scales, zeros, N, p.group_size,
-                                            p.symmetric, y, s));
+  return gemm_call(x, M, K, qweight, scales, zeros, N, p, y, nullptr, 0, false, true, stream);
+}
+
+gq_status gq_w4a16_gemm_f16_ws(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                               const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                               gq_qparams p, uint16_t* y, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return gemm_call(x, M, K, qweight, scales, zeros, N, p, y, workspace, workspace_bytes, true, true,
+                   stream);
 }
 
 gq_status gq_q4k_quantize(const void* w, gq_dtype w_dtype, int64_t N, int64_t K, uint8_t* blocks,

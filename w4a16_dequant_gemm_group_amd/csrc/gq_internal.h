@@ -92,15 +92,10 @@ __device__ __forceinline__ double load_elem_f64(const void* p, int64_t i, gq_dty
 // Compute units of the current device (set by the C ABI's device check).
 int num_cus();
 
-// Library scratch per (device, stream, slot); nullptr while s is being captured.
-// The first zero_bytes of a newly allocated buffer are cleared on s; a reused
-// buffer keeps what the last user left.  Words that must be zero at every
-// launch (the split GEMM's per-tile counters and flags, the small-batch
-// GEMV's per-row-group counters) get a slot of their
-// own that nothing else writes, cleared whole when allocated and reset by the
-// launch that used them.
-enum { kScratchGemv = 0, kScratchGemm = 1, kScratchGemmSync = 2, kScratchGemvSync = 3 };
-void* stream_scratch(int slot, size_t bytes, size_t zero_bytes, hipStream_t s);
+// A 64-bit id unique to each launch that needs one (odd, never 0), random
+// per process: kernels that hand partial sums between workgroups through
+// caller memory of unknown content tell this launch's words from stale ones by it.
+uint64_t next_launch_id();
 
 // ---------------------------------------------------------------------------
 // Launchers (arguments already validated by the C ABI layer)
@@ -117,12 +112,13 @@ hipError_t launch_dequantize(const uint8_t* qweight, const uint16_t* scales,
 hipError_t launch_ingest_group_major(const int8_t* codes, const uint16_t* scales, int64_t ng,
                                      int64_t group, int64_t N, uint8_t* qweight,
                                      uint16_t* scales_out, hipStream_t s);
-// workspace: caller scratch of ws_bytes (>= gemv_workspace_bytes), or NULL to
-// use the library's per-stream scratch for the matrix-core path.
+// The fused GEMV (1 <= M <= 16).  workspace: caller scratch of at least
+// gemv_workspace_bytes(...) bytes for the split-K matrix-core kernel, or NULL
+// (the call then runs a kernel that needs none).  xf16: fp16 activations and
+// output instead of bf16.
 hipError_t launch_w4a16_gemv(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
                              const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
-                             int symmetric, uint16_t* y, void* workspace, size_t ws_bytes,
-                             hipStream_t s);
+                             int symmetric, uint16_t* y, void* workspace, bool xf16, hipStream_t s);
 // Whether the persistent streaming GEMV (M = 1..4, no scratch) takes M rows at this K.
 bool gemv_stream_supported(int M, int64_t K);
 // Small-batch GEMV on the matrix cores with every activation row in LDS and K
@@ -132,30 +128,22 @@ hipError_t launch_w4a16_gemv_mfma_stream(const uint16_t* x, int M, int64_t K, co
                                          const uint16_t* scales, const uint16_t* zeros, int64_t N,
                                          int G, int symmetric, uint16_t* y, hipStream_t s,
                                          bool xf16 = false);
-// Small-batch GEMV on the matrix cores (4 <= M <= 16, split along K).  Sets
-// *launched = false without launching when it cannot run this call (no split
-// workspace while the stream is being captured); the caller then uses the
-// dot-product kernel.
+// Small-batch GEMV on the matrix cores split along K (4 <= M <= 16), partial
+// sums per 1024-wide slice in `workspace`, added by a second kernel.
 bool gemv_mfma_supported(int M, int64_t K, int64_t N, int G);
-// Scratch the GEMV needs for these arguments (0 unless the matrix-core path runs).
+// Scratch the GEMV can use for these arguments (0: no kernel would use any).
 size_t gemv_workspace_bytes(int M, int64_t K, int64_t N, int G);
 hipError_t launch_w4a16_gemv_mfma(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
                                   const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
-                                  int symmetric, uint16_t* y, void* workspace, hipStream_t s,
-                                  bool* launched);
+                                  int symmetric, uint16_t* y, void* workspace, bool xf16,
+                                  hipStream_t s);
+// The fused GEMM.  workspace: caller scratch of at least gemm_workspace_bytes
+// bytes for splitting K over two workgroups per tile in a round that fills at
+// most half of the GPU, or NULL (no split).  xf16 as for the GEMV.
+size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, int G);
 hipError_t launch_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
                              const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
-                             int symmetric, uint16_t* y, hipStream_t s);
-// fp16 activations and output: the M = 1 streaming GEMV and the 256 x 256 GEMM
-// kernel (K % 64 == 0, G = 64, 128 or a multiple of 256).
-bool gemv_f16_supported(int M, int64_t K, int64_t N, int G);
-hipError_t launch_w4a16_gemv_f16(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
-                                 const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
-                                 int symmetric, uint16_t* y, hipStream_t s);
-bool gemm_f16_supported(int64_t K, int G);
-hipError_t launch_w4a16_gemm_f16(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
-                                 const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
-                                 int symmetric, uint16_t* y, hipStream_t s);
+                             int symmetric, uint16_t* y, void* workspace, bool xf16, hipStream_t s);
 hipError_t launch_q4k_quantize(const void* w, gq_dtype dt, int64_t N, int64_t K, uint8_t* blocks,
                                hipStream_t s);
 hipError_t launch_q4k_gemv(const uint16_t* x, int M, int64_t K, const uint8_t* blocks, int64_t N,
