@@ -59,6 +59,7 @@
 #ifndef GQ_H_
 #define GQ_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -226,6 +227,29 @@ gq_status gq_w4a16_gemm_ws(const uint16_t* x, int64_t M, int64_t K, const uint8_
                            const uint16_t* scales, const uint16_t* zeros, int64_t N,
                            gq_qparams p, uint16_t* y, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* Bytes of the fixed device scratch behind gq_w4a16_gemm_noalloc: the split
+ * of the last round on a GPU of up to 256 compute units (at most 128 split
+ * tiles: 2048 bytes of handshake words and 128 partial tiles of 262144 bytes),
+ * rounded up to 32 MiB + 4 KiB. */
+#define GQ_NOALLOC_SCRATCH_BYTES ((size_t)(32u << 20) + 4096u)
+
+/* gq_w4a16_gemm for callers that cannot allocate device memory (code under
+ * stream capture, tight serving loops, harnesses that forbid allocation): the
+ * same kernels and result as gq_w4a16_gemm_ws, with the split scratch taken
+ * from a fixed array of GQ_NOALLOC_SCRATCH_BYTES in device memory that the
+ * library holds per GPU until the process ends (its address is looked up once
+ * per device, on the first call there).  The call allocates nothing.  Every
+ * call on a GPU shares that GPU's array: calls whose kernels may overlap on
+ * one GPU (different streams, concurrent graph replays) race and must not be
+ * made.  The array keeps the last call's content; nothing in it needs to be
+ * zero (the handshake tells stale words from this call's).  Errors: those of
+ * gq_w4a16_gemm; UNSUPPORTED when the split would need more than
+ * GQ_NOALLOC_SCRATCH_BYTES (not on a 256-CU gfx950); HIP when the array's
+ * address cannot be looked up. */
+gq_status gq_w4a16_gemm_noalloc(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                                const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                                gq_qparams p, uint16_t* y, void* stream);
 
 /* The fused matmuls with fp16 activations and fp16 output [P1 sec.2: the
  * fused kernel multiplies BF16/FP16 activations]: the same product as

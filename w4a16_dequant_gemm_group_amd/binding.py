@@ -26,7 +26,7 @@ GQ_F32, GQ_F16, GQ_BF16 = 0, 1, 2
 EXPORTS = (
     "gq_status_str", "gq_version", "gq_packed_sizes", "gq_quantize_groups", "gq_pack_int4",
     "gq_dequantize", "gq_w4a16_gemv", "gq_w4a16_gemv_workspace_size", "gq_w4a16_gemv_ws",
-    "gq_w4a16_gemm", "gq_w4a16_gemm_workspace_size", "gq_w4a16_gemm_ws",
+    "gq_w4a16_gemm", "gq_w4a16_gemm_workspace_size", "gq_w4a16_gemm_ws", "gq_w4a16_gemm_noalloc",
     "gq_q4k_quantize", "gq_q4k_gemv", "gq_ingest_group_major",
     "gq_w4a16_gemv_f16", "gq_w4a16_gemv_f16_ws", "gq_w4a16_gemm_f16", "gq_w4a16_gemm_f16_ws",
 )
@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
         "gq_w4a16_gemm": mm,
         "gq_w4a16_gemm_workspace_size": [i64, i64, i64, Q, ctypes.POINTER(sz)],
         "gq_w4a16_gemm_ws": mm_ws,
+        "gq_w4a16_gemm_noalloc": mm,
         "gq_q4k_quantize": [p, c, i64, i64, p, p],
         "gq_q4k_gemv": [p, i64, i64, p, i64, p, p],
         "gq_bf16_gemv": [p, i64, i64, p, i64, p, p],
@@ -367,6 +368,14 @@ def gq_w4a16_plain(name: str, x, qweight, scales, zeros, group_size: int = 128,
     _ok(getattr(lib(), name)(_ptr(x), M, K, _ptr(qweight), _ptr(scales), _ptr(zeros), N,
                              qparams(4, group_size, symmetric), _ptr(y), _stream(stream)), name)
     return y
+
+
+def gq_w4a16_gemm_noalloc(x, qweight, scales, zeros, group_size: int = 128, symmetric: bool = False,
+                          y=None, stream=None):
+    """gq_w4a16_gemm with its split scratch in the library's fixed device array
+    (no allocation by the call; calls that overlap on one GPU race)."""
+    return gq_w4a16_plain("gq_w4a16_gemm_noalloc", x, qweight, scales, zeros, group_size, symmetric,
+                          y, stream)
 
 
 def gq_q4k_quantize(w: torch.Tensor, blocks=None, stream=None):

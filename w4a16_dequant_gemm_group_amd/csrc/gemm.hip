@@ -50,6 +50,7 @@
 // In both, workgroups are dealt round-robin to the 8 XCDs with the M tile
 // varying fastest, so each XCD keeps the same activation rows in its L2.
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 #include <type_traits>
 
@@ -829,6 +830,33 @@ hipError_t dispatch(const uint16_t* x, int M, int K, const uint8_t* qw, const ui
 }
 
 }  // namespace
+
+// Scratch of gq_w4a16_gemm_noalloc: a fixed array in device memory, one per
+// GPU (each device's copy at its own address), held until the process ends.
+// It holds the split handshake words and partial sums of one call at a time;
+// nothing in it needs to start at zero (the handshake tells stale words from
+// this call's by the launch id).  Host code uses the per-device address from
+// hipGetSymbolAddress, never the array's name.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+void* noalloc_scratch(hipError_t* err) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<void*> addr[kMaxDev];
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDev) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
 
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, int G) {
   if (lds_mode((int)K, G) < 0) return 0;

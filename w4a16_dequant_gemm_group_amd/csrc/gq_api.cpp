@@ -307,6 +307,27 @@ gq_status gq_w4a16_gemm_ws(const uint16_t* x, int64_t M, int64_t K, const uint8_
                    stream);
 }
 
+gq_status gq_w4a16_gemm_noalloc(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
+                                const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                                gq_qparams p, uint16_t* y, void* stream) {
+  if (gq_status s = check_w4_matmul(x, M, K, qweight, scales, zeros, N, p, y)) return s;
+  if (gq_status s = check_gemm(M, K, N)) return s;
+  if (M == 0 || N == 0) return GQ_OK;
+  probe_device();  // the split depends on the device's compute-unit count
+  const size_t need = gq::gemm_workspace_bytes(M, K, N, p.group_size);
+  if (need > GQ_NOALLOC_SCRATCH_BYTES) return GQ_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  if (gq_status st = check_device(s)) return st;
+  void* ws = nullptr;
+  if (need > 0) {
+    hipError_t e = hipSuccess;
+    ws = gq::noalloc_scratch(&e);
+    if (!ws) return GQ_ERR_HIP;
+  }
+  return from_hip(gq::launch_w4a16_gemm(x, M, K, qweight, scales, zeros, N, p.group_size,
+                                        p.symmetric, y, ws, false, s));
+}
+
 gq_status gq_w4a16_gemm_f16(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
                             const uint16_t* scales, const uint16_t* zeros, int64_t N,
                             gq_qparams p, uint16_t* y, void* stream) {

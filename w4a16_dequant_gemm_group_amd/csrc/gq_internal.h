@@ -141,6 +141,11 @@ hipError_t launch_w4a16_gemv_mfma(const uint16_t* x, int M, int64_t K, const uin
 // bytes for splitting K over two workgroups per tile in a round that fills at
 // most half of the GPU, or NULL (no split).  xf16 as for the GEMV.
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, int G);
+// The fixed device scratch of gq_w4a16_gemm_noalloc (GQ_NOALLOC_SCRATCH_BYTES,
+// enough for the split of any 256-CU round): its address on the current
+// device, looked up once per device; nullptr with *err set on failure.
+constexpr size_t kNoAllocScratchBytes = GQ_NOALLOC_SCRATCH_BYTES;
+void* noalloc_scratch(hipError_t* err);
 hipError_t launch_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const uint8_t* qweight,
                              const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
                              int symmetric, uint16_t* y, void* workspace, bool xf16, hipStream_t s);
