@@ -320,6 +320,13 @@ def main():
                 # time of pure reads of the same byte counts over the time of the GEMVs
                 "frac_of_same_size_reads": round(sum(ceiling["per_shape_us"].values())
                                                  / (ms_per_step * 1e3), 4)}
+    # per projection (each in its own graph): its rate against the 8 TB/s peak,
+    # and the time a plain read of its byte count takes over its GEMV time
+    roofline["per_shape"] = {
+        nm: {"us": round(per_us[nm], 3), "frac": round(per_gbps[nm] / HBM_PEAK_GBPS, 4),
+             "same_size_read_us": ceiling["per_shape_us"][nm],
+             "frac_of_same_size_read": round(ceiling["per_shape_us"][nm] / per_us[nm], 4)}
+        for nm, _, _ in shapes}
     if tr is not None:
         roofline["traffic_per_shape"] = {k: round(v) for k, v in tr["hbm_bytes_per_launch"].items()}
 
