@@ -655,22 +655,42 @@ def run_extras(torch, B, synth, to_dev, dev, stream, shapes, W, X, gate, fused_s
     ex["small_batch_sym_g32"] = sb
     log(f"small batch {sb}")
 
-    # ---- super-block format GEMV, rotating copies -------------------------------------
+    # ---- super-block format GEMV, M = 1, 2, 4, rotating copies ---------------------------
+    from oracle import gq_oracle as O
+
+    def bits16(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
     q4 = {}
     for name in ("down", "gate_up"):
         n, k = synth.LLAMA3_8B_SHAPES[name]
-        w, x = synth.q4k_case(name)
+        w, _ = synth.q4k_case(name)
         blocks = B.gq_q4k_quantize(to_dev(w))
+        # parity gate: 256 sampled rows' blocks equal the oracle's bytes and the
+        # GEMV on them meets the parity bar, at every M timed below
+        rows = np.sort(np.random.default_rng(1).choice(n, 256, replace=False))
+        bref = O.q4k_encode(O.q4k_quantize(O.bf16_to_f64(w[rows])))
+        if not np.array_equal(blocks.cpu().numpy()[rows], bref):
+            raise SystemExit(f"parity gate: super-block bytes of {name} differ from the oracle")
+        wh = O.q4k_dequantize_fields(O.q4k_decode(bref))
         reps = max(2, int(np.ceil(2 ** 30 / blocks.numel())))
         bl = [blocks] + [blocks.clone() for _ in range(reps - 1)]
-        xd = to_dev(x)
-        y = torch.empty((1, n), dtype=torch.bfloat16, device=dev)
-        B.gq_q4k_gemv(xd, bl[0], y=y)
-        us = graph_time(torch, stream, lambda i: B.gq_q4k_gemv(xd, bl[i % reps], y=y), 4 * reps)
-        byt = 144 * n * k // 256 + 2 * k + 2 * n
-        q4[name] = {"us": round(us, 3), "GB/s": round(byt / (us * 1e-6) / 1e9, 1)}
+        for m in (1, 2, 4):
+            _, x = synth.q4k_case(name, m)
+            xd = to_dev(x)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            B.gq_q4k_gemv(xd, bl[0], y=y)
+            ref = O.q4k_reference(x, bref)
+            ok, rel, ratio = O.within_parity(O.bf16_to_f64(bits16(y))[:, rows], ref, O.bf16_to_f64(x), wh)
+            if not ok:
+                raise SystemExit(f"parity gate: super-block {name} M={m} relF {rel:.2e} max/allowed {ratio:.2f}")
+            us = graph_time(torch, stream, lambda i: B.gq_q4k_gemv(xd, bl[i % reps], y=y), 4 * reps)
+            byt = 144 * n * k // 256 + 2 * m * k + 2 * m * n
+            q4[name if m == 1 else f"{name}_M{m}"] = {"us": round(us, 3), "GB/s": round(byt / (us * 1e-6) / 1e9, 1)}
         del bl, blocks
-    ex["q4k_gemv_m1"] = q4
+    ex["q4k_gemv_m1"] = {k_: v for k_, v in q4.items() if "_M" not in k_}
+    ex["q4k_gemv_small_batch"] = {k_: v for k_, v in q4.items() if "_M" in k_}
+    log(f"super-block GEMV {q4}")
     return ex
 
 

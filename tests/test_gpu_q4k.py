@@ -39,12 +39,16 @@ def test_quantize_other_dtypes(dtype):
     assert np.array_equal(blocks.cpu().numpy(), ref)
 
 
-@pytest.mark.parametrize("M", [1, 2, 4, 16])
-@pytest.mark.parametrize("N,K", [(77, 2304), (64, 256), (33, 18432), (1031, 4096), (1031, 10496), (37, 28672)])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 16])
+@pytest.mark.parametrize("N,K", [(77, 2304), (64, 256), (33, 18432), (1031, 4096), (1031, 10496),
+                                 (37, 28672), (129, 73728)])
 def test_gemv_small(M, N, K):
-    """M = 1 with K up to 26624 takes the streaming kernel (ragged last step at
-    2304 and 256, a second x staging pass at 18432, several row pairs per wave
-    at 1031 rows); 28672 and M > 1 take the per-workgroup kernel."""
+    """M = 1..4 take the streaming kernel while every activation row fits one
+    compute unit's LDS (4352 bytes per row and 2048-step): a ragged last step at
+    2304 and 256, several row pairs per wave at 1031 rows, one workgroup per
+    compute unit from four steps on, x staged in more than one pass at M = 1
+    with 28672 and 73728 (36 steps) and at M = 2..4 with 18432 and beyond; M = 2
+    at 73728, M = 3, 4 from 28672 on and M = 16 take the per-workgroup kernel."""
     w, x = synth.small(N, K, M, seed=N + M)
     blocks = O.q4k_encode(O.q4k_quantize(O.bf16_to_f64(w)))
     y = B.gq_q4k_gemv(bf16_dev(x), u8_dev(blocks))
@@ -55,17 +59,19 @@ def test_gemv_small(M, N, K):
 
 
 @pytest.mark.parametrize("name", ["down", "gate_up"])
-def test_full_size(name):
-    """Full-size super-block quantize + GEMV at M = 1: every block's 144 bytes
-    and every output row against the oracle, in row chunks."""
-    w, x = synth.q4k_case(name)
-    announce(f"q4k {name} {w.shape} M=1, all rows")
+@pytest.mark.parametrize("M", [1, 4])
+def test_full_size(name, M):
+    """Full-size super-block quantize + GEMV at M = 1 and 4 (the streaming
+    kernel): every block's 144 bytes and every output row against the oracle,
+    in row chunks."""
+    w, x = synth.q4k_case(name, M)
+    announce(f"q4k {name} {w.shape} M={M}, all rows")
     blocks = B.gq_q4k_quantize(bf16_dev(w))
     y = B.gq_q4k_gemv(bf16_dev(x), blocks)
     torch.cuda.synchronize()
     got = blocks.cpu().numpy()
     N = w.shape[0]
-    ref = np.empty((1, N))
+    ref = np.empty((M, N))
     wmax = 0.0
     for r0 in range(0, N, 2048):
         r1 = min(N, r0 + 2048)
@@ -75,4 +81,4 @@ def test_full_size(name):
         wmax = max(wmax, float(np.abs(wh).max()))
         ref[:, r0:r1] = O.matmul_groupwise(O.bf16_to_f64(x), wh, O.Q4K_SUB)
     assert_parity(bits16(y), ref, O.bf16_to_f64(x), np.array([[wmax]]),
-                  f"q4k {name} {w.shape} M=1 full, all rows")
+                  f"q4k {name} {w.shape} M={M} full, all rows")

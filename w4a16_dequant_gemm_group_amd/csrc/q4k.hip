@@ -11,9 +11,10 @@
 // The GEMVs use the layout of the plain INT4 GEMV: lane l of a wave owns the
 // 32 weights at k = 2048 t + 32 l, which here is sub-block l%8 of block
 // 8t + l/8; it loads the block's 16-byte header (the eight lanes of one block
-// share one address) and its 16 nibble bytes, both as dwordx4.  M = 1 with x
-// in LDS (K <= 26624) runs the persistent streaming kernel of the INT4 GEMV;
-// other M and longer K run a per-workgroup kernel that stages x in k chunks.
+// share one address) and its 16 nibble bytes, both as dwordx4.  M = 1..4 with
+// every activation row in one compute unit's LDS run the persistent streaming
+// kernel of the INT4 GEMV; larger M and longer K run a per-workgroup kernel
+// that stages x in k chunks.
 #include <algorithm>
 
 #include "gq_internal.h"
@@ -212,31 +213,39 @@ __global__ __launch_bounds__(kThreads) void q4k_gemv_kernel(const uint16_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// M = 1: the streaming structure of the packed INT4 GEMV.  Persistent
-// workgroups stage x once (permuted pairs + chunk sums) and each wave walks
-// (row pair, 2048-wide k step) items with three register buffers, two items'
-// loads in flight.  Lane l loads, per row, the 16-byte header of block 8t + l/8
-// and the 16 nibble bytes of its sub-block l % 8 with raw buffer loads (the
-// header address is shared by 8 lanes); lanes past K and rows past N read zero
-// from the range check.
+// M = 1..4: the streaming structure of the packed INT4 GEMV.  Persistent
+// workgroups stage every activation row once (permuted pairs + chunk sums) and
+// each wave walks (row pair, 2048-wide k step) items with three register
+// buffers, two items' loads in flight.  Lane l loads, per row, the 16-byte
+// header of block 8t + l/8 and the 16 nibble bytes of its sub-block l % 8 with
+// raw buffer loads (the header address is shared by 8 lanes); lanes past K and
+// rows past N read zero from the range check.  With MT > 1 activation rows
+// each nibble word is unpacked once and multiplied against every row.
 // ---------------------------------------------------------------------------
 constexpr int kQRpw = 2;    // rows per item
 constexpr int kQNbuf = 3;   // register buffers
-constexpr int kQMaxT = 13;  // 2048-steps of x in LDS
+constexpr int kQMaxM = 4;   // activation rows the streaming kernel takes
+constexpr size_t kQLdsTwo = 80 * 1024;   // LDS of each of two workgroups per compute unit
+constexpr size_t kQLdsOne = 156 * 1024;  // LDS of one workgroup per compute unit
+
+// LDS bytes of the streaming kernel: per activation row and 2048-step 4 KiB of
+// permuted pairs and 64 chunk sums.
+size_t q4k_stream_lds(int M, int64_t K) { return (size_t)M * (size_t)((K + kStepK - 1) / kStepK) * (256 * 16 + 64 * 4); }
 
 struct QBuf {
   uint4 h[kQRpw], w[kQRpw];
 };
 
-template <int NT>
+// x [MT, K]; y row m at y + m * ldy.
+template <int NT, int MT>
 __global__ __launch_bounds__(NT) void q4k_stream_kernel(const uint16_t* __restrict__ x, int K,
                                                               const uint8_t* __restrict__ blocks,
-                                                              int N, uint16_t* __restrict__ y) {
+                                                              int N, uint16_t* __restrict__ y, int ldy) {
   namespace su = stream_util;
   extern __shared__ uint4 lds[];
   const int T = (K + kStepK - 1) / kStepK;
-  uint4* xs = lds;                      // [T][4][64] permuted x pairs
-  float* sxs = (float*)(xs + T * 256);  // [T * 64] chunk sums
+  uint4* xs = lds;                           // [MT][T][4][64] permuted x pairs
+  float* sxs = (float*)(xs + MT * T * 256);  // [MT][T * 64] chunk sums
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nb = (N + kQRpw - 1) / kQRpw;
@@ -263,17 +272,24 @@ __global__ __launch_bounds__(NT) void q4k_stream_kernel(const uint16_t* __restri
     }
   };
 
-  // x: first loads before the weight prefetch, staged after it
+  // x: first loads before the weight prefetch, staged after it.  Flat chunk
+  // f = m T 256 + c holds x[m, 8c .. 8c + 8).
   constexpr int kXr = 8;
+  const int TC = T * 256;  // chunks per activation row
   uint4 xv[kXr];
 #pragma unroll
   for (int i = 0; i < kXr; ++i) {
-    const int c = threadIdx.x + NT * i;
+    const int f = threadIdx.x + NT * i;
+    const int m = MT == 1 ? 0 : f / TC, c = f - m * TC;
     xv[i] = make_uint4(0, 0, 0, 0);
-    if (c < T * 256 && c * 8 < K) xv[i] = *(const uint4*)(x + c * 8);
+    if (f < MT * TC && c * 8 < K) xv[i] = *(const uint4*)(x + (size_t)m * K + c * 8);
   }
   QBuf buf[kQNbuf];
-  float acc[kQRpw] = {0.f, 0.f};
+  float acc[MT][kQRpw];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int r = 0; r < kQRpw; ++r) acc[m][r] = 0.f;
   int lb = (int)blockIdx.x * NW + wave, lt = 0;  // next item to load
   int cb = lb, ct = 0;                               // next item to compute
   auto advance = [&](int& b, int& t) {
@@ -288,30 +304,50 @@ __global__ __launch_bounds__(NT) void q4k_stream_kernel(const uint16_t* __restri
     __builtin_amdgcn_sched_barrier(0);  // keep the loads in item order: the loop's waits assume it
     advance(lb, lt);
   }
-  for (int c0 = 0; c0 < T * 256; c0 += kXr * NT) {
+  for (int c0 = 0; c0 < MT * TC; c0 += kXr * NT) {
 #pragma unroll
     for (int i = 0; i < kXr; ++i) {
-      const int c = c0 + threadIdx.x + NT * i;
+      const int f = c0 + threadIdx.x + NT * i;
+      const int m = MT == 1 ? 0 : f / TC, c = f - m * TC;
       // every load issued here is consumed here: a load left in flight on
       // some path would make the main loop wait for all loads at its head
-      if (c < T * 256) {  // uniform over each wave (T * 256 is a multiple of 64)
+      if (f < MT * TC) {  // uniform over each wave (T * 256 is a multiple of 64)
         uint4 v = xv[i];
         if (c0 > 0) {
           v = make_uint4(0, 0, 0, 0);
-          if (c * 8 < K) v = *(const uint4*)(x + c * 8);
+          if (c * 8 < K) v = *(const uint4*)(x + (size_t)m * K + c * 8);
         }
-        xs[(c & ~255) | ((c & 3) << 6) | ((c >> 2) & 63)] = su::perm_x_pairs(v);
+        // lane l of step p reads its four chunks at p*256 + j*64 + l
+        xs[m * TC + ((c & ~255) | ((c & 3) << 6) | ((c >> 2) & 63))] = su::perm_x_pairs(v);
         float sm = su::sum_bf16x8(v);
         sm += __shfl_xor(sm, 1, 64);
         sm += __shfl_xor(sm, 2, 64);
-        if ((c & 3) == 0) sxs[c >> 2] = sm;
+        if ((c & 3) == 0) sxs[m * T * 64 + (c >> 2)] = sm;
       }
     }
   }
   __syncthreads();
 
+  // the sub-block scale S = d sc and min Mn = dmin mn of row r's header
+  auto fields = [&](const uint4& h, float& S, float& Mn) {
+    const float d = f16_to_f32((uint16_t)(h.x & 0xFFFFu));
+    const float dmin = f16_to_f32((uint16_t)(h.x >> 16));
+    // 6-bit fields by 32-bit funnel shifts: the scale sits at bit 6 sub of
+    // {h.w : h.z : h.y}, the min at bit 6 sub + 48; each lane picks the two
+    // dwords holding its field
+    const uint32_t sc6 = __builtin_amdgcn_alignbit(shi ? h.w : h.z, shi ? h.z : h.y, o6 & 31u) & 63u;
+    const uint32_t mn6 = __builtin_amdgcn_alignbit(h.w, mhi ? h.w : h.z, (o6 + 16u) & 31u) & 63u;
+    S = d * (float)sc6;
+    Mn = dmin * (float)mn6;
+  };
   auto compute = [&](const QBuf& B, int b, int t) {
-    if (t == 0) acc[0] = acc[1] = 0.f;
+    if (t == 0) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int r = 0; r < kQRpw; ++r) acc[m][r] = 0.f;
+    }
+    if constexpr (MT == 1) {
     const uint4* xp = xs + t * 256 + lane;
     const uint4 x0 = xp[0], x1 = xp[64], x2 = xp[128], x3 = xp[192];
     const float sx = sxs[t * 64 + lane];
@@ -332,14 +368,66 @@ __global__ __launch_bounds__(NT) void q4k_stream_kernel(const uint16_t* __restri
       const uint32_t mn6 = __builtin_amdgcn_alignbit(h.w, mhi ? h.w : h.z, (o6 + 16u) & 31u) & 63u;
       const float S = d * (float)sc6;
       const float Mn = dmin * (float)mn6;
-      acc[r] = fmaf(S, a, fmaf(-Mn, sx, acc[r]));
+      acc[0][r] = fmaf(S, a, fmaf(-Mn, sx, acc[0][r]));
+    }
+    } else {
+      // activation row m: permuted pairs at xs[m T 256 ..], chunk sums at sxs[m T 64 ..]
+      uint4 xq[MT][4];
+      float sx[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const uint4* xp = xs + (m * T + t) * 256 + lane;
+        xq[m][0] = xp[0];
+        xq[m][1] = xp[64];
+        xq[m][2] = xp[128];
+        xq[m][3] = xp[192];
+        sx[m] = sxs[(m * T + t) * 64 + lane];
+      }
+#pragma unroll
+      for (int r = 0; r < kQRpw; ++r) {
+        const uint4 u0 = su::unpack8_words(B.w[r].x, 0x43004300u);
+        const uint4 u1 = su::unpack8_words(B.w[r].y, 0x43004300u);
+        const uint4 u2 = su::unpack8_words(B.w[r].z, 0x43004300u);
+        const uint4 u3 = su::unpack8_words(B.w[r].w, 0x43004300u);
+        float S, Mn;
+        fields(B.h[r], S, Mn);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          float a = su::dot8_words(u0, xq[m][0], -128.f * sx[m]);
+          a = su::dot8_words(u1, xq[m][1], a);
+          a = su::dot8_words(u2, xq[m][2], a);
+          a = su::dot8_words(u3, xq[m][3], a);
+          acc[m][r] = fmaf(S, a, fmaf(-Mn, sx[m], acc[m][r]));
+        }
+      }
     }
     if (t == T - 1) {
-      // both rows' sums together: row 0's in lane 31, row 1's in lane 63
       static_assert(kQRpw == 2, "the paired reduction takes two rows");
-      const float v = su::wave_sums_pair(acc[0], acc[1]);
-      const int row = b * kQRpw + (lane >> 5);
-      if ((lane & 31) == 31 && row < N) y[row] = f32_to_bf16_rne(v);
+      if constexpr (MT == 1) {
+        // both rows' sums together: row 0's in lane 31, row 1's in lane 63
+        const float v = su::wave_sums_pair(acc[0][0], acc[0][1]);
+        const int row = b * kQRpw + (lane >> 5);
+        if ((lane & 31) == 31 && row < N) y[row] = f32_to_bf16_rne(v);
+      } else {
+        // all (m, r) sums together, four per register (padded with zeros); the
+        // last lane of each 16-lane row stores the one its row holds
+        constexpr int V = MT * kQRpw;
+        constexpr int VP = V <= 4 ? 4 : 8;
+        float v[VP], u[VP / 4];
+#pragma unroll
+        for (int i = 0; i < VP; ++i) v[i] = i < V ? acc[i / kQRpw][i % kQRpw] : 0.f;
+        su::wave_sums_by_row<VP>(v, u);
+        const int q = lane >> 4;
+        const int qi = (q & 1) * 2 + (q >> 1);
+        if ((lane & 15) == 15) {
+#pragma unroll
+          for (int j = 0; j < VP / 4; ++j) {
+            const int idx = 4 * j + qi;
+            const int m = idx / kQRpw, row = b * kQRpw + idx % kQRpw;
+            if (idx < V && row < N) y[(size_t)m * ldy + row] = f32_to_bf16_rne(u[j]);
+          }
+        }
+      }
     }
   };
   // Whole buffer rounds in the loop, the last 0-2 items (already loaded) after
@@ -386,33 +474,46 @@ hipError_t launch_q4k_quantize(const void* w, gq_dtype dt, int64_t N, int64_t K,
   return hipGetLastError();
 }
 
+template <int MT>
+hipError_t q4k_stream(const uint16_t* x, int K, const uint8_t* blocks, int N, uint16_t* y, hipStream_t s) {
+  const int steps = (K + kStepK - 1) / kStepK;
+  // rows per launch so that every byte offset fits 32 bits
+  const uint64_t row_bytes = (uint64_t)(K / 256) * kBlockBytes;
+  const int64_t cap = (int64_t)(((uint64_t)1 << 31) / row_bytes);
+  const size_t lds = q4k_stream_lds(MT, K);
+  for (int64_t n0 = 0; n0 < N; n0 += cap) {
+    const int nn = (int)std::min<int64_t>(cap, N - n0);
+    const int nb = (nn + kQRpw - 1) / kQRpw;
+    // one workgroup of 8 waves per compute unit once K spans four or more
+    // 2048-steps or x needs more than two workgroups' LDS (x staged once per
+    // compute unit), else two of 4 waves
+    if (steps >= 4 || lds > kQLdsTwo) {
+      const int grid = std::max(1, std::min((nb + 7) / 8, num_cus()));
+      hipLaunchKernelGGL((q4k_stream_kernel<512, MT>), dim3(grid), dim3(512), lds, s, x, K,
+                         blocks + n0 * row_bytes, nn, y + n0, N);
+    } else {
+      const int grid = std::max(1, std::min((nb + kWaves - 1) / kWaves, 2 * num_cus()));
+      hipLaunchKernelGGL((q4k_stream_kernel<kThreads, MT>), dim3(grid), dim3(kThreads), lds, s, x, K,
+                         blocks + n0 * row_bytes, nn, y + n0, N);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_q4k_gemv(const uint16_t* x, int M, int64_t K, const uint8_t* blocks, int64_t N,
                            uint16_t* y, hipStream_t s) {
   const int steps = (int)((K + kStepK - 1) / kStepK);
   const int k = (int)K, n = (int)N;
-  if (M == 1 && steps <= kQMaxT) {
-    // rows per launch so that every byte offset fits 32 bits
-    const uint64_t row_bytes = (uint64_t)(K / 256) * kBlockBytes;
-    const int64_t cap = (int64_t)(((uint64_t)1 << 31) / row_bytes);
-    const size_t lds = (size_t)steps * (256 * 16 + 64 * 4);
-    for (int64_t n0 = 0; n0 < N; n0 += cap) {
-      const int nn = (int)std::min<int64_t>(cap, N - n0);
-      const int nb = (nn + kQRpw - 1) / kQRpw;
-      // one workgroup of 8 waves per compute unit once K spans four or more
-      // 2048-steps (x staged once per compute unit), else two of 4 waves
-      if (steps >= 4) {
-        const int grid = std::max(1, std::min((nb + 7) / 8, num_cus()));
-        hipLaunchKernelGGL(q4k_stream_kernel<512>, dim3(grid), dim3(512), lds, s, x, k,
-                           blocks + n0 * row_bytes, nn, y + n0);
-      } else {
-        const int grid = std::max(1, std::min((nb + kWaves - 1) / kWaves, 2 * num_cus()));
-        hipLaunchKernelGGL(q4k_stream_kernel<kThreads>, dim3(grid), dim3(kThreads), lds, s, x, k,
-                           blocks + n0 * row_bytes, nn, y + n0);
-      }
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
+  // the streaming kernel while every activation row fits one compute unit's LDS
+  if (M <= kQMaxM && q4k_stream_lds(M, K) <= kQLdsOne) {
+    switch (M) {
+      case 1: return q4k_stream<1>(x, k, blocks, n, y, s);
+      case 2: return q4k_stream<2>(x, k, blocks, n, y, s);
+      case 3: return q4k_stream<3>(x, k, blocks, n, y, s);
+      default: return q4k_stream<4>(x, k, blocks, n, y, s);
     }
-    return hipSuccess;
   }
   if (M == 1) {
     switch (steps) {
