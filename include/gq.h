@@ -160,7 +160,7 @@ gq_status gq_w4a16_gemv(const uint16_t* x, int64_t M, int64_t K, const uint8_t* 
 
 /* Scratch (bytes) that gq_w4a16_gemv_ws can use for these arguments; 0 when no
  * kernel for them would use any.  1 <= M <= 4 runs a streaming kernel that needs none
- * while x fits its LDS stage (K <= 26624, 34816, 22528, 16384 for M = 1, 2,
+ * while x fits its LDS stage (K <= 65536, 34816, 22528, 16384 for M = 1, 2,
  * 3, 4).  5 <= M <= 16 (and M = 4 beyond that K) runs a matrix-core kernel
  * that needs none either when the group size is 32, 64, 128, 256 or a
  * multiple of 512 and K is a multiple of 512: any such K for M <= 8 (x staged

@@ -64,9 +64,11 @@ def test_small_batch_matrix_core_shapes(M, sym, G):
     _run(x, qw, s, z, G, sym, f"[203,{K}] M={M} sym={sym} G={G} (matrix cores)")
 
 
-@pytest.mark.parametrize("K", [32, 96, 2048, 2080, 16384, 18432])
+@pytest.mark.parametrize("K", [32, 96, 2048, 2080, 16384, 18432, 40960, 65536, 67584])
 def test_k_extents(K):
-    # one lane's worth of k up to more than one LDS chunk (8 steps) of k
+    # one lane's worth of k up to more than one LDS chunk (8 steps) of k; at
+    # M = 1 the streaming kernel stages x in several passes up to K = 65536
+    # (32 steps) and the per-row kernel takes 67584
     w, x = synth.small(67, K, 1, seed=K)
     G = 32 if K % 128 else 128
     qw, s, z = _oracle_weights(w, G, False)

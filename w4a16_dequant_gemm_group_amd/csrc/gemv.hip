@@ -215,10 +215,9 @@ hipError_t dispatch(const uint16_t* x, int M, int K, const uint8_t* qw, const ui
 // ---------------------------------------------------------------------------
 
 constexpr int kSNbuf = 3;   // register buffers (items in flight + 1)
-constexpr int kSMaxT = 13;  // M = 1: 2048-steps of x that fit the LDS budget
 constexpr int kSMaxM = 4;   // activation rows the streaming kernel takes
-constexpr size_t kSLdsMulti = 80 * 1024;  // M > 1: LDS of two workgroups per compute unit
-constexpr size_t kSLdsOne = 156 * 1024;   // M > 1: LDS of one workgroup per compute unit
+constexpr size_t kSLdsMulti = 80 * 1024;  // LDS of each of two workgroups per compute unit
+constexpr size_t kSLdsOne = 156 * 1024;   // LDS of one workgroup per compute unit
 
 // LDS bytes of the streaming kernel: per activation row and 2048-step 4 KiB of
 // permuted pairs and 64 chunk sums; per step 512 B of offset tables (TAB).
@@ -557,8 +556,8 @@ hipError_t stream_any(const uint16_t* x, int M, int K, const uint8_t* qw, const 
 }  // namespace
 
 bool gemv_stream_supported(int M, int64_t K) {
-  if (M == 1) return (K + kStepK - 1) / kStepK <= kSMaxT;
-  return M >= 2 && M <= kSMaxM && stream_lds_bytes(M, K, true) <= kSLdsOne;
+  // every activation row (and the offset tables) in one compute unit's LDS
+  return M >= 1 && M <= kSMaxM && stream_lds_bytes(M, K, true) <= kSLdsOne;
 }
 
 // Kernel choice: the streaming kernel (M = 1..4 while x fits its LDS stage),
