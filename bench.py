@@ -98,7 +98,7 @@ def _counter_rows(d):
 def summarize_traffic(fetch_dir, write_dir):
     """Reduce the FETCH_SIZE and WRITE_SIZE passes of `--profile-pass` to
     per-launch HBM bytes of the GEMV, calibrated against the copy kernel."""
-    from w4a16_dequant_gemm_group_amd import synth
+    import synth
     shapes = [(nm,) + synth.LLAMA3_8B_SHAPES[nm] for nm in synth.SHAPE_ORDER]
     out = {"source_sha256_16": source_digest(), "kernel": GEMV_KERNEL, "calibration_bytes": CALIB_BYTES}
     for cname, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
@@ -163,7 +163,7 @@ def main():
 
     import torch
     from w4a16_dequant_gemm_group_amd import binding as B
-    from w4a16_dequant_gemm_group_amd import synth
+    import synth
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

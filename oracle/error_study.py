@@ -114,7 +114,7 @@ def traffic(n: int, k: int, G: int, m: int = 1, symmetric: bool = False):
 def study_matrix(seed: int = 5, n: int = 256, k: int = 2048):
     """The synthetic weight matrix of the study: N(0, 0.02) with 0.1 % of the
     input channels (two) scaled by 20, as the bench's decode weights."""
-    from w4a16_dequant_gemm_group_amd import synth
+    import synth
     bits, cols = synth.weights(n, k, seed=seed, outlier_frac=2.0 / k)
     return O.bf16_to_f64(bits), cols
 

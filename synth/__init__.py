@@ -1,6 +1,8 @@
 """Seeded synthetic inputs shared by the tests, the smoke check and the bench.
 
-This module only *draws* inputs: Gaussian weights with a few scaled-up input
+A package of its own, outside the library and the oracle, so that both sides
+take the same arrays without either importing the other.  It only *draws*
+inputs: Gaussian weights with a few scaled-up input
 channels (outliers) and Gaussian activations, rounded to bf16.  It holds none
 of the quantization or matmul arithmetic; both the CPU oracle and the GPU path
 receive the same arrays from here.

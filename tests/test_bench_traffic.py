@@ -19,7 +19,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
 import bench  # noqa: E402
-from w4a16_dequant_gemm_group_amd import synth  # noqa: E402
+import synth  # noqa: E402
 
 FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
 M1 = "void gq::(anonymous namespace)::gemv_stream_kernel<1, 2, 256, false, false, false>(x)"

@@ -10,7 +10,7 @@ import torch
 from gpu_util import announce, bf16_dev, bf16_out_to_f64, device
 from oracle import gq_oracle as O
 from w4a16_dequant_gemm_group_amd import binding as B
-from w4a16_dequant_gemm_group_amd import synth
+import synth
 
 pytestmark = pytest.mark.gpu
 

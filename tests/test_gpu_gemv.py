@@ -14,7 +14,7 @@ import torch
 from gpu_util import announce, assert_parity, bf16_dev, bits16, f16_dev, u8_dev
 from oracle import gq_oracle as O
 from w4a16_dequant_gemm_group_amd import binding as B
-from w4a16_dequant_gemm_group_amd import synth
+import synth
 
 pytestmark = pytest.mark.gpu
 

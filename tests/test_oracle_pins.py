@@ -15,7 +15,7 @@ import pytest
 
 from conftest import read_golden
 from oracle import gq_oracle as O
-from w4a16_dequant_gemm_group_amd import synth
+import synth
 
 
 # ---------------------------------------------------------------------------

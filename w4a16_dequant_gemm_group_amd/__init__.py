@@ -2,15 +2,14 @@
 AMD MI355X (gfx950), behind a C ABI (``include/gq.h``).
 
 The Python layer is a thin ctypes binding (``binding``) with the same names as
-the C entry points; ``synth`` draws the seeded synthetic inputs.  Importing the
-package does not load the shared library; the first call does, and fails
-loudly if it has not been built.
+the C entry points.  Importing the package does not load the shared library;
+the first call does, and fails loudly if it has not been built.
 """
-__all__ = ["binding", "synth"]
+__all__ = ["binding"]
 
 
 def __getattr__(name):
-    if name in ("binding", "synth"):
+    if name == "binding":
         import importlib
         return importlib.import_module(f"{__name__}.{name}")
     from . import binding
