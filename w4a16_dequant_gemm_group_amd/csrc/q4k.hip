@@ -255,8 +255,15 @@ __global__ __launch_bounds__(NT) void q4k_stream_kernel(const uint16_t* __restri
   const su::rsrc_t rb = su::make_rsrc(blocks, (uint32_t)N * row_bytes);
   const uint32_t hoff = (uint32_t)(lane >> 3) * kBlockBytes;
   const uint32_t woff = hoff + 16u + 16u * (uint32_t)(lane & 7);
-  const uint32_t o6 = 6u * (uint32_t)(lane & 7);  // bit offset of this lane's sub-block fields
-  const bool shi = o6 >= 32, mhi = o6 >= 16;
+  // This lane's sub-block fields: the 6-bit scale at bit o6 = 6 sub of the
+  // header's bytes 4..9 ({h.z : h.y}), the 6-bit min at bit o6 + 16 of bytes
+  // 8..15 ({h.w : h.z}).  Each lies within two bytes, which one v_perm with a
+  // per-lane selector brings to the bottom (selector byte 12 reads 0x00), so
+  // one bit-field extract at o6 & 7 finishes it.
+  const uint32_t o6 = 6u * (uint32_t)(lane & 7);
+  const uint32_t fbit = o6 & 7u, sbyte = o6 >> 3, mbyte = 2u + (o6 >> 3);
+  const uint32_t sel_sc = sbyte | ((sbyte + 1u) << 8) | 0x0C0C0000u;
+  const uint32_t sel_mn = mbyte | ((mbyte < 7u ? mbyte + 1u : 12u) << 8) | 0x0C0C0000u;
 
   auto load = [&](QBuf& B, int b, int t) {
     const bool kin = t * kStepK + lane * 32 < K;
@@ -332,11 +339,8 @@ __global__ __launch_bounds__(NT) void q4k_stream_kernel(const uint16_t* __restri
   auto fields = [&](const uint4& h, float& S, float& Mn) {
     const float d = f16_to_f32((uint16_t)(h.x & 0xFFFFu));
     const float dmin = f16_to_f32((uint16_t)(h.x >> 16));
-    // 6-bit fields by 32-bit funnel shifts: the scale sits at bit 6 sub of
-    // {h.w : h.z : h.y}, the min at bit 6 sub + 48; each lane picks the two
-    // dwords holding its field
-    const uint32_t sc6 = __builtin_amdgcn_alignbit(shi ? h.w : h.z, shi ? h.z : h.y, o6 & 31u) & 63u;
-    const uint32_t mn6 = __builtin_amdgcn_alignbit(h.w, mhi ? h.w : h.z, (o6 + 16u) & 31u) & 63u;
+    const uint32_t sc6 = __builtin_amdgcn_ubfe(__builtin_amdgcn_perm(h.z, h.y, sel_sc), fbit, 6);
+    const uint32_t mn6 = __builtin_amdgcn_ubfe(__builtin_amdgcn_perm(h.w, h.z, sel_mn), fbit, 6);
     S = d * (float)sc6;
     Mn = dmin * (float)mn6;
   };
@@ -361,11 +365,8 @@ __global__ __launch_bounds__(NT) void q4k_stream_kernel(const uint16_t* __restri
       const uint4 h = B.h[r];
       const float d = f16_to_f32((uint16_t)(h.x & 0xFFFFu));
       const float dmin = f16_to_f32((uint16_t)(h.x >> 16));
-      // 6-bit fields by 32-bit funnel shifts: the scale sits at bit 6 sub of
-      // {h.w : h.z : h.y}, the min at bit 6 sub + 48; each lane picks the two
-      // dwords holding its field
-      const uint32_t sc6 = __builtin_amdgcn_alignbit(shi ? h.w : h.z, shi ? h.z : h.y, o6 & 31u) & 63u;
-      const uint32_t mn6 = __builtin_amdgcn_alignbit(h.w, mhi ? h.w : h.z, (o6 + 16u) & 31u) & 63u;
+      const uint32_t sc6 = __builtin_amdgcn_ubfe(__builtin_amdgcn_perm(h.z, h.y, sel_sc), fbit, 6);
+      const uint32_t mn6 = __builtin_amdgcn_ubfe(__builtin_amdgcn_perm(h.w, h.z, sel_mn), fbit, 6);
       const float S = d * (float)sc6;
       const float Mn = dmin * (float)mn6;
       acc[0][r] = fmaf(S, a, fmaf(-Mn, sx, acc[0][r]));
