@@ -337,20 +337,17 @@ __global__ __launch_bounds__(NT) void q4k_stream_kernel(const uint16_t* __restri
 
   // the sub-block scale S = d sc and min Mn = dmin mn of row r's header
   auto fields = [&](const uint4& h, float& S, float& Mn) {
-    const float d = f16_to_f32((uint16_t)(h.x & 0xFFFFu));
-    const float dmin = f16_to_f32((uint16_t)(h.x >> 16));
+    const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(h.x & 0xFFFFu));
+    const _Float16 dmin = __builtin_bit_cast(_Float16, (uint16_t)(h.x >> 16));
     const uint32_t sc6 = __builtin_amdgcn_ubfe(__builtin_amdgcn_perm(h.z, h.y, sel_sc), fbit, 6);
     const uint32_t mn6 = __builtin_amdgcn_ubfe(__builtin_amdgcn_perm(h.w, h.z, sel_mn), fbit, 6);
-    S = d * (float)sc6;
-    Mn = dmin * (float)mn6;
+    // exact products (11 x 6 significant bits) in one mixed-precision fma each
+    S = __builtin_fmaf((float)d, (float)sc6, 0.f);
+    Mn = __builtin_fmaf((float)dmin, (float)mn6, 0.f);
   };
+  // the row block's sums start at zero and are cleared after its last k step
+  // (in the branch that stores them, so no other item pays for the reset)
   auto compute = [&](const QBuf& B, int b, int t) {
-    if (t == 0) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int r = 0; r < kQRpw; ++r) acc[m][r] = 0.f;
-    }
     if constexpr (MT == 1) {
     const uint4* xp = xs + t * 256 + lane;
     const uint4 x0 = xp[0], x1 = xp[64], x2 = xp[128], x3 = xp[192];
@@ -363,12 +360,13 @@ __global__ __launch_bounds__(NT) void q4k_stream_kernel(const uint16_t* __restri
       a = su::dot8_perm(B.w[r].z, x2, a, 0x43004300u);
       a = su::dot8_perm(B.w[r].w, x3, a, 0x43004300u);
       const uint4 h = B.h[r];
-      const float d = f16_to_f32((uint16_t)(h.x & 0xFFFFu));
-      const float dmin = f16_to_f32((uint16_t)(h.x >> 16));
+      const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(h.x & 0xFFFFu));
+      const _Float16 dmin = __builtin_bit_cast(_Float16, (uint16_t)(h.x >> 16));
       const uint32_t sc6 = __builtin_amdgcn_ubfe(__builtin_amdgcn_perm(h.z, h.y, sel_sc), fbit, 6);
       const uint32_t mn6 = __builtin_amdgcn_ubfe(__builtin_amdgcn_perm(h.w, h.z, sel_mn), fbit, 6);
-      const float S = d * (float)sc6;
-      const float Mn = dmin * (float)mn6;
+      // exact products (11 x 6 significant bits) in one mixed-precision fma each
+      const float S = __builtin_fmaf((float)d, (float)sc6, 0.f);
+      const float Mn = __builtin_fmaf((float)dmin, (float)mn6, 0.f);
       acc[0][r] = fmaf(S, a, fmaf(-Mn, sx, acc[0][r]));
     }
     } else {
@@ -429,6 +427,10 @@ __global__ __launch_bounds__(NT) void q4k_stream_kernel(const uint16_t* __restri
           }
         }
       }
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int r = 0; r < kQRpw; ++r) acc[m][r] = 0.f;
     }
   };
   // Whole buffer rounds in the loop, the last 0-2 items (already loaded) after
