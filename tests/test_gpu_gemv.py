@@ -107,6 +107,9 @@ def test_stream_multi_row_layouts(M, N, K, sym, G):
     (203, 4096, True, 32), (203, 4096, False, 64), (203, 4096, False, 128),
     (203, 4096, True, 256), (203, 4096, False, 512), (203, 4096, True, 1024),
     (16387, 4096, False, 128),   # several row blocks per workgroup
+    # M > 8: two teams of 8 waves per workgroup (>= 2 row blocks per compute
+    # unit; 1025 row blocks: the last workgroup's second team runs empty items)
+    (16387, 4096, True, 32), (16387, 4096, False, 32),
 ])
 def test_mfma_stream_shapes(M, N, K, sym, G):
     # the matrix-core GEMV with every activation row in LDS and K split over a

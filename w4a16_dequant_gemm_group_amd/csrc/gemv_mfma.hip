@@ -312,6 +312,7 @@ __global__ __launch_bounds__(256) void gemv_split_finalize_kernel(const float* _
 // activation rows (8 or 16, >= M).  Requires K % 512 == 0, KC % (NW * 512) ==
 // 0 and the LDS of mfma_stream_lds_bytes(MR, NW, KC, chunked).
 constexpr int kMSItem = 512;  // k per item
+constexpr size_t kMSTeamLds = 160 * 1024;  // LDS of one compute unit
 
 // Chunk sums are stored for the MR staged rows plus a zeroed slot read by the
 // lanes of rows >= MR; the chunked form keeps 16 rows per chunk (rows >= MR
@@ -372,10 +373,16 @@ __device__ __forceinline__ uint16_t ms_half(const uint32_t* v, int j) {
 }
 
 // XF16: fp16 activations and output (fp16 MFMA, nibbles as fp16 1024 + q).
-// Two workgroups per compute unit with 8 staged rows and 8 waves: the launch
-// bounds ask for four waves per SIMD (at most 128 registers).
-template <int MR, int NW, int GQ, bool SYM, bool CHUNKED, bool XF16>
-__global__ __launch_bounds__(NW * 64, MR == 8 && NW == 8 && !CHUNKED ? 4 : 1) void gemv_mfma_stream_kernel(
+// TM teams of NW waves share one workgroup and its staged x: each team works
+// as a workgroup of its own on its row blocks (K split over its waves), and
+// every team runs the same number of items (a team short of row blocks runs
+// empty ones: zero weights, no stores) so that all meet at the same barriers.
+// One team with 8 staged rows and 8 waves runs two workgroups per compute
+// unit: the launch bounds then ask for four waves per SIMD (at most 128
+// registers).
+template <int MR, int NW, int GQ, bool SYM, bool CHUNKED, bool XF16, int TM>
+__global__ __launch_bounds__(NW * 64 * TM, TM == 1 && MR == 8 && NW == 8 && !CHUNKED ? 4 : 1) void
+gemv_mfma_stream_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
     uint16_t* __restrict__ y, int KC) {
@@ -386,9 +393,13 @@ __global__ __launch_bounds__(NW * 64, MR == 8 && NW == 8 && !CHUNKED ? 4 : 1) vo
   constexpr int SXW = CHUNKED ? 16 : MR;         // chunk-sum rows stored per 32-chunk
   float* sxs = (float*)(xs + MR * XR);           // [KC / 32][SXW] chunk sums (+ 4 zeros)
   const int zslot = (KC / 32) * SXW;             // the zero slot (SXW == MR)
-  float* red = sxs + zslot + (CHUNKED ? 0 : 4);  // [NW][64][4] partial tiles
+  constexpr int NT = NW * 64 * TM;              // threads per workgroup
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int team = TM == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)threadIdx.x / (NW * 64));
+  float* red = sxs + zslot + (CHUNKED ? 0 : 4) + team * NW * 256;  // [TM][NW][64][4] partial tiles
+  const int tl = (int)threadIdx.x - team * NW * 64;  // thread within the team
+  const int w = __builtin_amdgcn_readfirstlane(tl >> 6);
+  const int vb = (int)blockIdx.x * TM + team, vgrid = (int)gridDim.x * TM;  // the team's place
   const int NB = (N + 15) / 16;
   const int NCH = (K + KC - 1) / KC;             // K chunks
   const int kw = KC / NW;                        // k per wave and chunk
@@ -397,26 +408,28 @@ __global__ __launch_bounds__(NW * 64, MR == 8 && NW == 8 && !CHUNKED ? 4 : 1) vo
   const rsrc_t rw = make_rsrc(qw, (uint32_t)N * (uint32_t)(K / 2));
   const rsrc_t rs = make_rsrc(scales, (uint32_t)N * (uint32_t)(K / G) * 2);
   const rsrc_t rz = make_rsrc(SYM ? (const void*)scales : (const void*)zeros, (uint32_t)N * (uint32_t)(K / G) * 2);
-  const int nrb = (int)blockIdx.x < NB ? (NB - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  // row blocks of the workgroup's first team (the others have as many or one fewer)
+  const int b0 = (int)blockIdx.x * TM;
+  const int nrb = b0 < NB ? (NB - 1 - b0) / vgrid + 1 : 0;
   const int items = nrb * IPW;                   // the same for every wave of the workgroup
 
-  // item i -> (row block, k0)
-  auto item_rb = [&](int i) { return (int)blockIdx.x + (i / IPW) * (int)gridDim.x; };
+  // item i -> (row block, k0); row blocks >= NB read zeros and store nothing
+  auto item_rb = [&](int i) { return vb + (i / IPW) * vgrid; };
   auto item_k0 = [&](int i) {
     const int j = i % IPW;
     return (j / IPC) * KC + w * kw + (j % IPC) * kMSItem;
   };
 
   // stage x[:, kb .. kb + KC) (rows >= M, k >= K and the chunk sums of rows
-  // >= MR are zero) in batches of eight 16-byte loads per thread, all in flight
-  // before any is used; MR KC / 8 is a multiple of 8 NW 64, so every lane runs
+  // >= MR are zero) in batches of kUX 16-byte loads per thread, all in flight
+  // before any is used; MR KC / 8 is a multiple of kUX NT, so every lane runs
   // every batch (the quad shuffles)
-  constexpr int kUX = 8;
+  constexpr int kUX = TM == 1 ? 8 : 4;
   const int CC = KC / 8;  // 16-byte chunks per row
   auto stage_load = [&](int kb, int f0, uint4 (&v)[kUX]) {
 #pragma unroll
     for (int u = 0; u < kUX; ++u) {
-      const int f = f0 + u * NW * 64 + (int)threadIdx.x;
+      const int f = f0 + u * NT + (int)threadIdx.x;
       const int m = f / CC, c = f - m * CC;
       v[u] = make_uint4(0, 0, 0, 0);
       if (m < M && kb + c * 8 < K) v[u] = *(const uint4*)(x + (size_t)m * K + (size_t)(kb + c * 8));
@@ -425,7 +438,7 @@ __global__ __launch_bounds__(NW * 64, MR == 8 && NW == 8 && !CHUNKED ? 4 : 1) vo
   auto stage_store = [&](int f0, const uint4 (&v)[kUX]) {
 #pragma unroll
     for (int u = 0; u < kUX; ++u) {
-      const int f = f0 + u * NW * 64 + (int)threadIdx.x;
+      const int f = f0 + u * NT + (int)threadIdx.x;
       const int m = f / CC, c = f - m * CC;
       xs[m * XR + c] = perm_x(v[u]);
       float sm = dot2x<XF16>(v[u].x, 0.f);  // against 1.0 pairs
@@ -438,7 +451,7 @@ __global__ __launch_bounds__(NW * 64, MR == 8 && NW == 8 && !CHUNKED ? 4 : 1) vo
     }
   };
   auto stage = [&](int kb, int from) {
-    for (int f0 = from; f0 < MR * CC; f0 += kUX * NW * 64) {
+    for (int f0 = from; f0 < MR * CC; f0 += kUX * NT) {
       uint4 v[kUX];
       stage_load(kb, f0, v);
       stage_store(f0, v);
@@ -454,11 +467,11 @@ __global__ __launch_bounds__(NW * 64, MR == 8 && NW == 8 && !CHUNKED ? 4 : 1) vo
   for (int j = 0; j < 2; ++j)
     if (j < items) ms_load<GQ, SYM>(buf[j], item_rb(j), item_k0(j), n, g, N, K, G, rw, rs, rz);
   stage_store(0, xv0);
-  stage(0, kUX * NW * 64);
+  stage(0, kUX * NT);
   if (SXW == MR) {
     if (threadIdx.x < 4) sxs[zslot + threadIdx.x] = 0.f;
   } else {
-    for (int i = threadIdx.x; i < (KC / 32) * (16 - MR); i += NW * 64)
+    for (int i = threadIdx.x; i < (KC / 32) * (16 - MR); i += NT)
       sxs[(i / (16 - MR)) * 16 + MR + i % (16 - MR)] = 0.f;
   }
   __syncthreads();
@@ -527,7 +540,7 @@ __global__ __launch_bounds__(NW * 64, MR == 8 && NW == 8 && !CHUNKED ? 4 : 1) vo
       *(float4*)&red[(w * 64 + lane) * 4] = make_float4(acc[0], acc[1], acc[2], acc[3]);
       acc[0] = acc[1] = acc[2] = acc[3] = 0.f;
       __syncthreads();
-      const int t = threadIdx.x;
+      const int t = tl;
       if (t < 16 * M) {
         const int m = t >> 4, nn = t & 15, rb = item_rb(i);
         const int src = (nn + 16 * (m >> 2)) * 4 + (m & 3);
@@ -559,18 +572,34 @@ __global__ __launch_bounds__(NW * 64, MR == 8 && NW == 8 && !CHUNKED ? 4 : 1) vo
   if (rest > 1) compute(buf[1], i++);
 }
 
+// Two teams per workgroup with 16 staged rows when x is staged whole, both
+// teams' partial tiles fit beside it, and there are row blocks for two teams
+// on every compute unit: the 16 waves of a compute unit then share one x stage
+// (one 8-wave workgroup per compute unit otherwise, as x takes most of LDS).
+// gate_up at M = 16: 26.7-26.8 -> 25.3-25.5 us.  With 8 staged rows, two
+// 8-wave workgroups per compute unit stay faster (gate_up at M = 8: 23.0 -> 25.2
+// us with one of 16 waves).  Not for asymmetric group-32 weights, which would
+// spill at the four waves per SIMD a 1024-thread workgroup implies.
 template <int MR, int NW, bool SYM, bool XF16>
 hipError_t launch_ms(const uint16_t* x, int M, int K, int KC, const uint8_t* qw, const uint16_t* sc,
                      const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
   const size_t lds = mfma_stream_lds_bytes(MR, NW, KC, KC < K);
+  const size_t lds2 = lds + (size_t)NW * 64 * 16;
+  const int nb = (N + 15) / 16;
+  const bool teams = MR == 16 && KC >= K && lds2 <= kMSTeamLds && nb >= 2 * num_cus() &&
+                     !(!SYM && G == 32);
   const int per_cu = lds <= 80 * 1024 ? 2 : 1;
-  const int grid = std::max(1, std::min((N + 15) / 16, per_cu * num_cus()));
-#define GQ_MS_LAUNCH(GQ_)                                                                      \
-  if (KC < K)                                                                                  \
-    hipLaunchKernelGGL((gemv_mfma_stream_kernel<MR, NW, GQ_, SYM, true, XF16>), dim3(grid),    \
-                       dim3(NW * 64), lds, s, x, M, K, qw, sc, zr, N, G, y, KC);               \
-  else                                                                                         \
-    hipLaunchKernelGGL((gemv_mfma_stream_kernel<MR, NW, GQ_, SYM, false, XF16>), dim3(grid),   \
+  const int grid = teams ? std::max(1, std::min((nb + 1) / 2, num_cus()))
+                         : std::max(1, std::min(nb, per_cu * num_cus()));
+#define GQ_MS_LAUNCH(GQ_)                                                                         \
+  if (KC < K)                                                                                     \
+    hipLaunchKernelGGL((gemv_mfma_stream_kernel<MR, NW, GQ_, SYM, true, XF16, 1>), dim3(grid),    \
+                       dim3(NW * 64), lds, s, x, M, K, qw, sc, zr, N, G, y, KC);                  \
+  else if (MR == 16 && teams)                                                                     \
+    hipLaunchKernelGGL((gemv_mfma_stream_kernel<MR, NW, GQ_, SYM, false, XF16, MR == 16 ? 2 : 1>),\
+                       dim3(grid), dim3(NW * 128), lds2, s, x, M, K, qw, sc, zr, N, G, y, KC);    \
+  else                                                                                            \
+    hipLaunchKernelGGL((gemv_mfma_stream_kernel<MR, NW, GQ_, SYM, false, XF16, 1>), dim3(grid),   \
                        dim3(NW * 64), lds, s, x, M, K, qw, sc, zr, N, G, y, KC)
   switch (G) {
     case 32: GQ_MS_LAUNCH(0); break;
