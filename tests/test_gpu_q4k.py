@@ -48,7 +48,10 @@ def test_gemv_small(M, N, K):
     2304 and 256, several row pairs per wave at 1031 rows, one workgroup per
     compute unit from four steps on, x staged in more than one pass at M = 1
     with 28672 and 73728 (36 steps) and at M = 2..4 with 18432 and beyond; M = 2
-    at 73728, M = 3, 4 from 28672 on and M = 16 take the per-workgroup kernel."""
+    at 73728 and M = 3, 4 from 28672 on take the per-workgroup kernel.  M = 16
+    takes the matrix-core kernel where K is a multiple of 512 (x in chunks of
+    4096 columns beyond 4096) and the per-workgroup kernel at 2304, 256 and
+    10496."""
     w, x = synth.small(N, K, M, seed=N + M)
     blocks = O.q4k_encode(O.q4k_quantize(O.bf16_to_f64(w)))
     y = B.gq_q4k_gemv(bf16_dev(x), u8_dev(blocks))
@@ -58,12 +61,31 @@ def test_gemv_small(M, N, K):
     assert_parity(bits16(y), ref, O.bf16_to_f64(x), wh, f"q4k gemv [{N},{K}] M={M}")
 
 
+@pytest.mark.parametrize("M", [5, 8, 9, 13, 16])
+@pytest.mark.parametrize("N,K", [(77, 4096), (1031, 4096), (33, 14336), (16, 2048), (203, 8192),
+                                 (3, 512), (21, 2560)])
+def test_gemv_matrix_cores(M, N, K):
+    """M = 5..16 on the matrix cores (one MFMA per sub-block and 16 rows): a
+    partial last row block (77, 33, 21, 3 rows), several row blocks per
+    workgroup (1031), x in chunks (14336: two chunks of 8192 with 8 staged
+    rows, four of 4096 with 16, the last partial), items past K (2048, 2560,
+    512), 8192 with 8 staged rows in one stage and with 16 in two."""
+    w, x = synth.small(N, K, M, seed=N + K + M)
+    blocks = O.q4k_encode(O.q4k_quantize(O.bf16_to_f64(w)))
+    y = B.gq_q4k_gemv(bf16_dev(x), u8_dev(blocks))
+    torch.cuda.synchronize()
+    ref = O.q4k_reference(x, blocks)
+    wh = O.q4k_dequantize_fields(O.q4k_decode(blocks))
+    assert_parity(bits16(y), ref, O.bf16_to_f64(x), wh, f"q4k gemv [{N},{K}] M={M} (matrix cores)")
+
+
 @pytest.mark.parametrize("name", ["down", "gate_up"])
-@pytest.mark.parametrize("M", [1, 4])
+@pytest.mark.parametrize("M", [1, 4, 8, 16])
 def test_full_size(name, M):
     """Full-size super-block quantize + GEMV at M = 1 and 4 (the streaming
-    kernel): every block's 144 bytes and every output row against the oracle,
-    in row chunks."""
+    kernel) and 8 and 16 (the matrix cores; down in chunks of x): every
+    block's 144 bytes and every output row against the oracle, in row
+    chunks."""
     w, x = synth.q4k_case(name, M)
     announce(f"q4k {name} {w.shape} M={M}, all rows")
     blocks = B.gq_q4k_quantize(bf16_dev(w))

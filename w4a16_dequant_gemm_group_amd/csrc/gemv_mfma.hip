@@ -572,6 +572,217 @@ gemv_mfma_stream_kernel(
   if (rest > 1) compute(buf[1], i++);
 }
 
+// Super-block (Q4_K-style) GEMV on the matrix cores, 5 <= M <= 16 ("量化" page,
+// "工作原理" figure, middle panel): the structure of gemv_mfma_stream_kernel
+// with the 144-byte blocks as the weight operand.  A 32-wide chunk of K is one
+// sub-block, so MFMA c of a 128-wide step covers sub-block c: lane (n, g)
+// loads the 16 nibble bytes of sub-block g of each step of its row (the same
+// nibble order as the packed INT4 rows) and both block headers of its row per
+// 512-wide item; after the 4 x 4 transpose MFMA c takes the scale and min of
+// sub-block c:
+//   acc[m][n] += S D[m][n] - (128 S + Mn) sum_{k in sub-block} x[m][k],
+//   S = d sc_j, Mn = dmin mn_j  (products of an fp16 and a 6-bit field: exact),
+// D being sum x (128 + q) from the bf16 magic-number unpack.
+struct QkBuf {
+  uint4 w[4];  // sub-block g of each 128-wide step
+  uint4 h[2];  // the headers of the item's two blocks
+};
+
+// 6-bit field at bit P of the 96-bit {h.w : h.z : h.y} (compile-time P)
+template <int P>
+__device__ __forceinline__ uint32_t q4k_field(const uint4& h) {
+  constexpr int wd = P / 32, sh = P % 32;
+  const uint32_t lo = wd == 0 ? h.y : wd == 1 ? h.z : h.w;
+  if constexpr (sh <= 26) {
+    return (lo >> sh) & 63u;
+  } else {
+    const uint32_t hi = wd == 0 ? h.z : h.w;
+    return __builtin_amdgcn_alignbit(hi, lo, sh) & 63u;
+  }
+}
+
+template <int MR, bool CHUNKED>
+__global__ __launch_bounds__(512, MR == 8 && !CHUNKED ? 4 : 1) void q4k_mfma_stream_kernel(
+    const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ blocks, int N,
+    uint16_t* __restrict__ y, int KC) {
+  constexpr int NW = 8, NT = NW * 64;
+  extern __shared__ uint4 lds4[];
+  const int XR = KC / 8 + 1;                     // uint4 per staged x row (+1: no bank conflicts)
+  uint4* xs = lds4;                              // [MR][XR] permuted pairs of the chunk
+  constexpr int SXW = CHUNKED ? 16 : MR;         // chunk-sum rows stored per 32-chunk
+  float* sxs = (float*)(xs + MR * XR);           // [KC / 32][SXW] chunk sums (+ 4 zeros)
+  const int zslot = (KC / 32) * SXW;             // the zero slot (SXW == MR)
+  float* red = sxs + zslot + (CHUNKED ? 0 : 4);  // [NW][64][4] partial tiles
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int NB = (N + 15) / 16;
+  const int NCH = (K + KC - 1) / KC;             // K chunks
+  const int kw = KC / NW;                        // k per wave and chunk
+  const int IPC = kw / kMSItem;                  // items per wave and chunk
+  const int IPW = NCH * IPC;                     // items per wave and row block
+  const uint32_t row_bytes = (uint32_t)(K / 256) * 144u;
+  const rsrc_t rb = make_rsrc(blocks, (uint32_t)N * row_bytes);
+  const int nrb = (int)blockIdx.x < NB ? (NB - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  const int items = nrb * IPW;                   // the same for every wave of the workgroup
+
+  auto item_rb = [&](int i) { return (int)blockIdx.x + (i / IPW) * (int)gridDim.x; };
+  auto item_k0 = [&](int i) {
+    const int j = i % IPW;
+    return (j / IPC) * KC + w * kw + (j % IPC) * kMSItem;
+  };
+  auto load = [&](QkBuf& B, int rbk, int k0) {
+    const int row = rbk * 16 + n;
+    const bool rin = row < N && k0 < K;  // k0 >= K: an item past a partial last chunk
+    const uint32_t base = rin ? (uint32_t)row * row_bytes + (uint32_t)(k0 / 256) * 144u : kOob;
+#pragma unroll
+    for (int L = 0; L < 4; ++L) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+          rb, base + (uint32_t)((L >> 1) * 144 + 16 + 16 * ((L & 1) * 4 + g)), 0, 2);
+      B.w[L] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rb, base + 144u * b, 0, 0);
+      B.h[b] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  };
+
+  // x staging as in gemv_mfma_stream_kernel (MR KC / 8 is a multiple of 8 NT)
+  constexpr int kUX = 8;
+  const int CC = KC / 8;  // 16-byte chunks per row
+  auto stage_load = [&](int kb, int f0, uint4 (&v)[kUX]) {
+#pragma unroll
+    for (int u = 0; u < kUX; ++u) {
+      const int f = f0 + u * NT + (int)threadIdx.x;
+      const int m = f / CC, c = f - m * CC;
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (m < M && kb + c * 8 < K) v[u] = *(const uint4*)(x + (size_t)m * K + (size_t)(kb + c * 8));
+    }
+  };
+  auto stage_store = [&](int f0, const uint4 (&v)[kUX]) {
+#pragma unroll
+    for (int u = 0; u < kUX; ++u) {
+      const int f = f0 + u * NT + (int)threadIdx.x;
+      const int m = f / CC, c = f - m * CC;
+      xs[m * XR + c] = perm_x(v[u]);
+      float sm = dot2x<false>(v[u].x, 0.f);  // against 1.0 pairs
+      sm = dot2x<false>(v[u].y, sm);
+      sm = dot2x<false>(v[u].z, sm);
+      sm = dot2x<false>(v[u].w, sm);
+      sm += __shfl_xor(sm, 1, 64);
+      sm += __shfl_xor(sm, 2, 64);
+      if ((c & 3) == 0) sxs[(c >> 2) * SXW + m] = sm;
+    }
+  };
+  auto stage = [&](int kb, int from) {
+    for (int f0 = from; f0 < MR * CC; f0 += kUX * NT) {
+      uint4 v[kUX];
+      stage_load(kb, f0, v);
+      stage_store(f0, v);
+    }
+  };
+
+  uint4 xv0[kUX];
+  stage_load(0, 0, xv0);
+  QkBuf buf[3];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    if (j < items) load(buf[j], item_rb(j), item_k0(j));
+  stage_store(0, xv0);
+  stage(0, kUX * NT);
+  if (SXW == MR) {
+    if (threadIdx.x < 4) sxs[zslot + threadIdx.x] = 0.f;
+  } else {
+    for (int i = threadIdx.x; i < (KC / 32) * (16 - MR); i += NT)
+      sxs[(i / (16 - MR)) * 16 + MR + i % (16 - MR)] = 0.f;
+  }
+  __syncthreads();
+
+  const int xrow = (n % MR) * XR;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const QkBuf& B, int i) {
+    const int k0 = item_k0(i);
+    const int kb = (i % IPW) / IPC * KC;  // the item's chunk
+    if (CHUNKED && i > 0 && i % IPC == 0) {  // a new chunk: every wave is done with the last one
+      __syncthreads();
+      stage(kb, 0);
+      __syncthreads();
+    }
+    const int xc0 = (k0 - kb) / 8, ch0 = (k0 - kb) / 32;
+    auto step = [&](auto Lc) {
+      constexpr int L = decltype(Lc)::value;
+      uint32_t e0 = B.w[L].x, e1 = B.w[L].y, e2 = B.w[L].z, e3 = B.w[L].w;
+      transpose4(e0, e1, e2, e3);
+      const uint32_t ev[4] = {e0, e1, e2, e3};
+      f32x4_t D[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 A = xs[xrow + xc0 + 16 * L + 4 * c + g];
+        D[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A),
+                                                       __builtin_bit_cast(bf16x8_t, unpack8(ev[c], 0x43004300u)),
+                                                       f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      }
+      const uint4 h = B.h[L >> 1];
+      const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(h.x & 0xFFFFu));
+      const _Float16 dmin = __builtin_bit_cast(_Float16, (uint16_t)(h.x >> 16));
+      auto corr = [&](auto Cc) {
+        constexpr int c = decltype(Cc)::value;
+        constexpr int j = (L & 1) * 4 + c;  // the sub-block of the block
+        const float S = __builtin_fmaf((float)d, (float)q4k_field<6 * j>(h), 0.f);
+        const float Mn = __builtin_fmaf((float)dmin, (float)q4k_field<48 + 6 * j>(h), 0.f);
+        const float T = __builtin_fmaf(128.f, S, Mn);
+        // rows 4 g .. 4 g + 3; lanes whose rows are >= MR read a zeroed slot
+        const float4 sx =
+            *(const float4*)&sxs[SXW == 16 || 4 * g < MR ? (ch0 + 4 * L + c) * SXW + 4 * g : zslot];
+        acc[0] = fmaf(S, D[c][0], fmaf(-T, sx.x, acc[0]));
+        acc[1] = fmaf(S, D[c][1], fmaf(-T, sx.y, acc[1]));
+        acc[2] = fmaf(S, D[c][2], fmaf(-T, sx.z, acc[2]));
+        acc[3] = fmaf(S, D[c][3], fmaf(-T, sx.w, acc[3]));
+      };
+      corr(std::integral_constant<int, 0>{});
+      corr(std::integral_constant<int, 1>{});
+      corr(std::integral_constant<int, 2>{});
+      corr(std::integral_constant<int, 3>{});
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
+    if (i % IPW == IPW - 1) {  // the row block is done: add the waves' tiles
+      *(float4*)&red[(w * 64 + lane) * 4] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      acc[0] = acc[1] = acc[2] = acc[3] = 0.f;
+      __syncthreads();
+      const int t = threadIdx.x;
+      if (t < 16 * M) {
+        const int m = t >> 4, nn = t & 15, rbk = item_rb(i);
+        const int src = (nn + 16 * (m >> 2)) * 4 + (m & 3);
+        float v = 0.f;
+        for (int u = 0; u < NW; ++u) v += red[u * 256 + src];
+        const int row = rbk * 16 + nn;
+        if (row < N) y[(size_t)m * N + row] = f32_to_bf16_rne(v);
+      }
+      __syncthreads();
+    }
+  };
+
+  // three register buffers: item i + 2 loads while item i is multiplied; whole
+  // rounds in the loop, the last 0-2 items after it
+  const int rounds = items / 3, rest = items % 3;
+  int i = 0;
+  for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      if (i + 2 < items) load(buf[(j + 2) % 3], item_rb(i + 2), item_k0(i + 2));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(buf[j], i);
+      ++i;
+    }
+  }
+  if (rest > 0) compute(buf[0], i++);
+  if (rest > 1) compute(buf[1], i++);
+}
+
 // Two teams per workgroup with 16 staged rows when x is staged whole, both
 // teams' partial tiles fit beside it, and there are row blocks for two teams
 // on every compute unit: the 16 waves of a compute unit then share one x stage
@@ -728,6 +939,52 @@ hipError_t launch_w4a16_gemv_mfma(const uint16_t* x, int M, int64_t K, const uin
   else
     hipLaunchKernelGGL(gemv_split_finalize_kernel<false>, dim3((unsigned)((mn + 255) / 256)), dim3(256),
                        0, s, (const float*)part, splits, mn, y);
+  return hipGetLastError();
+}
+
+// The super-block matrix-core GEMV: 8 staged rows (M <= 8) or 16, 8 waves per
+// workgroup, K in 512-wide items; x staged whole while it fits (two
+// workgroups per compute unit at 8 rows up to K = 4096), else in chunks of
+// 8192 (8 rows) or 4096 (16 rows) columns.  False if K is not a multiple of
+// 512 or a byte offset would not fit 32 bits.
+static bool q4k_mfma_config(int M, int64_t K, int64_t N, int* MR, int* KC) {
+  if (M < 5 || M > 16 || K % kMSItem != 0 || K > ((int64_t)1 << 24)) return false;
+  if (N * (K / 256) * 144 >= ((int64_t)1 << 31) || (int64_t)M * K * 2 >= ((int64_t)1 << 31)) return false;
+  *MR = M <= 8 ? 8 : 16;
+  const int kcmax = *MR == 8 ? 8192 : 4096;
+  *KC = (int)std::min<int64_t>(kcmax, (K + 4095) / 4096 * 4096);
+  return mfma_stream_lds_bytes(*MR, 8, *KC, *KC < K) <= 156 * 1024;
+}
+
+bool q4k_mfma_stream_supported(int M, int64_t K, int64_t N) {
+  int MR, KC;
+  return q4k_mfma_config(M, K, N, &MR, &KC);
+}
+
+hipError_t launch_q4k_gemv_mfma_stream(const uint16_t* x, int M, int64_t K, const uint8_t* blocks,
+                                       int64_t N, uint16_t* y, hipStream_t s) {
+  int MR, KC;
+  if (!q4k_mfma_config(M, K, N, &MR, &KC)) return hipErrorInvalidValue;
+  const int k = (int)K, n = (int)N;
+  const bool chunked = KC < k;
+  const size_t lds = mfma_stream_lds_bytes(MR, 8, KC, chunked);
+  const int per_cu = lds <= 80 * 1024 ? 2 : 1;
+  const int grid = std::max(1, std::min((n + 15) / 16, per_cu * num_cus()));
+  if (MR == 8) {
+    if (chunked)
+      hipLaunchKernelGGL((q4k_mfma_stream_kernel<8, true>), dim3(grid), dim3(512), lds, s, x, M, k, blocks,
+                         n, y, KC);
+    else
+      hipLaunchKernelGGL((q4k_mfma_stream_kernel<8, false>), dim3(grid), dim3(512), lds, s, x, M, k,
+                         blocks, n, y, KC);
+  } else {
+    if (chunked)
+      hipLaunchKernelGGL((q4k_mfma_stream_kernel<16, true>), dim3(grid), dim3(512), lds, s, x, M, k,
+                         blocks, n, y, KC);
+    else
+      hipLaunchKernelGGL((q4k_mfma_stream_kernel<16, false>), dim3(grid), dim3(512), lds, s, x, M, k,
+                         blocks, n, y, KC);
+  }
   return hipGetLastError();
 }
 

@@ -151,6 +151,10 @@ hipError_t launch_w4a16_gemm(const uint16_t* x, int64_t M, int64_t K, const uint
                              int symmetric, uint16_t* y, void* workspace, bool xf16, hipStream_t s);
 hipError_t launch_q4k_quantize(const void* w, gq_dtype dt, int64_t N, int64_t K, uint8_t* blocks,
                                hipStream_t s);
+// Super-block GEMV on the matrix cores (5 <= M <= 16, K a multiple of 512).
+bool q4k_mfma_stream_supported(int M, int64_t K, int64_t N);
+hipError_t launch_q4k_gemv_mfma_stream(const uint16_t* x, int M, int64_t K, const uint8_t* blocks,
+                                       int64_t N, uint16_t* y, hipStream_t s);
 hipError_t launch_q4k_gemv(const uint16_t* x, int M, int64_t K, const uint8_t* blocks, int64_t N,
                            uint16_t* y, hipStream_t s);
 

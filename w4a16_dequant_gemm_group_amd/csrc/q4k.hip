@@ -530,6 +530,9 @@ hipError_t launch_q4k_gemv(const uint16_t* x, int M, int64_t K, const uint8_t* b
       default: return launch_t<1, 2, 8>(x, M, k, blocks, n, y, s);
     }
   }
+  // M = 5..16: the matrix cores (one MFMA per sub-block and 16 rows)
+  if (M >= 5 && q4k_mfma_stream_supported(M, K, N))
+    return launch_q4k_gemv_mfma_stream(x, M, K, blocks, N, y, s);
   if (M == 2) return launch_t<2, 2, 2>(x, M, k, blocks, n, y, s);
   if (M <= 4) return launch_t<4, 2, 1>(x, M, k, blocks, n, y, s);
   if (M <= 8) return launch_t<8, 2, 1>(x, M, k, blocks, n, y, s);
