@@ -582,7 +582,13 @@ gemv_mfma_stream_kernel(
 // sub-block c:
 //   acc[m][n] += S D[m][n] - (128 S + Mn) sum_{k in sub-block} x[m][k],
 //   S = d sc_j, Mn = dmin mn_j  (products of an fp16 and a 6-bit field: exact),
-// D being sum x (128 + q) from the bf16 magic-number unpack.
+// D being sum x (128 + q) from the bf16 magic-number unpack.  The second term
+// is itself a product over the sub-blocks of a step, [16 rows of x sums] x
+// [4 sub-blocks x 16 weight rows], so it runs on one fp32 MFMA
+// (v_mfma_f32_16x16x4f32, fp32 products and sums) per step into an
+// accumulator of its own: lane (n, g) supplies the x sum of row n and the
+// -(128 S + Mn) of weight row n, both for sub-block g, and decodes the min of
+// that one sub-block only (per-lane byte selectors as in the M = 1 kernel).
 struct QkBuf {
   uint4 w[4];  // sub-block g of each 128-wide step
   uint4 h[2];  // the headers of the item's two blocks
@@ -602,7 +608,7 @@ __device__ __forceinline__ uint32_t q4k_field(const uint4& h) {
 }
 
 template <int MR, bool CHUNKED>
-__global__ __launch_bounds__(512, MR == 8 && !CHUNKED ? 4 : 1) void q4k_mfma_stream_kernel(
+__global__ __launch_bounds__(512, 1) void q4k_mfma_stream_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ blocks, int N,
     uint16_t* __restrict__ y, int KC) {
   constexpr int NW = 8, NT = NW * 64;
@@ -700,6 +706,18 @@ __global__ __launch_bounds__(512, MR == 8 && !CHUNKED ? 4 : 1) void q4k_mfma_str
 
   const int xrow = (n % MR) * XR;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t accz = {0.f, 0.f, 0.f, 0.f};  // the x-sum terms, from the fp32 MFMAs
+  // byte selectors and bit offset of the 6-bit scale and min of sub-block g
+  // (even steps) and 4 + g (odd steps) of a block, as in q4k_stream_kernel
+  uint32_t sel_sc[2], sel_mn[2], fbit[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const uint32_t o6 = 6u * (uint32_t)(4 * e + g);
+    const uint32_t sb = o6 >> 3, mb = 2u + (o6 >> 3);
+    fbit[e] = o6 & 7u;
+    sel_sc[e] = sb | ((sb + 1u) << 8) | 0x0C0C0000u;
+    sel_mn[e] = mb | ((mb < 7u ? mb + 1u : 12u) << 8) | 0x0C0C0000u;
+  }
 
   auto compute = [&](const QkBuf& B, int i) {
     const int k0 = item_k0(i);
@@ -730,28 +748,35 @@ __global__ __launch_bounds__(512, MR == 8 && !CHUNKED ? 4 : 1) void q4k_mfma_str
         constexpr int c = decltype(Cc)::value;
         constexpr int j = (L & 1) * 4 + c;  // the sub-block of the block
         const float S = __builtin_fmaf((float)d, (float)q4k_field<6 * j>(h), 0.f);
-        const float Mn = __builtin_fmaf((float)dmin, (float)q4k_field<48 + 6 * j>(h), 0.f);
-        const float T = __builtin_fmaf(128.f, S, Mn);
-        // rows 4 g .. 4 g + 3; lanes whose rows are >= MR read a zeroed slot
-        const float4 sx =
-            *(const float4*)&sxs[SXW == 16 || 4 * g < MR ? (ch0 + 4 * L + c) * SXW + 4 * g : zslot];
-        acc[0] = fmaf(S, D[c][0], fmaf(-T, sx.x, acc[0]));
-        acc[1] = fmaf(S, D[c][1], fmaf(-T, sx.y, acc[1]));
-        acc[2] = fmaf(S, D[c][2], fmaf(-T, sx.z, acc[2]));
-        acc[3] = fmaf(S, D[c][3], fmaf(-T, sx.w, acc[3]));
+        acc[0] = fmaf(S, D[c][0], acc[0]);
+        acc[1] = fmaf(S, D[c][1], acc[1]);
+        acc[2] = fmaf(S, D[c][2], acc[2]);
+        acc[3] = fmaf(S, D[c][3], acc[3]);
       };
       corr(std::integral_constant<int, 0>{});
       corr(std::integral_constant<int, 1>{});
       corr(std::integral_constant<int, 2>{});
       corr(std::integral_constant<int, 3>{});
+      // sub-block g of the step: -(128 S + Mn) of weight row n against the x
+      // sum of activation row n (0 for rows >= MR)
+      constexpr int e = L & 1;
+      const uint32_t sc6 = __builtin_amdgcn_ubfe(__builtin_amdgcn_perm(h.z, h.y, sel_sc[e]), fbit[e], 6);
+      const uint32_t mn6 = __builtin_amdgcn_ubfe(__builtin_amdgcn_perm(h.w, h.z, sel_mn[e]), fbit[e], 6);
+      const float Sg = __builtin_fmaf((float)d, (float)sc6, 0.f);
+      const float Mg = __builtin_fmaf((float)dmin, (float)mn6, 0.f);
+      const float Tg = -__builtin_fmaf(128.f, Sg, Mg);
+      const float sxg = SXW == 16 || n < MR ? sxs[(ch0 + 4 * L + g) * SXW + n] : 0.f;
+      accz = __builtin_amdgcn_mfma_f32_16x16x4f32(sxg, Tg, accz, 0, 0, 0);
     };
     step(std::integral_constant<int, 0>{});
     step(std::integral_constant<int, 1>{});
     step(std::integral_constant<int, 2>{});
     step(std::integral_constant<int, 3>{});
     if (i % IPW == IPW - 1) {  // the row block is done: add the waves' tiles
-      *(float4*)&red[(w * 64 + lane) * 4] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      *(float4*)&red[(w * 64 + lane) * 4] =
+          make_float4(acc[0] + accz[0], acc[1] + accz[1], acc[2] + accz[2], acc[3] + accz[3]);
       acc[0] = acc[1] = acc[2] = acc[3] = 0.f;
+      accz = f32x4_t{0.f, 0.f, 0.f, 0.f};
       __syncthreads();
       const int t = threadIdx.x;
       if (t < 16 * M) {
@@ -942,10 +967,9 @@ hipError_t launch_w4a16_gemv_mfma(const uint16_t* x, int M, int64_t K, const uin
   return hipGetLastError();
 }
 
-// The super-block matrix-core GEMV: 8 staged rows (M <= 8) or 16, 8 waves per
-// workgroup, K in 512-wide items; x staged whole while it fits (two
-// workgroups per compute unit at 8 rows up to K = 4096), else in chunks of
-// 8192 (8 rows) or 4096 (16 rows) columns.  False if K is not a multiple of
+// The super-block matrix-core GEMV: 8 staged rows (M <= 8) or 16, one
+// workgroup of 8 waves per compute unit, K in 512-wide items; x staged whole
+// while it fits, else in chunks of 8192 (8 rows) or 4096 (16 rows) columns.  False if K is not a multiple of
 // 512 or a byte offset would not fit 32 bits.
 static bool q4k_mfma_config(int M, int64_t K, int64_t N, int* MR, int* KC) {
   if (M < 5 || M > 16 || K % kMSItem != 0 || K > ((int64_t)1 << 24)) return false;
@@ -968,8 +992,7 @@ hipError_t launch_q4k_gemv_mfma_stream(const uint16_t* x, int M, int64_t K, cons
   const int k = (int)K, n = (int)N;
   const bool chunked = KC < k;
   const size_t lds = mfma_stream_lds_bytes(MR, 8, KC, chunked);
-  const int per_cu = lds <= 80 * 1024 ? 2 : 1;
-  const int grid = std::max(1, std::min((n + 15) / 16, per_cu * num_cus()));
+  const int grid = std::max(1, std::min((n + 15) / 16, num_cus()));
   if (MR == 8) {
     if (chunked)
       hipLaunchKernelGGL((q4k_mfma_stream_kernel<8, true>), dim3(grid), dim3(512), lds, s, x, M, k, blocks,
