@@ -655,7 +655,7 @@ def run_extras(torch, B, synth, to_dev, dev, stream, shapes, W, X, gate, fused_s
     ex["small_batch_sym_g32"] = sb
     log(f"small batch {sb}")
 
-    # ---- super-block format GEMV, M = 1, 2, 4, rotating copies ---------------------------
+    # ---- super-block format GEMV, M = 1, 2, 4, 8, 16, rotating copies -------------------
     from oracle import gq_oracle as O
 
     def bits16(t):
@@ -675,7 +675,7 @@ def run_extras(torch, B, synth, to_dev, dev, stream, shapes, W, X, gate, fused_s
         wh = O.q4k_dequantize_fields(O.q4k_decode(bref))
         reps = max(2, int(np.ceil(2 ** 30 / blocks.numel())))
         bl = [blocks] + [blocks.clone() for _ in range(reps - 1)]
-        for m in (1, 2, 4):
+        for m in (1, 2, 4, 8, 16):
             _, x = synth.q4k_case(name, m)
             xd = to_dev(x)
             y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
