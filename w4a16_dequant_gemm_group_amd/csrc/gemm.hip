@@ -673,10 +673,17 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
       if (tid == 0) __hip_atomic_store(flag, launch_id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
+    if (tid == 0) {
+      __hip_atomic_store(arrive, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(flag, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     if (role == 2) {
 #pragma clang fp contract(off)
-      // one accumulator tile (16 values) at a time: hoisting all 128 loads
-      // above their adds would need 128 more registers
+      // One accumulator tile (16 values) at a time: load the partner's 16
+      // partial sums, add, and store that tile's outputs right away.  (Adding
+      // all 128 first and storing after kept every sum live across the
+      // stores, spilled, and made the stores ten times slower than in the
+      // unsplit kernel.)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -686,26 +693,28 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
           for (int v = 0; v < 16; ++v)
             o[v] = __hip_atomic_load(&slot[((i * 2 + j) * 16 + v) * 64], __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
-          // round(a c) + round(a' c'): each half's product is rounded on its own
-          // (contraction off), so the sum does not depend on which half came first
+          const int gn = n0 + lcol0 + 32 * j;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) acc[i][j][v] = acc[i][j][v] * cref[j] + o[v];
+          for (int v = 0; v < 16; ++v) {
+            // round(a c) + round(a' c'): each half's product is rounded on its
+            // own (contraction off), so the sum does not depend on which half
+            // came first
+            const float s_ = acc[i][j][v] * cref[j] + o[v];
+            const int gm = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (gm < M && gn < N) y[(size_t)gm * N + gn] = out16<XF16>(s_);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
-    } else {
-      // never silently wrong: a tile whose other half never arrived is NaN
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_nanf("");
+      return;
     }
-    cref[0] = cref[1] = 1.f;  // acc now holds the true sum
-    if (tid == 0) {
-      __hip_atomic_store(arrive, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(flag, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    // never silently wrong: a tile whose other half never arrived is NaN
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_nanf("");
+    cref[0] = cref[1] = 1.f;
   }
 
   // lane holds column (lane & 31) and rows 8*(v/4) + 4*(lane/32) + v%4 of each MFMA tile
