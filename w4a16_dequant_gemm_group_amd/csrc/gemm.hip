@@ -679,32 +679,34 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
     }
     if (role == 2) {
 #pragma clang fp contract(off)
-      // One accumulator tile (16 values) at a time: load the partner's 16
-      // partial sums, add, and store that tile's outputs right away.  (Adding
-      // all 128 first and storing after kept every sum live across the
-      // stores, spilled, and made the stores ten times slower than in the
-      // unsplit kernel.)
+      // One accumulator tile (16 values) at a time: add the partner's 16
+      // partial sums and store that tile's outputs right away, with the next
+      // tile's partial sums already in flight.  (Adding all 128 first and
+      // storing after kept every sum live across the stores, spilled, and made
+      // the stores ten times slower than in the unsplit kernel.)
+      float o[2][16];
+      auto ld = [&](int q, float* d) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int v = 0; v < 16; ++v)
+          d[v] = __hip_atomic_load(&slot[(q * 16 + v) * 64], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      };
+      ld(0, o[0]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          float o[16];
+      for (int q = 0; q < 8; ++q) {  // q = i * 2 + j
+        const int i = q >> 1, j = q & 1;
+        if (q < 7) ld(q + 1, o[(q + 1) & 1]);
+        const int gn = n0 + lcol0 + 32 * j;
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            o[v] = __hip_atomic_load(&slot[((i * 2 + j) * 16 + v) * 64], __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-          const int gn = n0 + lcol0 + 32 * j;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            // round(a c) + round(a' c'): each half's product is rounded on its
-            // own (contraction off), so the sum does not depend on which half
-            // came first
-            const float s_ = acc[i][j][v] * cref[j] + o[v];
-            const int gm = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            if (gm < M && gn < N) y[(size_t)gm * N + gn] = out16<XF16>(s_);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+        for (int v = 0; v < 16; ++v) {
+          // round(a c) + round(a' c'): each half's product is rounded on its
+          // own (contraction off), so the sum does not depend on which half
+          // came first
+          const float s_ = acc[i][j][v] * cref[j] + o[q & 1][v];
+          const int gm = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          if (gm < M && gn < N) y[(size_t)gm * N + gn] = out16<XF16>(s_);
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
       return;
     }
     // never silently wrong: a tile whose other half never arrived is NaN
