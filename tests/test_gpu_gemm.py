@@ -49,6 +49,24 @@ def test_small_shapes(M, N, K, G, sym):
     assert_parity(bits16(y), ref, O.bf16_to_f64(x), wh, f"gemm [{M}x{N}x{K}] G={G} sym={sym}")
 
 
+@pytest.mark.parametrize("M,N,K,G,sym", [
+    (1000, 12288, 1024, 128, False),   # 4 x 48 = 192 tiles of 256 columns -> 256 of 192
+    (1024, 12288, 1536, 64, True),     # the same with whole row tiles, symmetric g64
+])
+def test_192_column_tiles(M, N, K, G, sym):
+    """Where 256-wide tiles would leave part of the GPU idle without a split
+    and 192-wide ones fill it exactly, the 256-row kernel runs 256 x 192 tiles
+    (waves of 64 x 96): every output against the oracle, ragged M."""
+    w, _ = synth.weights(N, K, seed=N + K + G)
+    x, _ = synth.activations(M, K, seed=M + 3, n_outlier_channels=4)
+    qw, s, z = _oracle_weights(w, G, sym)
+    y = B.gq_w4a16_gemm(bf16_dev(x), u8_dev(qw), f16_dev(s), None if sym else f16_dev(z), G, sym)
+    torch.cuda.synchronize()
+    ref = O.w4a16_reference(x, qw, s, z, G, sym)
+    wh = O.dequantize_packed(qw, s, z, G, sym)
+    assert_parity(bits16(y), ref, O.bf16_to_f64(x), wh, f"gemm [{M}x{N}x{K}] G={G} sym={sym} (192-wide tiles)")
+
+
 @pytest.mark.parametrize("name", synth.SHAPE_ORDER)
 def test_prefill_shapes_full_size(name):
     w, x = synth.prefill_case(name)

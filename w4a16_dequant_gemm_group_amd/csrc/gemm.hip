@@ -420,7 +420,7 @@ struct WStage {
 // the second clears both words, so a graph that replays the same id finds
 // them clear.
 // XF16: fp16 activations and output (fp16 MFMA), otherwise bf16.
-template <bool SYM, int MODE, bool SPLIT, bool XF16 = false>
+template <bool SYM, int MODE, bool SPLIT, bool XF16 = false, bool NARROW = false>
 __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
@@ -430,15 +430,22 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
   __shared__ uint4 sB0[kLN * kLBRow / 8], sB1[kLN * kLBRow / 8];      // 2 x 36 KiB
   __shared__ float sC0[2 * kLN], sC1[2 * kLN];                        // scales per column half
 
+  // NARROW: 256 x 192 tiles, waves 4 (rows) x 2 (columns) of 64 x 96 (2 x 3
+  // MFMA tiles); otherwise 256 x 256 tiles, waves 2 x 4 of 128 x 64 (4 x 2).
+  // The weight stages keep 256 columns; the threads of columns >= 192 load
+  // zeros (range check) and expand them into columns no wave reads.
+  constexpr int TN = NARROW ? 192 : kLN;
+  constexpr int TI = NARROW ? 2 : 4, TJ = NARROW ? 3 : 2;
+  constexpr int WMW = NARROW ? 4 : 2;  // waves along M
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WMW, wn = wave / WMW;
   const int ntm = (M + kLM - 1) / kLM;
   const int split = SPLIT && (int)blockIdx.x >= nt;
   const int lt = (int)blockIdx.x - split * nt;  // tile within the launch: its sync and partial slot
   const int tile_id = tile0 + lt;
   const int m0 = (tile_id % ntm) * kLM;
-  const int n0 = (tile_id / ntm) * kLN;
+  const int n0 = (tile_id / ntm) * TN;
   const int ng = K / G;
   const uint32_t rb = (uint32_t)K / 2;
   // this workgroup's 64-k tiles: [kt0, kt0 + T)
@@ -463,8 +470,8 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
   }
   // Weights: a thread expands column tid/2, k half tid%2 of each tile.
   const int bcol = tid >> 1, bhalf = tid & 1;
-  const uint32_t voB = (uint32_t)bcol * rb + (uint32_t)bhalf * 16u;
-  const uint32_t voS = (uint32_t)(bcol * ng) * 2u + (MODE == 0 && bhalf ? 2u : 0u);
+  const uint32_t voB = bcol < TN ? (uint32_t)bcol * rb + (uint32_t)bhalf * 16u : kOob;
+  const uint32_t voS = bcol < TN ? (uint32_t)(bcol * ng) * 2u + (MODE == 0 && bhalf ? 2u : 0u) : kOob;
 
   auto issueA = [&](uint4* sA, int k0) {
     // scalar offsets stay in SGPRs (a non-uniform soffset turns into a lane loop)
@@ -494,21 +501,21 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
     sC[bhalf * kLN + bcol] = h2f(S.s);
   };
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  float cref[2];
-  const int lcol0 = wn * 64 + (lane & 31);
+  float cref[TJ];
+  const int lcol0 = wn * 32 * TJ + (lane & 31);
 
   // factors moving the running sum from scale cref to the next group's scale
   // (exactly 1 when no group starts here: use = false)
-  auto factors = [&](const float* sC, int half, float (&r)[2], bool use) {
+  auto factors = [&](const float* sC, int half, float (&r)[TJ], bool use) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < TJ; ++j) {
       const float sn = use ? sC[half * kLN + lcol0 + 32 * j] : cref[j];
       const float cn = sn != 0.f ? sn : cref[j];
       r[j] = cref[j] * __builtin_amdgcn_rcpf(cn);  // within 1 ulp of the quotient
@@ -518,7 +525,7 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
 
   // per-lane LDS offsets (uint4 units) of the MFMA operands
   const int fl = swz(lane & 31);
-  const int arow = wm * 128 + (lane & 31);
+  const int arow = wm * 32 * TI + (lane & 31);
   int aoff[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) aoff[ks] = arow * 8 + ((2 * ks + (lane >> 5)) ^ fl);
@@ -529,16 +536,18 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
   auto tile = [&](auto R0c, auto R2c, const uint4* sA, const uint4* sB, const float* sC,
                   const WStage& Wn, uint4* sBn, float* sCn, bool start) {
     constexpr bool R0 = decltype(R0c)::value, R2 = decltype(R2c)::value;
-    float r0[2] = {1.f, 1.f}, r2[2] = {1.f, 1.f};
+    float r0[TJ], r2[TJ];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) r0[j] = r2[j] = 1.f;
     if (R0) factors(sC, 0, r0, start);
     const float m = mult(Wn), nz = negz(Wn, m);
     uint4* dn = sBn + (bcol * kLBRow + bhalf * 32) / 8;
-    opnd8_t<XF16> a[2][4], b[2][2];
+    opnd8_t<XF16> a[2][TI], b[2][TJ];
     auto ld = [&](int ks, int buf) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[buf][i] = __builtin_bit_cast(opnd8_t<XF16>, sA[aoff[ks] + i * 32 * 8]);
+      for (int i = 0; i < TI; ++i) a[buf][i] = __builtin_bit_cast(opnd8_t<XF16>, sA[aoff[ks] + i * 32 * 8]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < TJ; ++j)
         b[buf][j] = __builtin_bit_cast(opnd8_t<XF16>, sB[boff + ks * 2 + j * 32 * kLBRow / 8]);
     };
     ld(0, 0);
@@ -550,9 +559,9 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
       const uint32_t word = ks == 0 ? Wn.b.x : ks == 1 ? Wn.b.y : ks == 2 ? Wn.b.z : Wn.b.w;
       const uint4 e = expand8m<XF16>(word, m, nz);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < TJ; ++j) {
           if (R0 && ks == 0) acc[i][j] *= r0[j];
           if (R2 && ks == 2) acc[i][j] *= r2[j];
           acc[i][j] = mfma32<XF16>(a[ks & 1][i], b[ks & 1][j], acc[i][j]);
@@ -560,10 +569,11 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
       dn[ks] = e;
       // the next step's LDS reads first, then every MFMA behind its share of the
       // vector work (its accumulator's rescale, the expansion)
-      if (ks < 3) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+      constexpr int kX = (24 + TI * TJ - 1) / (TI * TJ);  // expansion instructions per MFMA
+      if (ks < 3) __builtin_amdgcn_sched_group_barrier(0x100, TI + TJ, 0);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x2, RS ? 19 : 3, 0);
+      for (int q = 0; q < TI * TJ; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x2, RS ? 16 + kX : kX, 0);
         __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -599,7 +609,7 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
   expand_all(w0, sB0, sC0);
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < TJ; ++j) {
     const float c0 = sC0[lcol0 + 32 * j];
     cref[j] = c0 != 0.f ? c0 : 1.f;  // the first tile's factors are then 1
   }
@@ -661,12 +671,12 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
     const uint32_t role = s_role;
     if (role == 1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
           for (int v = 0; v < 16; ++v)
-            __hip_atomic_store(&slot[((i * 2 + j) * 16 + v) * 64], acc[i][j][v] * cref[j],
+            __hip_atomic_store(&slot[((i * TJ + j) * 16 + v) * 64], acc[i][j][v] * cref[j],
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       wait_vm<0>();
       __syncthreads();
@@ -692,9 +702,9 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
       };
       ld(0, o[0]);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {  // q = i * 2 + j
-        const int i = q >> 1, j = q & 1;
-        if (q < 7) ld(q + 1, o[(q + 1) & 1]);
+      for (int q = 0; q < TI * TJ; ++q) {  // q = i TJ + j
+        const int i = q / TJ, j = q % TJ;
+        if (q < TI * TJ - 1) ld(q + 1, o[(q + 1) & 1]);
         const int gn = n0 + lcol0 + 32 * j;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -702,7 +712,7 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
           // own (contraction off), so the sum does not depend on which half
           // came first
           const float s_ = acc[i][j][v] * cref[j] + o[q & 1][v];
-          const int gm = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int gm = m0 + wm * 32 * TI + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           if (gm < M && gn < N) y[(size_t)gm * N + gn] = out16<XF16>(s_);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -711,23 +721,24 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
     }
     // never silently wrong: a tile whose other half never arrived is NaN
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < TJ; ++j) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_nanf("");
-    cref[0] = cref[1] = 1.f;
+        cref[j] = 1.f;
+      }
   }
 
   // lane holds column (lane & 31) and rows 8*(v/4) + 4*(lane/32) + v%4 of each MFMA tile
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < TJ; ++j) {
       const int gn = n0 + lcol0 + 32 * j;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int gm = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int gm = m0 + wm * 32 * TI + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (gm < M && gn < N) {
           const float v_ = acc[i][j][v] * cref[j];
           y[(size_t)gm * N + gn] = out16<XF16>(v_);
@@ -736,13 +747,25 @@ __global__ __launch_bounds__(kLT, 1) void w4a16_gemm_lds_kernel(
     }
 }
 
+// Tile width of the 256-row kernel: 192 when 256-wide tiles would run more
+// than half of the compute units but leave part of a round idle (too many to
+// split in two) while 192-wide tiles fill whole rounds exactly (qkv at
+// M = 2048: 192 tiles of 256 columns, 256 of 192); else 256.
+int lds_tile_n(int M, int N) {
+  const int64_t ntm = (M + kLM - 1) / kLM, cus = num_cus();
+  const int64_t t256 = ntm * ((N + kLN - 1) / kLN), t192 = ntm * ((N + 191) / 192);
+  if (N % 192 == 0 && 2 * t256 > cus && t256 % cus != 0 && t192 % cus == 0) return 192;
+  return kLN;
+}
+
 // Split K in two for the tiles of a round that fills at most half of the
 // compute units: all tiles when there are at most half as many as compute
 // units, else the last partial round (launched after the full rounds, so its
 // 2r half-tile workgroups run side by side).  Each half keeps at least two
 // groups' worth of 64-k tiles.  Returns the number of split tiles (0: no split).
 int64_t split_tail(int M, int K, int N, int G, int64_t cus, int* tsplit) {
-  const int64_t tiles = (int64_t)((M + kLM - 1) / kLM) * ((N + kLN - 1) / kLN);
+  const int tn = lds_tile_n(M, N);
+  const int64_t tiles = (int64_t)((M + kLM - 1) / kLM) * ((N + tn - 1) / tn);
   const int T = K / kBK;
   const int tpg = G >= kBK ? G / kBK : 1;  // 64-k tiles per group
   *tsplit = (T / 2) / std::max(tpg, 2) * std::max(tpg, 2);
@@ -769,10 +792,11 @@ int split_poll_limit() {
 
 // ws: scratch of at least split_bytes(split_tail(...)) bytes, or NULL: the
 // tiles then all run unsplit.
-template <bool SYM, int MODE, bool XF16 = false>
-hipError_t launch_lds(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
+template <bool SYM, int MODE, bool XF16, bool NARROW>
+hipError_t launch_lds_t(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
                       const uint16_t* zr, int N, int G, uint16_t* y, void* ws, hipStream_t s) {
-  const int64_t tiles = (int64_t)((M + kLM - 1) / kLM) * ((N + kLN - 1) / kLN);
+  constexpr int TN = NARROW ? 192 : kLN;
+  const int64_t tiles = (int64_t)((M + kLM - 1) / kLM) * ((N + TN - 1) / TN);
   int tsplit = 0;
   const int64_t tail = ws ? split_tail(M, K, N, G, num_cus(), &tsplit) : 0;
   if (tail > 0) {
@@ -780,20 +804,27 @@ hipError_t launch_lds(const uint16_t* x, int M, int K, const uint8_t* qw, const 
     float* part = (float*)((char*)ws + split_sync_bytes(tail));
     const int64_t full = tiles - tail;  // a multiple of the CU count: whole rounds
     if (full > 0) {
-      hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE, false, XF16>), dim3((unsigned)full),
+      hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE, false, XF16, NARROW>), dim3((unsigned)full),
                          dim3(kLT), 0, s, x, M, K, qw, sc, zr, N, G, y, nullptr, nullptr, 0, 0,
                          (int)full, (uint64_t)0, 0);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE, true, XF16>), dim3((unsigned)(2 * tail)),
+    hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE, true, XF16, NARROW>), dim3((unsigned)(2 * tail)),
                        dim3(kLT), 0, s, x, M, K, qw, sc, zr, N, G, y, sync, part, tsplit,
                        (int)full, (int)tail, next_launch_id(), split_poll_limit());
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE, false, XF16>), dim3((unsigned)tiles), dim3(kLT), 0,
+  hipLaunchKernelGGL((w4a16_gemm_lds_kernel<SYM, MODE, false, XF16, NARROW>), dim3((unsigned)tiles), dim3(kLT), 0,
                      s, x, M, K, qw, sc, zr, N, G, y, nullptr, nullptr, 0, 0, (int)tiles, (uint64_t)0, 0);
   return hipGetLastError();
+}
+
+template <bool SYM, int MODE, bool XF16 = false>
+hipError_t launch_lds(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
+                      const uint16_t* zr, int N, int G, uint16_t* y, void* ws, hipStream_t s) {
+  if (lds_tile_n(M, N) == 192) return launch_lds_t<SYM, MODE, XF16, true>(x, M, K, qw, sc, zr, N, G, y, ws, s);
+  return launch_lds_t<SYM, MODE, XF16, false>(x, M, K, qw, sc, zr, N, G, y, ws, s);
 }
 
 // Boundary pattern of the 256 x 256 kernel for this group size, or -1.
