@@ -135,6 +135,30 @@ def load_traffic():
 
 
 # ----------------------------------------------------------------------------
+# issue-rate probes: the GPU facts behind the kernels' instruction scheduling
+# ----------------------------------------------------------------------------
+
+def run_probes(torch, B, iters=2000):
+    """Per-wave loop cycles of the two probes in libgq (include/gq_bench.h), one
+    workgroup per compute unit: cycles per iteration of 8 independent
+    v_mfma_f32_32x32x16_bf16 with 0/32/64/128 fp32 FMAs behind them (two waves
+    per SIMD), and LDS bytes per clock of a compute unit for 16-byte reads with
+    4, 8 and 16 waves (the slowest wave of each workgroup sets its time)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = {"compute_units": cus, "iterations": iters,
+           "mfma_valu": {"what": "s_memtime cycles per iteration of one wave (8 MFMAs + n FMAs), median over waves"},
+           "lds_read": {"what": "LDS bytes per clock of a compute unit, median over workgroups"}}
+    for valu in (0, 32, 64, 128):
+        c = B.gq_probe_mfma_valu(valu, iters, cus).cpu().numpy()
+        out["mfma_valu"][f"fma_{valu}"] = round(float(np.median(c)) / iters, 1)
+    for waves in (4, 8, 16):
+        c = B.gq_probe_lds_read(waves, iters, cus).cpu().numpy().reshape(cus, waves)
+        bpc = waves * iters * 16 * 1024 / c.max(axis=1)
+        out["lds_read"][f"waves_{waves}"] = round(float(np.median(bpc)), 1)
+    return out
+
+
+# ----------------------------------------------------------------------------
 
 def main():
     ap = argparse.ArgumentParser()
@@ -149,6 +173,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--profile-pass", action="store_true",
                     help="run a few decode steps and one calibration copy, for rocprofv3 --pmc")
+    ap.add_argument("--probes", action="store_true",
+                    help="run the issue-rate probes (MFMA with vector work, LDS reads) and print their JSON")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="reduce two rocprofv3 --pmc passes of --profile-pass to per-launch bytes")
     args = ap.parse_args()
@@ -189,6 +215,9 @@ def main():
     torch.cuda.synchronize()
     Y = {nm: torch.empty((1, n), dtype=torch.bfloat16, device=dev) for nm, n, _ in shapes}
 
+    if args.probes:
+        print(json.dumps(run_probes(torch, B)), flush=True)
+        return
     if args.profile_pass:
         for _ in range(3):
             for nm, _, _ in shapes:

@@ -1,7 +1,8 @@
 /*
  * gq_bench.h - comparators and probes exported by libgq beside the quantized
- * path of gq.h.  Nothing here quantizes: these are the 16-bit baseline and the
- * bandwidth ceiling that the 4-bit kernels are measured against.
+ * path of gq.h.  Nothing here quantizes: these are the 16-bit baseline, the
+ * bandwidth ceiling that the 4-bit kernels are measured against, and two
+ * issue-rate probes of the GPU facts the kernels are designed around.
  *
  *   [P1] "vLLM 量化与推测解码：怎样减少容量、带宽与串行轮次", section 2: at
  *        decode every weight is read once per token, so the time follows the
@@ -47,6 +48,26 @@ gq_status gq_bf16_gemv(const uint16_t* x, int64_t M, int64_t K, const uint16_t* 
  * MISALIGNED (buf not 16-byte aligned, sink not 4-byte aligned), UNSUPPORTED
  * (device). */
 gq_status gq_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
+/* Issue-rate probe of the matrix cores and the vector ALU: `grid` workgroups of
+ * 512 threads (two waves per SIMD) each run `iters` iterations in which every
+ * wave issues 8 independent v_mfma_f32_32x32x16_bf16, each followed by
+ * valu / 8 independent fp32 FMAs; wave w of workgroup g writes its loop's
+ * s_memtime cycle count to cycles[8 g + w].  valu in {0, 32, 64, 128};
+ * 1 <= iters <= 2^20, 1 <= grid <= 65536.  cycles (8-byte aligned, 8 grid
+ * entries) and sink (4-byte aligned, never read, written only in a rare case)
+ * are device pointers.  Errors: INVALID_ARG, MISALIGNED, UNSUPPORTED (device). */
+gq_status gq_probe_mfma_valu(int32_t valu, int32_t iters, int32_t grid, uint64_t* cycles, float* sink,
+                             void* stream);
+
+/* LDS read probe: `grid` workgroups of `waves` waves (1..16) each fill a
+ * 64 KiB LDS buffer and then run `iters` iterations of 16 independent
+ * conflict-free 16-byte reads per lane; wave w of workgroup g writes its
+ * loop's s_memtime cycle count to cycles[waves g + w].  LDS bytes per clock
+ * of a compute unit = waves * iters * 16 KiB / cycles when one workgroup
+ * runs per compute unit.  Limits and errors as gq_probe_mfma_valu. */
+gq_status gq_probe_lds_read(int32_t waves, int32_t iters, int32_t grid, uint64_t* cycles, float* sink,
+                            void* stream);
 
 #ifdef __cplusplus
 }

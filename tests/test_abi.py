@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
     for n in names:
         assert hasattr(lib, n), n
     bench = header_functions(BENCH_HEADER)
-    assert set(bench) == set(B.BENCH_EXPORTS) and len(bench) == 2
+    assert set(bench) == set(B.BENCH_EXPORTS) and len(bench) == 4
     for n in bench:
         assert hasattr(lib, n), n
 
@@ -172,6 +172,15 @@ def test_bench_entry_point_validation(lib):
     assert L.gq_stream_read(FAKE, 64, ctypes.c_void_p(4098), None) == B.GQ_ERR_MISALIGNED
     assert L.gq_stream_read(FAKE, 64, None, None) == B.GQ_ERR_INVALID_ARG
     assert L.gq_stream_read(None, 0, None, None) == B.GQ_OK
+    # issue-rate probes: fixed vector-work counts, bounded iterations and grid, alignment
+    assert L.gq_probe_mfma_valu(16, 10, 1, FAKE, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_probe_mfma_valu(32, 0, 1, FAKE, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_probe_mfma_valu(32, 10, 0, FAKE, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_probe_mfma_valu(32, 10, 1, None, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_probe_mfma_valu(32, 10, 1, ctypes.c_void_p(4100), FAKE, None) == B.GQ_ERR_MISALIGNED
+    assert L.gq_probe_lds_read(17, 10, 1, FAKE, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_probe_lds_read(8, (1 << 20) + 1, 1, FAKE, FAKE, None) == B.GQ_ERR_INVALID_ARG
+    assert L.gq_probe_lds_read(8, 10, 1, FAKE, ctypes.c_void_p(4098), None) == B.GQ_ERR_MISALIGNED
 
 
 

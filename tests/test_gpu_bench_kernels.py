@@ -75,3 +75,20 @@ def test_unfused_dequantize_then_bf16_gemv(M, sym, G):
     x64 = O.bf16_to_f64(x)
     ok, rel, ratio = O.within_parity(bf16_out_to_f64(y), x64 @ wh_b.T, x64, wh_b)
     assert ok, (rel, ratio)
+
+
+def test_issue_rate_probes():
+    """The matrix-core / vector-ALU and LDS probes run and report plausible
+    per-wave loop cycles: at least 16 cycles per MFMA of the loop, not fewer
+    when vector work is added, and LDS reads below 256 bytes per clock."""
+    announce("issue-rate probes")
+    iters = 200
+    base = B.gq_probe_mfma_valu(0, iters, 4).cpu().numpy()
+    more = B.gq_probe_mfma_valu(128, iters, 4).cpu().numpy()
+    assert np.all(base > 0) and np.all(more > 0)
+    assert np.median(base) / iters >= 8 * 16
+    assert np.median(more) >= np.median(base) * 0.95
+    waves = 8
+    lds = B.gq_probe_lds_read(waves, iters, 4).cpu().numpy().reshape(4, waves)
+    bpc = waves * iters * 16 * 1024 / lds.max(axis=1)
+    assert np.all(bpc > 8) and np.all(bpc < 256), bpc

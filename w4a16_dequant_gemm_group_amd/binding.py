@@ -31,7 +31,7 @@ EXPORTS = (
     "gq_w4a16_gemv_f16", "gq_w4a16_gemv_f16_ws", "gq_w4a16_gemm_f16", "gq_w4a16_gemm_f16_ws",
 )
 # comparators and probes (include/gq_bench.h)
-BENCH_EXPORTS = ("gq_bf16_gemv", "gq_stream_read")
+BENCH_EXPORTS = ("gq_bf16_gemv", "gq_stream_read", "gq_probe_mfma_valu", "gq_probe_lds_read")
 
 
 class GqQParams(ctypes.Structure):
@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
         "gq_w4a16_gemm_f16": mm,
         "gq_w4a16_gemm_f16_ws": mm_ws,
         "gq_stream_read": [p, i64, p, p],
+        "gq_probe_mfma_valu": [i32, i32, i32, p, p, p],
+        "gq_probe_lds_read": [i32, i32, i32, p, p, p],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -447,6 +449,28 @@ def gq_stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     _on_device(buf.device, sink=sink)
     nbytes = buf.numel() * buf.element_size()
     _ok(lib().gq_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "gq_stream_read")
+
+
+def gq_probe_mfma_valu(valu: int, iters: int, grid: int, stream=None) -> torch.Tensor:
+    """Per-wave loop cycles [grid * 8] (int64, on the current device) of the
+    matrix-core / vector-ALU issue probe (include/gq_bench.h)."""
+    dev = torch.device("cuda", torch.cuda.current_device())
+    cycles = torch.zeros(grid * 8, dtype=torch.int64, device=dev)
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    _ok(lib().gq_probe_mfma_valu(valu, iters, grid, _ptr(cycles), _ptr(sink), _stream(stream)),
+        "gq_probe_mfma_valu")
+    return cycles
+
+
+def gq_probe_lds_read(waves: int, iters: int, grid: int, stream=None) -> torch.Tensor:
+    """Per-wave loop cycles [grid * waves] (int64, on the current device) of the
+    LDS read probe (include/gq_bench.h)."""
+    dev = torch.device("cuda", torch.cuda.current_device())
+    cycles = torch.zeros(grid * waves, dtype=torch.int64, device=dev)
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    _ok(lib().gq_probe_lds_read(waves, iters, grid, _ptr(cycles), _ptr(sink), _stream(stream)),
+        "gq_probe_lds_read")
+    return cycles
 
 
 def gq_ingest_group_major(codes: torch.Tensor, scales: torch.Tensor, qweight=None, scales_out=None,

@@ -7,7 +7,10 @@
 //     weight in HBM, then multiply" ("量化" chapter, "亲手实现", the paragraph
 //     on the common pitfall of materializing the weight);
 //   - an HBM stream read: the read bandwidth one kernel reaches on this GPU,
-//     the practical ceiling for every weight-streaming kernel.
+//     the practical ceiling for every weight-streaming kernel;
+//   - two issue-rate probes behind the kernels' design: how many vector
+//     instructions hide behind matrix-core instructions, and how fast 16-byte
+//     LDS reads go (each wave times its own loop with s_memtime).
 #include "gq_internal.h"
 
 namespace gq {
@@ -144,6 +147,83 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restr
   if (a == 0x2545F491u) sink[0] = a;
 }
 
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// Per iteration every wave issues 8 independent v_mfma_f32_32x32x16_bf16 (one
+// per accumulator), each followed by VALU / 8 independent fp32 FMAs (16
+// chains).  512 threads: two waves per SIMD.
+template <int VALU>
+__global__ __launch_bounds__(512, 1) void mfma_valu_probe_kernel(int iters, uint64_t* __restrict__ cycles,
+                                                                   float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float seed = (float)(lane + 1) * 1e-3f;
+  bf16x8_t a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(seed * (float)(i + 1));
+    b[i] = (__bf16)(seed - 1e-4f * (float)i);
+  }
+  f32x16_t acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[k][v] = 0.f;
+  float r[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) r[j] = seed * (float)j;
+  constexpr int kPer = VALU / 8;  // FMAs behind each MFMA
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[k], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) r[(k * kPer + j) & 15] = fmaf(r[(k * kPer + j) & 15], 0.999f, 1e-6f);
+      __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
+      if (kPer > 0) __builtin_amdgcn_sched_group_barrier(0x2, kPer, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  float sum = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sum += acc[k][v];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) sum += r[j];
+  if (lane == 0) cycles[(size_t)blockIdx.x * (blockDim.x / 64) + wave] = t1 - t0;
+  if (sum == 1234.5f) sink[0] = sum;  // keeps the work; (almost) never stores
+}
+
+// Each wave reads 16 independent 16-byte words per iteration from a 64 KiB LDS
+// buffer (64 consecutive words per wave-wide read: no bank conflicts) and
+// folds them into a value that is stored only in the rare case that it equals
+// a constant.
+__global__ __launch_bounds__(1024, 1) void lds_read_probe_kernel(int iters, uint64_t* __restrict__ cycles,
+                                                                  float* __restrict__ sink) {
+  __shared__ uint4 buf[4096];
+  for (int i = threadIdx.x; i < 4096; i += blockDim.x)
+    buf[i] = make_uint4((uint32_t)i, (uint32_t)i * 3u, (uint32_t)i * 5u, (uint32_t)i * 7u);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = 0;
+  int base = (wave * 64 + lane) & 4095;
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const uint4 v = buf[(base + u * 256) & 4095];
+      x ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    base = (base + 64) & 4095;
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  if (lane == 0) cycles[(size_t)blockIdx.x * (blockDim.x / 64) + wave] = t1 - t0;
+  if (x == 0x12345678u) sink[0] = 1.f;
+}
 }  // namespace
 
 int bf16_gemv_kpad(int64_t K) {
@@ -172,6 +252,24 @@ hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hi
   const int64_t per_wg = 256 * kReadUnroll;
   const int64_t blocks = (n16 + per_wg - 1) / per_wg;
   stream_read_kernel<<<dim3((unsigned)blocks), 256, 0, s>>>((const u32x4_t*)buf, n16, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_mfma_valu(int valu, int iters, int grid, uint64_t* cycles, float* sink,
+                                  hipStream_t s) {
+  switch (valu) {
+    case 0: mfma_valu_probe_kernel<0><<<grid, 512, 0, s>>>(iters, cycles, sink); break;
+    case 32: mfma_valu_probe_kernel<32><<<grid, 512, 0, s>>>(iters, cycles, sink); break;
+    case 64: mfma_valu_probe_kernel<64><<<grid, 512, 0, s>>>(iters, cycles, sink); break;
+    case 128: mfma_valu_probe_kernel<128><<<grid, 512, 0, s>>>(iters, cycles, sink); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_lds_read(int waves, int iters, int grid, uint64_t* cycles, float* sink,
+                                 hipStream_t s) {
+  lds_read_probe_kernel<<<grid, waves * 64, 0, s>>>(iters, cycles, sink);
   return hipGetLastError();
 }
 

@@ -389,4 +389,26 @@ gq_status gq_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* s
   return from_hip(gq::launch_stream_read(buf, bytes, sink, s));
 }
 
+gq_status gq_probe_mfma_valu(int32_t valu, int32_t iters, int32_t grid, uint64_t* cycles, float* sink,
+                             void* stream) {
+  if (valu != 0 && valu != 32 && valu != 64 && valu != 128) return GQ_ERR_INVALID_ARG;
+  if (iters < 1 || iters > (1 << 20) || grid < 1 || grid > 65536 || !cycles || !sink)
+    return GQ_ERR_INVALID_ARG;
+  if (((uintptr_t)cycles & 7u) || ((uintptr_t)sink & 3u)) return GQ_ERR_MISALIGNED;
+  hipStream_t s = (hipStream_t)stream;
+  if (gq_status st = check_device(s)) return st;
+  return from_hip(gq::launch_probe_mfma_valu(valu, iters, grid, cycles, sink, s));
+}
+
+gq_status gq_probe_lds_read(int32_t waves, int32_t iters, int32_t grid, uint64_t* cycles, float* sink,
+                            void* stream) {
+  if (waves < 1 || waves > 16 || iters < 1 || iters > (1 << 20) || grid < 1 || grid > 65536 ||
+      !cycles || !sink)
+    return GQ_ERR_INVALID_ARG;
+  if (((uintptr_t)cycles & 7u) || ((uintptr_t)sink & 3u)) return GQ_ERR_MISALIGNED;
+  hipStream_t s = (hipStream_t)stream;
+  if (gq_status st = check_device(s)) return st;
+  return from_hip(gq::launch_probe_lds_read(waves, iters, grid, cycles, sink, s));
+}
+
 }  // extern "C"

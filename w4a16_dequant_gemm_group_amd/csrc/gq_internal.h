@@ -164,5 +164,9 @@ int bf16_gemv_kpad(int64_t K);
 hipError_t launch_bf16_gemv(const uint16_t* x, int M, int64_t K, const uint16_t* w, int64_t N,
                             uint16_t* y, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
+hipError_t launch_probe_mfma_valu(int valu, int iters, int grid, uint64_t* cycles, float* sink,
+                                  hipStream_t s);
+hipError_t launch_probe_lds_read(int waves, int iters, int grid, uint64_t* cycles, float* sink,
+                                 hipStream_t s);
 
 }  // namespace gq
