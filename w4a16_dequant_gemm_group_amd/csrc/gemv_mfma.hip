@@ -379,9 +379,14 @@ __device__ __forceinline__ uint16_t ms_half(const uint32_t* v, int j) {
 // empty ones: zero weights, no stores) so that all meet at the same barriers.
 // One team with 8 staged rows and 8 waves runs two workgroups per compute
 // unit: the launch bounds then ask for four waves per SIMD (at most 128
-// registers).
+// registers) — except with asymmetric group-32 weights, whose register stages
+// (16 scale and 16 zero halves per item) would spill there: one workgroup.
 template <int MR, int NW, int GQ, bool SYM, bool CHUNKED, bool XF16, int TM>
-__global__ __launch_bounds__(NW * 64 * TM, TM == 1 && MR == 8 && NW == 8 && !CHUNKED ? 4 : 1) void
+constexpr bool ms_two_per_cu() {
+  return TM == 1 && MR == 8 && NW == 8 && !CHUNKED && !(GQ == 0 && !SYM);
+}
+template <int MR, int NW, int GQ, bool SYM, bool CHUNKED, bool XF16, int TM>
+__global__ __launch_bounds__(NW * 64 * TM, (ms_two_per_cu<MR, NW, GQ, SYM, CHUNKED, XF16, TM>() ? 4 : 1)) void
 gemv_mfma_stream_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
@@ -824,7 +829,7 @@ hipError_t launch_ms(const uint16_t* x, int M, int K, int KC, const uint8_t* qw,
   const int nb = (N + 15) / 16;
   const bool teams = MR == 16 && KC >= K && lds2 <= kMSTeamLds && nb >= 2 * num_cus() &&
                      !(!SYM && G == 32);
-  const int per_cu = lds <= 80 * 1024 ? 2 : 1;
+  const int per_cu = lds <= 80 * 1024 && !(!SYM && G == 32) ? 2 : 1;
   const int grid = teams ? std::max(1, std::min((nb + 1) / 2, num_cus()))
                          : std::max(1, std::min(nb, per_cu * num_cus()));
 #define GQ_MS_LAUNCH(GQ_)                                                                         \
@@ -832,7 +837,7 @@ hipError_t launch_ms(const uint16_t* x, int M, int K, int KC, const uint8_t* qw,
     hipLaunchKernelGGL((gemv_mfma_stream_kernel<MR, NW, GQ_, SYM, true, XF16, 1>), dim3(grid),    \
                        dim3(NW * 64), lds, s, x, M, K, qw, sc, zr, N, G, y, KC);                  \
   else if (MR == 16 && teams)                                                                     \
-    hipLaunchKernelGGL((gemv_mfma_stream_kernel<MR, NW, GQ_, SYM, false, XF16, MR == 16 ? 2 : 1>),\
+    hipLaunchKernelGGL((gemv_mfma_stream_kernel<MR, NW, GQ_, SYM, false, XF16, MR == 16 && (SYM || GQ_ != 0) ? 2 : 1>),\
                        dim3(grid), dim3(NW * 128), lds2, s, x, M, K, qw, sc, zr, N, G, y, KC);    \
   else                                                                                            \
     hipLaunchKernelGGL((gemv_mfma_stream_kernel<MR, NW, GQ_, SYM, false, XF16, 1>), dim3(grid),   \
