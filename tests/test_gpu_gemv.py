@@ -347,3 +347,26 @@ def test_mfma_stream_tiny_row_counts(M, N):
     w, x = synth.small(N, K, M, seed=N * 31 + M)
     qw, s, z = _oracle_weights(w, G, False)
     _run(x, qw, s, z, G, False, f"[{N},{K}] M={M} asym G={G} (matrix cores, streaming)")
+
+
+@pytest.mark.parametrize("M", [5, 7, 12, 16])
+@pytest.mark.parametrize("K", [512, 1024, 2048])
+@pytest.mark.parametrize("sym,G", [(True, 32), (False, 64), (False, 128), (True, 256), (False, 512)])
+def test_xreg_k_extents(M, K, sym, G):
+    # x held in registers: one 512-wide column range per wave, K / 512 waves
+    # per workgroup (1, 2, 4), a partial last row block (77 rows)
+    assert B.gq_w4a16_gemv_workspace_size(M, K, 77, G, sym) == 0
+    w, x = synth.small(77, K, M, seed=M * 101 + K + G)
+    qw, s, z = _oracle_weights(w, G, sym)
+    _run(x, qw, s, z, G, sym, f"[77,{K}] M={M} sym={sym} G={G} (x in registers)")
+
+
+@pytest.mark.parametrize("M,N,K", [(9, 100003, 512), (6, 70001, 1024), (16, 36001, 2048)])
+def test_xreg_many_row_blocks(M, N, K):
+    # more row blocks than the grid has workgroups: every workgroup runs
+    # several items, including the two-item tail, and alternates its tile
+    # buffers; checked on the first, middle and last rows
+    w, x = synth.small(N, K, M, seed=N + M)
+    qw, s, z = _oracle_weights(w, 128, False)
+    rows = np.r_[0:64, N // 2:N // 2 + 64, N - 67:N]
+    _run(x, qw, s, z, 128, False, f"[{N},{K}] M={M} asym G=128 (x in registers, many rows)", rows=rows)

@@ -339,14 +339,16 @@ __device__ __forceinline__ void ms_load(MsBuf<GQ, SYM>& B, int rb, int k0, int n
   const uint32_t wo = rin ? (uint32_t)row * rbytes + (uint32_t)(k0 + 32 * g) / 2 : kOob;
 #pragma unroll
   for (int L = 0; L < 4; ++L) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, wo, rin ? 64u * L : 0u, 2);
+    // the step in the lane offset (kOob + 192 is still out of range); a
+    // lane-dependent scalar offset would need a waterfall loop per load
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, wo + 64u * L, 0, 2);
     B.w[L] = make_uint4(v[0], v[1], v[2], v[3]);
   }
   const uint32_t so = rin ? ((uint32_t)row * (uint32_t)(K / G) + (uint32_t)(k0 / G)) * 2u : kOob;
   auto ld = [&](rsrc_t r, uint32_t* d) {
     if constexpr (GQ == 0) {
       const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, so, 0, 0);
-      const auto b = __builtin_amdgcn_raw_buffer_load_b128(r, so, rin ? 16u : 0u, 0);
+      const auto b = __builtin_amdgcn_raw_buffer_load_b128(r, so + 16u, 0, 0);
       d[0] = a[0]; d[1] = a[1]; d[2] = a[2]; d[3] = a[3];
       d[4] = b[0]; d[5] = b[1]; d[6] = b[2]; d[7] = b[3];
     } else if constexpr (GQ == 1) {
@@ -568,6 +570,173 @@ gemv_mfma_stream_kernel(
     for (int j = 0; j < 3; ++j) {
       if (i + 2 < items)
         ms_load<GQ, SYM>(buf[(j + 2) % 3], item_rb(i + 2), item_k0(i + 2), n, g, N, K, G, rw, rs, rz);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(buf[j], i);
+      ++i;
+    }
+  }
+  if (rest > 0) compute(buf[0], i++);
+  if (rest > 1) compute(buf[1], i++);
+}
+
+constexpr int kXrGroup = 8;  // row blocks per group (the waves meet once per group)
+
+// Small-batch GEMV with the activations in registers (5 <= M <= 16, K = 512 NW
+// for NW = 1..8 waves): the product, operands and MFMAs of
+// gemv_mfma_stream_kernel, but wave w always covers the same 512 columns
+// [512 w, 512 w + 512) of every row block, so the A operands of its 16
+// 32-wide chunks (16 bytes per lane and chunk, 64 registers) are loaded from x
+// once, permuted into the pair order of the nibble unpack, and kept for the
+// whole launch: no x in LDS, no LDS reads or address arithmetic per MFMA, no
+// staging barrier.  The zero-point term goes to the matrix cores as in the
+// super-block kernel:
+//   acc[m][n] = sum_c S_c (D_c[m][n] - (128 + z_c) sx[m][c])
+//             = sum_c S_c D_c[m][n]  +  sum_c sx[m][c] T[c][n],   T = -S (128 + z),
+// the second sum over the four chunks of a 128-wide step being one
+// v_mfma_f32_16x16x4f32 (fp32): lane (n, g) supplies the sum over chunk g of
+// activation row n (kept in a register with the operands) and T of weight row
+// n, chunk g.  Each row block is one item per wave (16 rows x 512 columns,
+// 4 KiB), two items in flight; each wave leaves its 16 x 16 tile of a row
+// block in an LDS slot, and only once per group of eight row blocks do the
+// waves meet at a barrier, after which the workgroup adds each row block's
+// tiles in wave order and stores y, rounded once (two sets of slots, so the
+// next group's tiles cannot meet this group's reads).  A barrier per row
+// block made every row block wait for the workgroup's slowest wave.
+template <int NW, int GQ, bool SYM, bool XF16>
+__global__ __launch_bounds__(NW * 64, 2) void gemv_mfma_xreg_kernel(
+    const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
+    uint16_t* __restrict__ y) {
+  constexpr int CPG = GQ >= 2 ? 4 : (1 << GQ);  // 32-chunks per correction segment
+  // partial tiles [slot][wave][lane][4]: two sets of kXrGroup item slots
+  __shared__ float red[2 * kXrGroup * NW * 256];
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int NB = (N + 15) / 16;
+  const int k0 = w * kMSItem;  // K == NW * 512
+  const rsrc_t rw = make_rsrc(qw, (uint32_t)N * (uint32_t)(K / 2));
+  const rsrc_t rs = make_rsrc(scales, (uint32_t)N * (uint32_t)(K / G) * 2);
+  const rsrc_t rz = make_rsrc(SYM ? (const void*)scales : (const void*)zeros, (uint32_t)N * (uint32_t)(K / G) * 2);
+  const int items = (int)blockIdx.x < NB ? (NB - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  auto item_rb = [&](int i) { return (int)blockIdx.x + i * (int)gridDim.x; };
+
+  // x first (loads retire in order: the weight prefetch behind them does not
+  // hold up the operand set-up); rows >= M read zero.  (Staging x through LDS
+  // with coalesced loads and a barrier measured slower: every wave then waits
+  // for the slowest one's loads.)
+  const rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+  uint4 xa[4][4];  // [step L][chunk c]: x[n][k0 + 128 L + 32 c + 8 g .. + 8), permuted
+#pragma unroll
+  for (int L = 0; L < 4; ++L)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t off = n < M ? ((uint32_t)n * (uint32_t)K + (uint32_t)(k0 + 128 * L + 32 * c + 8 * g)) * 2u : kOob;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+      xa[L][c] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  MsBuf<GQ, SYM> buf[3];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    if (j < items) ms_load<GQ, SYM>(buf[j], item_rb(j), k0, n, g, N, K, G, rw, rs, rz);
+  // chunk sums of row n: lane (n, g) holds 8 of each chunk's 32 values (a
+  // partial sum p_c per chunk c); the 4 x 4 transpose across the lane rows
+  // gives lane (n, g) the four partials of chunk g, whose sum it keeps
+  float sxa[4];
+#pragma unroll
+  for (int L = 0; L < 4; ++L) {
+    uint32_t p[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 v = xa[L][c];
+      float s = dot2x<XF16>(v.x, 0.f);
+      s = dot2x<XF16>(v.y, s);
+      s = dot2x<XF16>(v.z, s);
+      s = dot2x<XF16>(v.w, s);
+      p[c] = __builtin_bit_cast(uint32_t, s);
+      xa[L][c] = perm_x(v);
+    }
+    transpose4(p[0], p[1], p[2], p[3]);
+    sxa[L] = (__builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1])) +
+             (__builtin_bit_cast(float, p[2]) + __builtin_bit_cast(float, p[3]));
+  }
+
+  const uint32_t magic = XF16 ? 0x64006400u : 0x43004300u;  // 1024 + q or 128 + q
+  constexpr float kOff = XF16 ? 1024.f : 128.f;
+  // byte selector of the scale (and zero) half of chunk g of a step within
+  // its two words (group 32: word 2L + g / 2; group 64: word L, half g / 2)
+  const uint32_t hsel = GQ == 0 ? (uint32_t)(2 * g) | ((uint32_t)(2 * g + 1) << 8) | 0x0C0C0000u
+                                : (uint32_t)(2 * (g >> 1)) | ((uint32_t)(2 * (g >> 1) + 1) << 8) | 0x0C0C0000u;
+  auto lane_half = [&](const uint32_t* v, int L) -> uint16_t {
+    if constexpr (GQ == 0) return (uint16_t)__builtin_amdgcn_perm(v[2 * L + 1], v[2 * L], hsel);
+    else if constexpr (GQ == 1) return (uint16_t)__builtin_amdgcn_perm(v[L], v[L], hsel);
+    else return ms_half<GQ>(v, 4 * L);
+  };
+
+  auto compute = [&](const MsBuf<GQ, SYM>& B, int i) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t accz = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int L = 0; L < 4; ++L) {
+      uint32_t e0 = B.w[L].x, e1 = B.w[L].y, e2 = B.w[L].z, e3 = B.w[L].w;
+      transpose4(e0, e1, e2, e3);
+      const uint32_t ev[4] = {e0, e1, e2, e3};
+      f32x4_t Dq[4 / CPG];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 Bv = unpack8(ev[c], magic);
+        const int sg = c / CPG;
+        const f32x4_t Cin = (c % CPG == 0) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : Dq[sg];
+        if constexpr (XF16)
+          Dq[sg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, xa[L][c]),
+                                                          __builtin_bit_cast(f16x8_t, Bv), Cin, 0, 0, 0);
+        else
+          Dq[sg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[L][c]),
+                                                           __builtin_bit_cast(bf16x8_t, Bv), Cin, 0, 0, 0);
+      }
+      // x-sum term of the step: T of chunk g of weight row n
+      const float sg_ = f16_to_f32(lane_half(B.s, L));
+      const float zg = kOff + (SYM ? 8.f : f16_to_f32(lane_half(B.z, L)));
+      accz = __builtin_amdgcn_mfma_f32_16x16x4f32(sxa[L], -sg_ * zg, accz, 0, 0, 0);
+#pragma unroll
+      for (int sg = 0; sg < 4 / CPG; ++sg) {
+        const float sc = f16_to_f32(ms_half<GQ>(B.s, 4 * L + sg * CPG));
+        acc[0] = fmaf(sc, Dq[sg][0], acc[0]);
+        acc[1] = fmaf(sc, Dq[sg][1], acc[1]);
+        acc[2] = fmaf(sc, Dq[sg][2], acc[2]);
+        acc[3] = fmaf(sc, Dq[sg][3], acc[3]);
+      }
+    }
+    // the wave's tile of this row block waits in its slot until the group's
+    // barrier
+    const int grp = i / kXrGroup;
+    *(float4*)&red[((grp & 1) * kXrGroup + i % kXrGroup) * NW * 256 + (w * 64 + lane) * 4] =
+        make_float4(acc[0] + accz[0], acc[1] + accz[1], acc[2] + accz[2], acc[3] + accz[3]);
+    if (i % kXrGroup != kXrGroup - 1 && i != items - 1) return;
+    // a group of row blocks is done (the waves meet once per group, not per
+    // row block): add the waves' tiles of each in wave order and store y; the
+    // next group writes the other set of slots
+    __syncthreads();
+    const int i0g = grp * kXrGroup, nrb = i - i0g + 1;
+    for (int t = threadIdx.x; t < nrb * 16 * M; t += NW * 64) {
+      const int j = t / (16 * M), r = t - j * (16 * M);
+      const int m = r >> 4, nn = r & 15;
+      const float* rd = red + ((grp & 1) * kXrGroup + j) * NW * 256;
+      const int src = (nn + 16 * (m >> 2)) * 4 + (m & 3);
+      float v = 0.f;
+#pragma unroll
+      for (int u = 0; u < NW; ++u) v += rd[u * 256 + src];
+      const int row = item_rb(i0g + j) * 16 + nn;
+      if (row < N)
+        y[(size_t)m * N + row] = XF16 ? __builtin_bit_cast(uint16_t, (_Float16)v) : f32_to_bf16_rne(v);
+    }
+  };
+
+  const int rounds = items / 3, rest = items % 3;
+  int i = 0;
+  for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      if (i + 2 < items) ms_load<GQ, SYM>(buf[(j + 2) % 3], item_rb(i + 2), k0, n, g, N, K, G, rw, rs, rz);
       __builtin_amdgcn_sched_barrier(0);
       compute(buf[j], i);
       ++i;
@@ -853,6 +1022,39 @@ hipError_t launch_ms(const uint16_t* x, int M, int K, int KC, const uint8_t* qw,
   return hipGetLastError();
 }
 
+// One workgroup of K / 512 waves per row-block stream; as many workgroups per
+// compute unit as make 8 waves (two per SIMD, the launch bounds' register cap).
+template <int NW, bool SYM, bool XF16>
+hipError_t launch_xreg(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
+                       const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
+  const int nb = (N + 15) / 16;
+  const int grid = std::max(1, std::min(nb, num_cus() * (8 / NW)));
+#define GQ_XR_LAUNCH(GQ_)                                                                       \
+  hipLaunchKernelGGL((gemv_mfma_xreg_kernel<NW, GQ_, SYM, XF16>), dim3(grid), dim3(NW * 64), 0, s, \
+                     x, M, K, qw, sc, zr, N, G, y)
+  switch (G) {
+    case 32: GQ_XR_LAUNCH(0); break;
+    case 64: GQ_XR_LAUNCH(1); break;
+    case 128: GQ_XR_LAUNCH(2); break;
+    case 256: GQ_XR_LAUNCH(3); break;
+    default: GQ_XR_LAUNCH(4); break;
+  }
+#undef GQ_XR_LAUNCH
+  return hipGetLastError();
+}
+
+template <bool SYM, bool XF16>
+hipError_t xreg_nw(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
+                   const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
+  switch (K / kMSItem) {
+    case 1: return launch_xreg<1, SYM, XF16>(x, M, K, qw, sc, zr, N, G, y, s);
+    case 2: return launch_xreg<2, SYM, XF16>(x, M, K, qw, sc, zr, N, G, y, s);
+    case 4: return launch_xreg<4, SYM, XF16>(x, M, K, qw, sc, zr, N, G, y, s);
+    case 8: return launch_xreg<8, SYM, XF16>(x, M, K, qw, sc, zr, N, G, y, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int CPG, bool SYM, bool XF16>
 hipError_t launch_cpg(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
                       const uint16_t* zr, int N, int G, float* part, int splits, hipStream_t s) {
@@ -929,6 +1131,29 @@ hipError_t launch_w4a16_gemv_mfma_stream(const uint16_t* x, int M, int64_t K, co
   if (MR == 8) return GQ_MS_ROWS(8, 8);
   return GQ_MS_ROWS(16, 8);
 #undef GQ_MS_ROWS
+}
+
+// The register-resident small-batch GEMV: K of 512, 1024, 2048 or 4096 (one
+// 512-wide column range per wave), 5 <= M <= 16, group sizes as for the
+// streaming matrix-core kernel.
+bool gemv_xreg_supported(int M, int64_t K, int64_t N, int G) {
+  if (M < 5 || M > 16) return false;
+  if (K != 512 && K != 1024 && K != 2048 && K != 4096) return false;
+  if (G % 32 != 0 || (G < 512 && 512 % G != 0) || (G >= 512 && G % 512 != 0)) return false;
+  if (N * (K / 2) >= ((int64_t)1 << 31) || (int64_t)M * K * 2 >= ((int64_t)1 << 31)) return false;
+  return true;
+}
+
+hipError_t launch_w4a16_gemv_xreg(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
+                                  const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
+                                  int symmetric, uint16_t* y, hipStream_t s, bool xf16) {
+  if (!gemv_xreg_supported(M, K, N, G)) return hipErrorInvalidValue;
+  const int k = (int)K, n = (int)N;
+  if (xf16)
+    return symmetric ? xreg_nw<true, true>(x, M, k, qweight, scales, zeros, n, G, y, s)
+                     : xreg_nw<false, true>(x, M, k, qweight, scales, zeros, n, G, y, s);
+  return symmetric ? xreg_nw<true, false>(x, M, k, qweight, scales, zeros, n, G, y, s)
+                   : xreg_nw<false, false>(x, M, k, qweight, scales, zeros, n, G, y, s);
 }
 
 bool gemv_mfma_supported(int M, int64_t K, int64_t N, int G) {
