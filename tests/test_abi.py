@@ -118,18 +118,21 @@ def test_other_entry_point_validation(lib):
 
 def test_gemv_workspace_size_and_validation(lib):
     # the split-K matrix-core path (4 <= M <= 16, G in {32, 64, 128k}, K % 256
-    # == 0, where neither streaming kernel takes the call: K % 512 != 0 for M > 4)
+    # == 0, where no scratch-free kernel takes the call: M = 4 beyond the
+    # dot-product kernel's K, or K <= 4096 not a multiple of 512 for M > 4)
     # keeps ceil(K / 1024) * M * N fp32 partial sums; other calls need none
-    assert B.gq_w4a16_gemv_workspace_size(16, 14080, 4096, 32, True) == 14 * 16 * 4096 * 4
-    assert B.gq_w4a16_gemv_workspace_size(8, 6400, 203, 128) == 7 * 8 * 203 * 4
+    assert B.gq_w4a16_gemv_workspace_size(16, 2304, 4096, 32, True) == 3 * 16 * 4096 * 4
+    assert B.gq_w4a16_gemv_workspace_size(8, 3328, 203, 128) == 4 * 8 * 203 * 4
     assert B.gq_w4a16_gemv_workspace_size(4, 18176, 4096, 128) == 18 * 4 * 4096 * 4
     assert B.gq_w4a16_gemv_workspace_size(4, 16384, 4096, 128) == 0
     assert B.gq_w4a16_gemv_workspace_size(4, 4096, 4096, 128) == 0
-    assert B.gq_w4a16_gemv_workspace_size(8, 4096, 4096, 128) == 0    # streaming matrix-core path
+    assert B.gq_w4a16_gemv_workspace_size(8, 4096, 4096, 128) == 0    # x in registers
     assert B.gq_w4a16_gemv_workspace_size(16, 4096, 4096, 32, True) == 0
-    assert B.gq_w4a16_gemv_workspace_size(8, 14336, 4096, 32, True) == 0   # K in chunks
-    assert B.gq_w4a16_gemv_workspace_size(16, 14336, 4096, 32, True) == 14 * 16 * 4096 * 4
-    assert B.gq_w4a16_gemv_workspace_size(8, 4352, 4096, 128) == 5 * 8 * 4096 * 4
+    assert B.gq_w4a16_gemv_workspace_size(8, 14336, 4096, 32, True) == 0   # x streamed per item
+    assert B.gq_w4a16_gemv_workspace_size(16, 14336, 4096, 32, True) == 0
+    assert B.gq_w4a16_gemv_workspace_size(16, 14080, 4096, 32, True) == 0
+    assert B.gq_w4a16_gemv_workspace_size(8, 4352, 4096, 128) == 0
+    assert B.gq_w4a16_gemv_workspace_size(8, 3072, 4096, 128) == 0    # x staged in LDS
     assert B.gq_w4a16_gemv_workspace_size(3, 4096, 4096, 128) == 0
     assert B.gq_w4a16_gemv_workspace_size(1, 4096, 4096, 128) == 0
     assert B.gq_w4a16_gemv_workspace_size(8, 6528, 203, 128) == 0   # K % 256 != 0
@@ -140,13 +143,14 @@ def test_gemv_workspace_size_and_validation(lib):
     assert lib.gq_w4a16_gemv_workspace_size(8, 4096, 64, q(g=48), ctypes.byref(nbytes)) == B.GQ_ERR_INVALID_ARG
     assert lib.gq_w4a16_gemv_workspace_size(8, 4096, 64, q(), None) == B.GQ_ERR_INVALID_ARG
     # a needed workspace that is missing, too small or misaligned is rejected before any device call
-    need = B.gq_w4a16_gemv_workspace_size(8, 4352, 4096, 128)
-    args = (FAKE, 8, 4352, FAKE, FAKE, FAKE, 4096, q(), FAKE)
+    need = B.gq_w4a16_gemv_workspace_size(8, 3328, 4096, 128)
+    assert need > 0
+    args = (FAKE, 8, 3328, FAKE, FAKE, FAKE, 4096, q(), FAKE)
     assert lib.gq_w4a16_gemv_ws(*args, None, need, None) == B.GQ_ERR_INVALID_ARG
     assert lib.gq_w4a16_gemv_ws(*args, FAKE, need - 4, None) == B.GQ_ERR_INVALID_ARG
     assert lib.gq_w4a16_gemv_ws(*args, FAKE_MIS, need, None) == B.GQ_ERR_MISALIGNED
     # the plain GEMV checks still apply
-    assert lib.gq_w4a16_gemv_ws(FAKE, 17, 4352, FAKE, FAKE, FAKE, 4096, q(), FAKE, FAKE, need, None) == B.GQ_ERR_INVALID_ARG
+    assert lib.gq_w4a16_gemv_ws(FAKE, 17, 3328, FAKE, FAKE, FAKE, 4096, q(), FAKE, FAKE, need, None) == B.GQ_ERR_INVALID_ARG
 
 
 def test_bench_entry_point_validation(lib):
@@ -203,9 +207,9 @@ def test_f16_entry_point_validation(lib):
     assert L.gq_w4a16_gemm_f16(FAKE_MIS, 64, 4096, FAKE, FAKE, FAKE, 4096, q(), FAKE, None) == B.GQ_ERR_MISALIGNED
     assert L.gq_w4a16_gemm_f16(FAKE, 64, 4096, FAKE, FAKE, None, 4096, q(), FAKE, None) == B.GQ_ERR_INVALID_ARG
     assert L.gq_w4a16_gemm_f16(FAKE, 64, 4096, FAKE, FAKE, FAKE, 4096, q(bits=8), FAKE, None) == B.GQ_ERR_UNSUPPORTED
-    need = B.gq_w4a16_gemv_workspace_size(16, 14336, 4096, 128)
+    need = B.gq_w4a16_gemv_workspace_size(16, 2304, 4096, 128)
     assert need > 0
-    args = (FAKE, 16, 14336, FAKE, FAKE, FAKE, 4096, q(), FAKE)
+    args = (FAKE, 16, 2304, FAKE, FAKE, FAKE, 4096, q(), FAKE)
     assert L.gq_w4a16_gemv_f16_ws(*args, None, need, None) == B.GQ_ERR_INVALID_ARG
     assert L.gq_w4a16_gemv_f16_ws(*args, FAKE_MIS, need, None) == B.GQ_ERR_MISALIGNED
 

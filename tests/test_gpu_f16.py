@@ -50,7 +50,7 @@ def _check(y, x_bits, qw, s, z, G, sym, what):
     (4, 4096, 14336, 32, True),    # one 8-wave workgroup per compute unit
     (4, 16387, 4096, 128, False),  # four weight rows per item
     (5, 203, 4096, 64, False),     # matrix-core streaming kernel
-    (8, 4096, 14336, 128, False),  # x staged in chunks
+    (8, 4096, 14336, 128, False),  # x streamed per item
     (12, 3001, 4096, 256, True),
     (16, 203, 4096, 32, True),
 ])
@@ -81,11 +81,13 @@ def test_gemm_f16(M, N, K, G, sym):
 
 
 @pytest.mark.parametrize("M,K,G,ws", [
-    (16, 14336, 128, True),     # split-K matrix-core kernel (workspace), 16 rows
-    (9, 4352, 128, True),       # K not a multiple of 512
-    (16, 14336, 32, True),      # group 32 through the split kernel
-    (9, 4352, 128, False),      # no workspace: the per-row dot-product kernel
+    (16, 2304, 128, True),      # split-K matrix-core kernel (workspace), 16 rows
+    (9, 3328, 128, True),       # K at most 4096, not a multiple of 512
+    (16, 2304, 32, True),       # group 32 through the split kernel
+    (9, 3328, 128, False),      # no workspace: the per-row dot-product kernel
     (6, 4160, 64, False),
+    (12, 14336, 32, False),     # long K: x streamed per item (no workspace needed)
+    (7, 4352, 128, False),
 ])
 def test_gemv_f16_split_and_dot_product_shapes(M, K, G, ws):
     qw, s, z = _weights(203, K, G, False, seed=M + K)

@@ -125,13 +125,10 @@ def test_mfma_stream_shapes(M, N, K, sym, G):
 @pytest.mark.parametrize("M", [4, 5, 8, 13])
 @pytest.mark.parametrize("K", [1024, 2048, 6144, 8192, 14336, 16896, 18432])
 def test_mfma_stream_k_extents(M, K):
-    # (M = 4 takes the dot-product streaming kernel up to K = 16384 and the
-    # matrix-core one, in chunks, beyond)
-    # 8 staged rows: K = 2048 runs 4 waves with one 512-wide item each, 8192 8
-    # waves with two; longer K runs in chunks of x staged one after the other, a
-    # partial last chunk loading zeros (16 staged rows beyond K = 4096 take the
-    # split-K kernel)
-    assert (B.gq_w4a16_gemv_workspace_size(M, K, 333, 64, False) == 0) == (M <= 8 or K <= 4096)
+    # (M = 4 takes the dot-product streaming kernel; M > 4 the register-x
+    # kernel at K = 1024 and 2048 and the streamed-x kernel beyond 4096, none
+    # of them with scratch)
+    assert B.gq_w4a16_gemv_workspace_size(M, K, 333, 64, False) == 0
     w, x = synth.small(333, K, M, seed=M + K)
     qw, s, z = _oracle_weights(w, 64, False)
     _run(x, qw, s, z, 64, False, f"[333,{K}] M={M} asym G=64 (matrix cores, streaming)")
@@ -190,7 +187,7 @@ def test_decode_shapes_full_size(name):
                                     ("gate_up", 8), ("gate_up", 16), ("o", 12)])
 def test_small_batch_full_size_sym_g32(name, M):
     # M <= 4 take the dot-product streaming kernel, M > 4 at K = 4096 the
-    # matrix-core streaming kernel, M > 4 on down the split-K matrix-core kernel
+    # register-x matrix-core kernel, M > 4 on down the streamed-x one
     w, _ = synth.decode_case(name)
     x, _ = synth.activations(M, w.shape[1], seed=2003)
     rows = np.sort(np.random.default_rng(4).choice(w.shape[0], 256, replace=False))
@@ -234,7 +231,7 @@ def test_split_slices_and_plain_entry_point():
     workspace (the binding's default) repeated calls of falling and rising N
     and M agree bit for bit; gq_w4a16_gemv without a workspace runs the per-row
     dot-product kernel.  Both meet the oracle on sampled rows."""
-    K, G = 4352, 128  # not a multiple of 512: the split-K matrix-core path
+    K, G = 2304, 128  # at most 4096, not a multiple of 512: the split-K matrix-core path
     for M, N, seed in ((8, 3000, 90), (5, 64, 91), (16, 1000, 92), (8, 20000, 94), (8, 3000, 93)):
         announce(f"small-batch split slices M={M} N={N} K={K}")
         w, x = synth.small(N, K, M, seed=seed)
@@ -263,14 +260,14 @@ def test_workspace_entry_point_and_graph_replays():
     # from torch run the same kernels: identical bits.  Captured into a graph,
     # the call gets its scratch from the graph's pool and every replay must
     # reproduce the eager result, with other eager work on the stream between
-    # replays.  (K = 4352, not a multiple of 512, keeps the call on the split-K
-    # matrix-core path.)
-    M, K, N, G = 12, 4352, 1000, 32
+    # replays.  (K = 2304, at most 4096 and not a multiple of 512, keeps the
+    # call on the split-K matrix-core path.)
+    M, K, N, G = 12, 2304, 1000, 32
     w, x = synth.small(N, K, M, seed=77)
     qw, s, _ = _oracle_weights(w, G, True)
     xd, qd, sd = bf16_dev(x), u8_dev(qw), f16_dev(s)
     need = B.gq_w4a16_gemv_workspace_size(M, K, N, G, True)
-    assert need == 5 * M * N * 4
+    assert need == 3 * M * N * 4
     y_auto = B.gq_w4a16_gemv(xd, qd, sd, None, G, True)
     ws = torch.full((need + 64,), 0xA5, dtype=torch.uint8, device=xd.device)
     y_ws = B.gq_w4a16_gemv(xd, qd, sd, None, G, True, workspace=ws)
@@ -370,3 +367,31 @@ def test_xreg_many_row_blocks(M, N, K):
     qw, s, z = _oracle_weights(w, 128, False)
     rows = np.r_[0:64, N // 2:N // 2 + 64, N - 67:N]
     _run(x, qw, s, z, 128, False, f"[{N},{K}] M={M} asym G=128 (x in registers, many rows)", rows=rows)
+
+
+@pytest.mark.parametrize("M", [5, 8, 11, 16])
+@pytest.mark.parametrize("K,sym,G", [(4352, True, 32), (4352, False, 64), (4608, False, 128),
+                                     (5120, True, 256), (6144, False, 512), (14336, True, 1024)])
+def test_xs_k_extents(M, K, sym, G):
+    # long K with x streamed per item: items per row block not a multiple of
+    # the 8 waves (17, 18, 20 of 256 columns: the last items of some waves lie
+    # past K), every group class, a partial last row block (203 rows)
+    assert B.gq_w4a16_gemv_workspace_size(M, K, 203, G, sym) == 0
+    w, x = synth.small(203, K, M, seed=M * 7 + K + G)
+    qw, s, z = _oracle_weights(w, G, sym)
+    _run(x, qw, s, z, G, sym, f"[203,{K}] M={M} sym={sym} G={G} (x streamed)")
+
+
+@pytest.mark.parametrize("M,N,K,sym,G", [(7, 300001, 512, False, 128), (13, 40003, 4352, True, 32)])
+def test_many_row_block_groups(M, N, K, sym, G):
+    # more than eight row blocks per workgroup, so the tile slots of a second
+    # group of row blocks are used (register-resident x at K = 512, streamed x
+    # at 4352); random packed weights and fp16 scales (and zero points),
+    # checked on rows of the first and the last groups
+    rng = np.random.default_rng(N + K)
+    qw = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    s = rng.uniform(1e-3, 1e-2, size=(N, K // G)).astype(np.float16).view(np.uint16)
+    z = None if sym else rng.uniform(0, 15, size=(N, K // G)).astype(np.float16).view(np.uint16)
+    x, _ = synth.activations(M, K, seed=N)
+    rows = np.r_[0:64, 16 * 8 * 256:16 * 8 * 256 + 64, N - 67:N]
+    _run(x, qw, s, z, G, sym, f"[{N},{K}] M={M} sym={sym} G={G} (two row-block groups)", rows=rows)

@@ -577,6 +577,8 @@ hipError_t launch_w4a16_gemv(const uint16_t* x, int M, int64_t K, const uint8_t*
   }
   if (gemv_xreg_supported(M, K, N, G))
     return launch_w4a16_gemv_xreg(x, M, K, qweight, scales, zeros, N, G, symmetric, y, s, xf16);
+  if (gemv_xs_supported(M, K, N, G))
+    return launch_w4a16_gemv_xs(x, M, K, qweight, scales, zeros, N, G, symmetric, y, s, xf16);
   if (gemv_mfma_stream_supported(M, K, N, G))
     return launch_w4a16_gemv_mfma_stream(x, M, K, qweight, scales, zeros, N, G, symmetric, y, s, xf16);
   if (workspace && gemv_workspace_bytes(M, K, N, G) > 0)

@@ -746,6 +746,202 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_mfma_xreg_kernel(
   if (rest > 1) compute(buf[1], i++);
 }
 
+// Small-batch GEMV for long K (5 <= M <= 16, K a multiple of 256 beyond the
+// register-resident kernel's range): the operands, MFMAs and fp32 zero-point
+// MFMA of gemv_mfma_xreg_kernel, but x is too long to stay in registers, so
+// each 256-wide item brings its own activation operands: lane (n, g) loads
+// x[n][k0 + 128 L + 32 c + 8 g .. + 8) for its two steps L and four chunks c
+// (rows >= M read zero) together with the item's weights, two items ahead,
+// and permutes and sums them when the item is multiplied.  Every compute unit
+// reads all of x once per row block from L2 (no staging in LDS, no barrier
+// per chunk, no scratch).  Wave w takes items w, w + NW, ... of each row
+// block (items at or past K load zeros); the tiles meet in LDS once per group
+// of row blocks as in the register-resident kernel.
+template <int GQ, bool SYM>
+struct XsBuf {
+  static constexpr int kHalves = GQ >= 3 ? 1 : (8 >> GQ);  // scale halves per item and lane
+  static constexpr int kWords = (kHalves + 1) / 2;
+  uint4 w[2];  // sub-chunk g of each 128-wide step
+  uint4 x[8];  // [step][chunk]: activation operands (natural order)
+  uint32_t s[kWords], z[SYM ? 1 : kWords];
+};
+
+constexpr int kXsItem = 256;  // k per item
+
+template <int GQ, bool SYM>
+__device__ __forceinline__ void xs_load(XsBuf<GQ, SYM>& B, int rb, int k0, int n, int g, int M, int N,
+                                        int K, int G, rsrc_t rx, rsrc_t rw, rsrc_t rs, rsrc_t rz) {
+  const int row = rb * 16 + n;
+  const bool kin = k0 < K;
+  const bool rin = row < N && kin;
+  const uint32_t wo = rin ? (uint32_t)row * (uint32_t)(K / 2) + (uint32_t)(k0 + 32 * g) / 2 : kOob;
+#pragma unroll
+  for (int L = 0; L < 2; ++L) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, wo + 64u * L, 0, 2);
+    B.w[L] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+  const uint32_t xo = (n < M && kin) ? ((uint32_t)n * (uint32_t)K + (uint32_t)(k0 + 8 * g)) * 2u : kOob;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {  // step j / 4, chunk j % 4
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 64u * j, 0, 0);
+    B.x[j] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+  const uint32_t so = rin ? ((uint32_t)row * (uint32_t)(K / G) + (uint32_t)(k0 / G)) * 2u : kOob;
+  auto ld = [&](rsrc_t r, uint32_t* d) {
+    if constexpr (GQ == 0) {
+      const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, so, 0, 0);
+      d[0] = a[0]; d[1] = a[1]; d[2] = a[2]; d[3] = a[3];
+    } else if constexpr (GQ == 1) {
+      const auto a = __builtin_amdgcn_raw_buffer_load_b64(r, so, 0, 0);
+      d[0] = a[0]; d[1] = a[1];
+    } else if constexpr (GQ == 2) {
+      d[0] = __builtin_amdgcn_raw_buffer_load_b32(r, so, 0, 0);
+    } else {
+      d[0] = __builtin_amdgcn_raw_buffer_load_b16(r, so, 0, 0);
+    }
+  };
+  ld(rs, B.s);
+  if (!SYM) ld(rz, B.z);
+}
+
+template <int NW, int GQ, bool SYM, bool XF16>
+__global__ __launch_bounds__(NW * 64, 2) void gemv_mfma_xs_kernel(
+    const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
+    uint16_t* __restrict__ y) {
+  constexpr int CPG = GQ >= 2 ? 4 : (1 << GQ);  // 32-chunks per correction segment
+  __shared__ float red[2 * kXrGroup * NW * 256];  // [slot][wave][lane][4] partial tiles
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int NB = (N + 15) / 16;
+  const int NI = K / kXsItem;                 // items per row block
+  const int IPW = (NI + NW - 1) / NW;         // of them per wave (the last ones may lie past K)
+  const rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+  const rsrc_t rw = make_rsrc(qw, (uint32_t)N * (uint32_t)(K / 2));
+  const rsrc_t rs = make_rsrc(scales, (uint32_t)N * (uint32_t)(K / G) * 2);
+  const rsrc_t rz = make_rsrc(SYM ? (const void*)scales : (const void*)zeros, (uint32_t)N * (uint32_t)(K / G) * 2);
+  const int nrb = (int)blockIdx.x < NB ? (NB - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  const int items = nrb * IPW;
+  auto item_rb = [&](int i) { return (int)blockIdx.x + (i / IPW) * (int)gridDim.x; };
+  auto item_k0 = [&](int i) { return ((i % IPW) * NW + w) * kXsItem; };
+
+  XsBuf<GQ, SYM> buf[3];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    if (j < items) xs_load<GQ, SYM>(buf[j], item_rb(j), item_k0(j), n, g, M, N, K, G, rx, rw, rs, rz);
+
+  const uint32_t magic = XF16 ? 0x64006400u : 0x43004300u;  // 1024 + q or 128 + q
+  constexpr float kOff = XF16 ? 1024.f : 128.f;
+  const uint32_t hsel = GQ == 0 ? (uint32_t)(2 * g) | ((uint32_t)(2 * g + 1) << 8) | 0x0C0C0000u
+                                : (uint32_t)(2 * (g >> 1)) | ((uint32_t)(2 * (g >> 1) + 1) << 8) | 0x0C0C0000u;
+  // scale (zero) half of chunk g of step L of the item, and of the segment
+  // starting at chunk 4 L + c0
+  auto lane_half = [&](const uint32_t* v, int L) -> uint16_t {
+    if constexpr (GQ == 0) return (uint16_t)__builtin_amdgcn_perm(v[2 * L + 1], v[2 * L], hsel);
+    else if constexpr (GQ == 1) return (uint16_t)__builtin_amdgcn_perm(v[L], v[L], hsel);
+    else if constexpr (GQ == 2) return (uint16_t)(v[0] >> (16 * L));
+    else return (uint16_t)v[0];
+  };
+  auto seg_half = [&](const uint32_t* v, int L, int c0) -> uint16_t {
+    if constexpr (GQ <= 2) {
+      const int h = (4 * L + c0) >> GQ;
+      return (uint16_t)(v[h >> 1] >> (16 * (h & 1)));
+    } else {
+      return (uint16_t)v[0];
+    }
+  };
+
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t accz = {0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const XsBuf<GQ, SYM>& B, int i) {
+#pragma unroll
+    for (int L = 0; L < 2; ++L) {
+      // the step's activation operands and chunk sums (row n, chunk g)
+      uint4 A[4];
+      uint32_t p[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 v = B.x[4 * L + c];
+        float s = dot2x<XF16>(v.x, 0.f);
+        s = dot2x<XF16>(v.y, s);
+        s = dot2x<XF16>(v.z, s);
+        s = dot2x<XF16>(v.w, s);
+        p[c] = __builtin_bit_cast(uint32_t, s);
+        A[c] = perm_x(v);
+      }
+      transpose4(p[0], p[1], p[2], p[3]);
+      const float sx = (__builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1])) +
+                       (__builtin_bit_cast(float, p[2]) + __builtin_bit_cast(float, p[3]));
+      uint32_t e0 = B.w[L].x, e1 = B.w[L].y, e2 = B.w[L].z, e3 = B.w[L].w;
+      transpose4(e0, e1, e2, e3);
+      const uint32_t ev[4] = {e0, e1, e2, e3};
+      f32x4_t Dq[4 / CPG];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 Bv = unpack8(ev[c], magic);
+        const int sg = c / CPG;
+        const f32x4_t Cin = (c % CPG == 0) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : Dq[sg];
+        if constexpr (XF16)
+          Dq[sg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, A[c]),
+                                                          __builtin_bit_cast(f16x8_t, Bv), Cin, 0, 0, 0);
+        else
+          Dq[sg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A[c]),
+                                                           __builtin_bit_cast(bf16x8_t, Bv), Cin, 0, 0, 0);
+      }
+      const float sg_ = f16_to_f32(lane_half(B.s, L));
+      const float zg = kOff + (SYM ? 8.f : f16_to_f32(lane_half(B.z, L)));
+      accz = __builtin_amdgcn_mfma_f32_16x16x4f32(sx, -sg_ * zg, accz, 0, 0, 0);
+#pragma unroll
+      for (int sg = 0; sg < 4 / CPG; ++sg) {
+        const float sc = f16_to_f32(seg_half(B.s, L, sg * CPG));
+        acc[0] = fmaf(sc, Dq[sg][0], acc[0]);
+        acc[1] = fmaf(sc, Dq[sg][1], acc[1]);
+        acc[2] = fmaf(sc, Dq[sg][2], acc[2]);
+        acc[3] = fmaf(sc, Dq[sg][3], acc[3]);
+      }
+    }
+    if (i % IPW != IPW - 1) return;
+    // the wave's part of the row block is done: its tile waits in the row
+    // block's slot until the group's barrier
+    const int r = i / IPW;  // the workgroup's row block index
+    const int grp = r / kXrGroup;
+    *(float4*)&red[((grp & 1) * kXrGroup + r % kXrGroup) * NW * 256 + (w * 64 + lane) * 4] =
+        make_float4(acc[0] + accz[0], acc[1] + accz[1], acc[2] + accz[2], acc[3] + accz[3]);
+    acc[0] = acc[1] = acc[2] = acc[3] = 0.f;
+    accz = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (r % kXrGroup != kXrGroup - 1 && r != nrb - 1) return;
+    __syncthreads();
+    const int r0 = grp * kXrGroup, nr = r - r0 + 1;
+    for (int t = threadIdx.x; t < nr * 16 * M; t += NW * 64) {
+      const int j = t / (16 * M), q = t - j * (16 * M);
+      const int m = q >> 4, nn = q & 15;
+      const float* rd = red + ((grp & 1) * kXrGroup + j) * NW * 256;
+      const int src = (nn + 16 * (m >> 2)) * 4 + (m & 3);
+      float v = 0.f;
+#pragma unroll
+      for (int u = 0; u < NW; ++u) v += rd[u * 256 + src];
+      const int row = ((int)blockIdx.x + (r0 + j) * (int)gridDim.x) * 16 + nn;
+      if (row < N)
+        y[(size_t)m * N + row] = XF16 ? __builtin_bit_cast(uint16_t, (_Float16)v) : f32_to_bf16_rne(v);
+    }
+  };
+
+  const int rounds = items / 3, rest = items % 3;
+  int i = 0;
+  for (int rr = 0; rr < rounds; ++rr) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      if (i + 2 < items)
+        xs_load<GQ, SYM>(buf[(j + 2) % 3], item_rb(i + 2), item_k0(i + 2), n, g, M, N, K, G, rx, rw, rs, rz);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(buf[j], i);
+      ++i;
+    }
+  }
+  if (rest > 0) compute(buf[0], i++);
+  if (rest > 1) compute(buf[1], i++);
+}
+
 // Super-block (Q4_K-style) GEMV on the matrix cores, 5 <= M <= 16 ("量化" page,
 // "工作原理" figure, middle panel): the structure of gemv_mfma_stream_kernel
 // with the 144-byte blocks as the weight operand.  A 32-wide chunk of K is one
@@ -1055,6 +1251,26 @@ hipError_t xreg_nw(const uint16_t* x, int M, int K, const uint8_t* qw, const uin
   }
 }
 
+// One workgroup of 8 waves per compute unit (its tiles take 128 KiB of LDS).
+template <bool SYM, bool XF16>
+hipError_t launch_xs(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
+                     const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
+  const int nb = (N + 15) / 16;
+  const int grid = std::max(1, std::min(nb, num_cus()));
+#define GQ_XS_LAUNCH(GQ_)                                                                     \
+  hipLaunchKernelGGL((gemv_mfma_xs_kernel<8, GQ_, SYM, XF16>), dim3(grid), dim3(512), 0, s, x, M, \
+                     K, qw, sc, zr, N, G, y)
+  switch (G) {
+    case 32: GQ_XS_LAUNCH(0); break;
+    case 64: GQ_XS_LAUNCH(1); break;
+    case 128: GQ_XS_LAUNCH(2); break;
+    case 256: GQ_XS_LAUNCH(3); break;
+    default: GQ_XS_LAUNCH(4); break;
+  }
+#undef GQ_XS_LAUNCH
+  return hipGetLastError();
+}
+
 template <int CPG, bool SYM, bool XF16>
 hipError_t launch_cpg(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
                       const uint16_t* zr, int N, int G, float* part, int splits, hipStream_t s) {
@@ -1156,6 +1372,28 @@ hipError_t launch_w4a16_gemv_xreg(const uint16_t* x, int M, int64_t K, const uin
                    : xreg_nw<false, false>(x, M, k, qweight, scales, zeros, n, G, y, s);
 }
 
+// The long-K small-batch GEMV with x streamed from L2 (5 <= M <= 16, K a
+// multiple of 256 beyond 4096, groups that divide 256 or are multiples of it).
+bool gemv_xs_supported(int M, int64_t K, int64_t N, int G) {
+  if (M < 5 || M > 16) return false;
+  if (K <= 4096 || K % kXsItem != 0 || K > ((int64_t)1 << 24)) return false;
+  if (G % 32 != 0 || (G <= kXsItem && kXsItem % G != 0) || (G > kXsItem && G % kXsItem != 0)) return false;
+  if (N * (K / 2) >= ((int64_t)1 << 31) || (int64_t)M * K * 2 >= ((int64_t)1 << 31)) return false;
+  return true;
+}
+
+hipError_t launch_w4a16_gemv_xs(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
+                                const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
+                                int symmetric, uint16_t* y, hipStream_t s, bool xf16) {
+  if (!gemv_xs_supported(M, K, N, G)) return hipErrorInvalidValue;
+  const int k = (int)K, n = (int)N;
+  if (xf16)
+    return symmetric ? launch_xs<true, true>(x, M, k, qweight, scales, zeros, n, G, y, s)
+                     : launch_xs<false, true>(x, M, k, qweight, scales, zeros, n, G, y, s);
+  return symmetric ? launch_xs<true, false>(x, M, k, qweight, scales, zeros, n, G, y, s)
+                   : launch_xs<false, false>(x, M, k, qweight, scales, zeros, n, G, y, s);
+}
+
 bool gemv_mfma_supported(int M, int64_t K, int64_t N, int G) {
   if (M < 4 || M > 16) return false;
   if (G != 32 && G != 64 && G % 128 != 0) return false;
@@ -1166,8 +1404,8 @@ bool gemv_mfma_supported(int M, int64_t K, int64_t N, int G) {
 }
 
 size_t gemv_workspace_bytes(int M, int64_t K, int64_t N, int G) {
-  if (gemv_stream_supported(M, K) || gemv_mfma_stream_supported(M, K, N, G) ||
-      !gemv_mfma_supported(M, K, N, G))
+  if (gemv_stream_supported(M, K) || gemv_xreg_supported(M, K, N, G) || gemv_xs_supported(M, K, N, G) ||
+      gemv_mfma_stream_supported(M, K, N, G) || !gemv_mfma_supported(M, K, N, G))
     return 0;
   return (size_t)((K + kKC - 1) / kKC) * (size_t)M * (size_t)N * sizeof(float);
 }

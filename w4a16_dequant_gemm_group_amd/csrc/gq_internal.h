@@ -134,6 +134,11 @@ bool gemv_xreg_supported(int M, int64_t K, int64_t N, int G);
 hipError_t launch_w4a16_gemv_xreg(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
                                   const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
                                   int symmetric, uint16_t* y, hipStream_t s, bool xf16);
+// The same for long K with x streamed from L2 (K > 4096, a multiple of 256).
+bool gemv_xs_supported(int M, int64_t K, int64_t N, int G);
+hipError_t launch_w4a16_gemv_xs(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
+                                const uint16_t* scales, const uint16_t* zeros, int64_t N, int G,
+                                int symmetric, uint16_t* y, hipStream_t s, bool xf16);
 // Small-batch GEMV on the matrix cores split along K (4 <= M <= 16), partial
 // sums per 1024-wide slice in `workspace`, added by a second kernel.
 bool gemv_mfma_supported(int M, int64_t K, int64_t N, int G);
