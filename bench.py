@@ -61,8 +61,8 @@ SMALL_BATCH_KERNELS = {
     2: "gemv_stream_kernel (dot products, 2 activation rows in LDS)",
     3: "gemv_stream_kernel (dot products, 3 activation rows in LDS)",
     4: "gemv_stream_kernel (dot products, 4 activation rows in LDS)",
-    5: "gemv_mfma_stream_kernel (matrix cores, no scratch) on qkv/o/gate_up and on down up to "
-       "M = 8; split-K gemv_mfma_tile_kernel + finalize on down above M = 8",
+    5: "gemv_mfma_xreg_kernel (matrix cores, x in registers) on qkv/o/gate_up; "
+       "gemv_mfma_xs_kernel (matrix cores, x streamed per item) on down; no scratch",
 }
 
 
