@@ -125,9 +125,9 @@ def test_mfma_stream_shapes(M, N, K, sym, G):
 @pytest.mark.parametrize("M", [4, 5, 8, 13])
 @pytest.mark.parametrize("K", [1024, 2048, 6144, 8192, 14336, 16896, 18432])
 def test_mfma_stream_k_extents(M, K):
-    # (M = 4 takes the dot-product streaming kernel; M > 4 the register-x
-    # kernel at K = 1024 and 2048 and the streamed-x kernel beyond 4096, none
-    # of them with scratch)
+    # (M = 4 and M > 4 take the register-x kernel at K = 1024 and 2048; beyond
+    # 4096 M = 4 takes the dot-product streaming kernel and M > 4 the
+    # streamed-x kernel; none of them with scratch)
     assert B.gq_w4a16_gemv_workspace_size(M, K, 333, 64, False) == 0
     w, x = synth.small(333, K, M, seed=M + K)
     qw, s, z = _oracle_weights(w, 64, False)
@@ -186,8 +186,9 @@ def test_decode_shapes_full_size(name):
                                     ("gate_up", 2), ("gate_up", 3), ("gate_up", 4), ("qkv", 4),
                                     ("gate_up", 8), ("gate_up", 16), ("o", 12)])
 def test_small_batch_full_size_sym_g32(name, M):
-    # M <= 4 take the dot-product streaming kernel, M > 4 at K = 4096 the
-    # register-x matrix-core kernel, M > 4 on down the streamed-x one
+    # M <= 3 take the dot-product streaming kernel, M >= 4 at K = 4096 the
+    # register-x matrix-core kernel, M = 2..4 on down the dot-product kernel
+    # and M > 4 there the streamed-x one
     w, _ = synth.decode_case(name)
     x, _ = synth.activations(M, w.shape[1], seed=2003)
     rows = np.sort(np.random.default_rng(4).choice(w.shape[0], 256, replace=False))
@@ -346,7 +347,7 @@ def test_mfma_stream_tiny_row_counts(M, N):
     _run(x, qw, s, z, G, False, f"[{N},{K}] M={M} asym G={G} (matrix cores, streaming)")
 
 
-@pytest.mark.parametrize("M", [5, 7, 12, 16])
+@pytest.mark.parametrize("M", [4, 5, 7, 12, 16])
 @pytest.mark.parametrize("K", [512, 1024, 2048])
 @pytest.mark.parametrize("sym,G", [(True, 32), (False, 64), (False, 128), (True, 256), (False, 512)])
 def test_xreg_k_extents(M, K, sym, G):

@@ -104,3 +104,27 @@ def test_full_size(name, M):
         ref[:, r0:r1] = O.matmul_groupwise(O.bf16_to_f64(x), wh, O.Q4K_SUB)
     assert_parity(bits16(y), ref, O.bf16_to_f64(x), np.array([[wmax]]),
                   f"q4k {name} {w.shape} M={M} full, all rows")
+
+
+@pytest.mark.parametrize("M,N,K", [(7, 300001, 512), (13, 40003, 4352)])
+def test_gemv_many_row_block_groups(M, N, K):
+    """More than eight row blocks per workgroup on the matrix cores (x in
+    registers at K = 512, streamed per block at K = 4352), so a second group of
+    tile slots is used: blocks quantized on the GPU from seeded N(0, 0.02)
+    weights, checked bit-exact and through the GEMV on rows of the first and
+    last groups."""
+    gen = torch.Generator(device=device()).manual_seed(N + K)
+    wd = (torch.randn((N, K), generator=gen, device=device()) * 0.02).to(torch.bfloat16)
+    x, _ = synth.activations(M, K, seed=N)
+    announce(f"q4k gemv [{N},{K}] M={M}, two row-block groups")
+    blocks = B.gq_q4k_quantize(wd)
+    y = B.gq_q4k_gemv(bf16_dev(x), blocks)
+    torch.cuda.synchronize()
+    rows = np.r_[0:64, N - 67:N]
+    wr = wd[torch.from_numpy(rows).to(device())].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    del wd
+    ref_blocks = O.q4k_encode(O.q4k_quantize(O.bf16_to_f64(wr)))
+    assert np.array_equal(blocks.cpu().numpy()[rows], ref_blocks)
+    ref = O.q4k_reference(x, ref_blocks)
+    wh = O.q4k_dequantize_fields(O.q4k_decode(ref_blocks))
+    assert_parity(bits16(y)[:, rows], ref, O.bf16_to_f64(x), wh, f"q4k gemv [{N},{K}] M={M} (two groups), sampled")

@@ -1178,6 +1178,259 @@ __global__ __launch_bounds__(512, 1) void q4k_mfma_stream_kernel(
   if (rest > 1) compute(buf[1], i++);
 }
 
+// Super-block GEMV on the matrix cores with x in registers (K = 512 NW,
+// q4k_mfma_xreg_kernel) or streamed with each 256-wide item (longer K,
+// q4k_mfma_xs_kernel), 5 <= M <= 16: the structures of gemv_mfma_xreg_kernel
+// and gemv_mfma_xs_kernel with the operands and per-step scale and min terms
+// of q4k_mfma_stream_kernel (one bf16 MFMA per sub-block and 16 rows, the
+// x-sum term -(128 S + Mn) on one fp32 MFMA per step).
+
+// per-lane byte selectors and bit offset of the 6-bit scale and min of
+// sub-block 4 e + g of a block (e = 0, 1)
+struct QkSel {
+  uint32_t sc[2], mn[2], fbit[2];
+};
+__device__ __forceinline__ QkSel qk_sel(int g) {
+  QkSel q;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const uint32_t o6 = 6u * (uint32_t)(4 * e + g);
+    const uint32_t sb = o6 >> 3, mb = 2u + (o6 >> 3);
+    q.fbit[e] = o6 & 7u;
+    q.sc[e] = sb | ((sb + 1u) << 8) | 0x0C0C0000u;
+    q.mn[e] = mb | ((mb < 7u ? mb + 1u : 12u) << 8) | 0x0C0C0000u;
+  }
+  return q;
+}
+
+// One 128-wide step covering sub-blocks 4 E .. 4 E + 3 of the block with
+// header h: lane (n, g) holds sub-block g's 16 nibble bytes of row n (before
+// the transpose), A[c] the activation operands of chunk c and sx the sum of
+// row n over chunk g.
+template <int E>
+__device__ __forceinline__ void qk_step(const uint4& wv, const uint4 (&A)[4], float sx, const uint4& h,
+                                        const QkSel& q, float (&acc)[4], f32x4_t& accz) {
+  uint32_t e0 = wv.x, e1 = wv.y, e2 = wv.z, e3 = wv.w;
+  transpose4(e0, e1, e2, e3);
+  const uint32_t ev[4] = {e0, e1, e2, e3};
+  f32x4_t D[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    D[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A[c]),
+                                                   __builtin_bit_cast(bf16x8_t, unpack8(ev[c], 0x43004300u)),
+                                                   f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(h.x & 0xFFFFu));
+  const _Float16 dmin = __builtin_bit_cast(_Float16, (uint16_t)(h.x >> 16));
+  auto corr = [&](auto Cc) {
+    constexpr int c = decltype(Cc)::value;
+    const float S = __builtin_fmaf((float)d, (float)q4k_field<6 * (4 * E + c)>(h), 0.f);
+    acc[0] = fmaf(S, D[c][0], acc[0]);
+    acc[1] = fmaf(S, D[c][1], acc[1]);
+    acc[2] = fmaf(S, D[c][2], acc[2]);
+    acc[3] = fmaf(S, D[c][3], acc[3]);
+  };
+  corr(std::integral_constant<int, 0>{});
+  corr(std::integral_constant<int, 1>{});
+  corr(std::integral_constant<int, 2>{});
+  corr(std::integral_constant<int, 3>{});
+  const uint32_t sc6 = __builtin_amdgcn_ubfe(__builtin_amdgcn_perm(h.z, h.y, q.sc[E]), q.fbit[E], 6);
+  const uint32_t mn6 = __builtin_amdgcn_ubfe(__builtin_amdgcn_perm(h.w, h.z, q.mn[E]), q.fbit[E], 6);
+  const float Sg = __builtin_fmaf((float)d, (float)sc6, 0.f);
+  const float Mg = __builtin_fmaf((float)dmin, (float)mn6, 0.f);
+  accz = __builtin_amdgcn_mfma_f32_16x16x4f32(sx, -__builtin_fmaf(128.f, Sg, Mg), accz, 0, 0, 0);
+}
+
+// x operands of four chunks (natural order in v) -> permuted operands and the
+// sum of row n over chunk g (4 x 4 lane-row transpose of the partial sums)
+__device__ __forceinline__ float qk_operands(const uint4* v, uint4 (&A)[4]) {
+  uint32_t p[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float s = dot2x<false>(v[c].x, 0.f);
+    s = dot2x<false>(v[c].y, s);
+    s = dot2x<false>(v[c].z, s);
+    s = dot2x<false>(v[c].w, s);
+    p[c] = __builtin_bit_cast(uint32_t, s);
+    A[c] = perm_x(v[c]);
+  }
+  transpose4(p[0], p[1], p[2], p[3]);
+  return (__builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1])) +
+         (__builtin_bit_cast(float, p[2]) + __builtin_bit_cast(float, p[3]));
+}
+
+// the workgroup's row block r is done for this wave: its tile waits in the
+// row block's slot; at the end of a group of kXrGroup row blocks (or of the
+// workgroup's last) the waves meet and add each row block's tiles in wave
+// order
+template <int NW>
+__device__ __forceinline__ void qk_tile_done(float* red, int r, int nrb, int w, int lane, int M, int N,
+                                             float (&acc)[4], f32x4_t& accz, uint16_t* __restrict__ y) {
+  const int grp = r / kXrGroup;
+  *(float4*)&red[((grp & 1) * kXrGroup + r % kXrGroup) * NW * 256 + (w * 64 + lane) * 4] =
+      make_float4(acc[0] + accz[0], acc[1] + accz[1], acc[2] + accz[2], acc[3] + accz[3]);
+  acc[0] = acc[1] = acc[2] = acc[3] = 0.f;
+  accz = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (r % kXrGroup != kXrGroup - 1 && r != nrb - 1) return;
+  __syncthreads();
+  const int r0 = grp * kXrGroup, nr = r - r0 + 1;
+  for (int t = threadIdx.x; t < nr * 16 * M; t += NW * 64) {
+    const int j = t / (16 * M), q = t - j * (16 * M);
+    const int m = q >> 4, nn = q & 15;
+    const float* rd = red + ((grp & 1) * kXrGroup + j) * NW * 256;
+    const int src = (nn + 16 * (m >> 2)) * 4 + (m & 3);
+    float v = 0.f;
+#pragma unroll
+    for (int u = 0; u < NW; ++u) v += rd[u * 256 + src];
+    const int row = ((int)blockIdx.x + (r0 + j) * (int)gridDim.x) * 16 + nn;
+    if (row < N) y[(size_t)m * N + row] = f32_to_bf16_rne(v);
+  }
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 2) void q4k_mfma_xreg_kernel(
+    const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ blocks, int N,
+    uint16_t* __restrict__ y) {
+  __shared__ float red[2 * kXrGroup * NW * 256];
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int NB = (N + 15) / 16;
+  const int k0 = w * kMSItem;  // K == NW * 512
+  const uint32_t row_bytes = (uint32_t)(K / 256) * 144u;
+  const rsrc_t rb = make_rsrc(blocks, (uint32_t)N * row_bytes);
+  const rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+  const int items = (int)blockIdx.x < NB ? (NB - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  auto item_rb = [&](int i) { return (int)blockIdx.x + i * (int)gridDim.x; };
+  auto load = [&](QkBuf& B, int rbk) {
+    const int row = rbk * 16 + n;
+    const uint32_t base = row < N ? (uint32_t)row * row_bytes + (uint32_t)(k0 / 256) * 144u : kOob;
+#pragma unroll
+    for (int L = 0; L < 4; ++L) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+          rb, base + (uint32_t)((L >> 1) * 144 + 16 + 16 * ((L & 1) * 4 + g)), 0, 2);
+      B.w[L] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rb, base + 144u * b, 0, 0);
+      B.h[b] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  };
+  // x first (loads retire in order), then the weight prefetch
+  uint4 xa[4][4];  // [step L][chunk c]: x[n][k0 + 128 L + 32 c + 8 g .. + 8)
+#pragma unroll
+  for (int L = 0; L < 4; ++L)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t off = n < M ? ((uint32_t)n * (uint32_t)K + (uint32_t)(k0 + 128 * L + 32 * c + 8 * g)) * 2u : kOob;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+      xa[L][c] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  QkBuf buf[3];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    if (j < items) load(buf[j], item_rb(j));
+  float sxa[4];
+#pragma unroll
+  for (int L = 0; L < 4; ++L) {
+    const uint4 v[4] = {xa[L][0], xa[L][1], xa[L][2], xa[L][3]};
+    sxa[L] = qk_operands(v, xa[L]);
+  }
+  const QkSel q = qk_sel(g);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t accz = {0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const QkBuf& B, int i) {
+    qk_step<0>(B.w[0], xa[0], sxa[0], B.h[0], q, acc, accz);
+    qk_step<1>(B.w[1], xa[1], sxa[1], B.h[0], q, acc, accz);
+    qk_step<0>(B.w[2], xa[2], sxa[2], B.h[1], q, acc, accz);
+    qk_step<1>(B.w[3], xa[3], sxa[3], B.h[1], q, acc, accz);
+    qk_tile_done<NW>(red, i, items, w, lane, M, N, acc, accz, y);
+  };
+  const int rounds = items / 3, rest = items % 3;
+  int i = 0;
+  for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      if (i + 2 < items) load(buf[(j + 2) % 3], item_rb(i + 2));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(buf[j], i);
+      ++i;
+    }
+  }
+  if (rest > 0) compute(buf[0], i++);
+  if (rest > 1) compute(buf[1], i++);
+}
+
+// one 256-wide item of q4k_mfma_xs_kernel: sub-block g of both steps, the
+// block header, the activation operands of both steps
+struct QxBuf {
+  uint4 w[2], h, x[8];
+};
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 2) void q4k_mfma_xs_kernel(
+    const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ blocks, int N,
+    uint16_t* __restrict__ y) {
+  __shared__ float red[2 * kXrGroup * NW * 256];
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int NB = (N + 15) / 16;
+  const int NI = K / 256;               // blocks (items) per row
+  const int IPW = (NI + NW - 1) / NW;   // of them per wave (the last ones may lie past K)
+  const uint32_t row_bytes = (uint32_t)(K / 256) * 144u;
+  const rsrc_t rb = make_rsrc(blocks, (uint32_t)N * row_bytes);
+  const rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+  const int nrb = (int)blockIdx.x < NB ? (NB - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  const int items = nrb * IPW;
+  auto item_rb = [&](int i) { return (int)blockIdx.x + (i / IPW) * (int)gridDim.x; };
+  auto item_blk = [&](int i) { return (i % IPW) * NW + w; };
+  auto load = [&](QxBuf& B, int i) {
+    const int row = item_rb(i) * 16 + n, blk = item_blk(i);
+    const bool kin = blk < NI;
+    const uint32_t base = row < N && kin ? (uint32_t)row * row_bytes + (uint32_t)blk * 144u : kOob;
+#pragma unroll
+    for (int L = 0; L < 2; ++L) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rb, base + (uint32_t)(16 + 16 * (L * 4 + g)), 0, 2);
+      B.w[L] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+    const auto hv = __builtin_amdgcn_raw_buffer_load_b128(rb, base, 0, 0);
+    B.h = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+    const uint32_t xo = n < M && kin ? ((uint32_t)n * (uint32_t)K + (uint32_t)(blk * 256 + 8 * g)) * 2u : kOob;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {  // step j / 4, chunk j % 4
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 64u * j, 0, 0);
+      B.x[j] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  };
+  QxBuf buf[3];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    if (j < items) load(buf[j], j);
+  const QkSel q = qk_sel(g);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t accz = {0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const QxBuf& B, int i) {
+    uint4 A[4];
+    float sx = qk_operands(&B.x[0], A);
+    qk_step<0>(B.w[0], A, sx, B.h, q, acc, accz);
+    sx = qk_operands(&B.x[4], A);
+    qk_step<1>(B.w[1], A, sx, B.h, q, acc, accz);
+    if (i % IPW == IPW - 1) qk_tile_done<NW>(red, i / IPW, nrb, w, lane, M, N, acc, accz, y);
+  };
+  const int rounds = items / 3, rest = items % 3;
+  int i = 0;
+  for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      if (i + 2 < items) load(buf[(j + 2) % 3], i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(buf[j], i);
+      ++i;
+    }
+  }
+  if (rest > 0) compute(buf[0], i++);
+  if (rest > 1) compute(buf[1], i++);
+}
+
 // Two teams per workgroup with 16 staged rows when x is staged whole, both
 // teams' partial tiles fit beside it, and there are row blocks for two teams
 // on every compute unit: the 16 waves of a compute unit then share one x stage
@@ -1350,10 +1603,10 @@ hipError_t launch_w4a16_gemv_mfma_stream(const uint16_t* x, int M, int64_t K, co
 }
 
 // The register-resident small-batch GEMV: K of 512, 1024, 2048 or 4096 (one
-// 512-wide column range per wave), 5 <= M <= 16, group sizes as for the
+// 512-wide column range per wave), 4 <= M <= 16, group sizes as for the
 // streaming matrix-core kernel.
 bool gemv_xreg_supported(int M, int64_t K, int64_t N, int G) {
-  if (M < 5 || M > 16) return false;
+  if (M < 4 || M > 16) return false;
   if (K != 512 && K != 1024 && K != 2048 && K != 4096) return false;
   if (G % 32 != 0 || (G < 512 && 512 % G != 0) || (G >= 512 && G % 512 != 0)) return false;
   if (N * (K / 2) >= ((int64_t)1 << 31) || (int64_t)M * K * 2 >= ((int64_t)1 << 31)) return false;
@@ -1448,16 +1701,46 @@ static bool q4k_mfma_config(int M, int64_t K, int64_t N, int* MR, int* KC) {
   return mfma_stream_lds_bytes(*MR, 8, *KC, *KC < K) <= 156 * 1024;
 }
 
+// x in registers: K of 512 .. 4096 (one 512-wide column range per wave); x
+// streamed per block: longer K.
+static bool q4k_xreg_ok(int M, int64_t K, int64_t N) {
+  if (M < 5 || M > 16 || (K != 512 && K != 1024 && K != 2048 && K != 4096)) return false;
+  return N * (K / 256) * 144 < ((int64_t)1 << 31) && (int64_t)M * K * 2 < ((int64_t)1 << 31);
+}
+static bool q4k_xs_ok(int M, int64_t K, int64_t N) {
+  if (M < 5 || M > 16 || K <= 4096 || K % 256 != 0 || K > ((int64_t)1 << 24)) return false;
+  return N * (K / 256) * 144 < ((int64_t)1 << 31) && (int64_t)M * K * 2 < ((int64_t)1 << 31);
+}
+
 bool q4k_mfma_stream_supported(int M, int64_t K, int64_t N) {
   int MR, KC;
-  return q4k_mfma_config(M, K, N, &MR, &KC);
+  return q4k_xreg_ok(M, K, N) || q4k_xs_ok(M, K, N) || q4k_mfma_config(M, K, N, &MR, &KC);
 }
 
 hipError_t launch_q4k_gemv_mfma_stream(const uint16_t* x, int M, int64_t K, const uint8_t* blocks,
                                        int64_t N, uint16_t* y, hipStream_t s) {
+  const int k = (int)K, n = (int)N;
+  const int nb = (n + 15) / 16;
+  if (q4k_xreg_ok(M, K, N)) {  // as many workgroups per compute unit as make 8 waves
+#define GQ_QX_LAUNCH(NW_)                                                                          \
+  hipLaunchKernelGGL((q4k_mfma_xreg_kernel<NW_>), dim3(std::max(1, std::min(nb, num_cus() * (8 / NW_)))), \
+                     dim3(NW_ * 64), 0, s, x, M, k, blocks, n, y)
+    switch (k / kMSItem) {
+      case 1: GQ_QX_LAUNCH(1); break;
+      case 2: GQ_QX_LAUNCH(2); break;
+      case 4: GQ_QX_LAUNCH(4); break;
+      default: GQ_QX_LAUNCH(8); break;
+    }
+#undef GQ_QX_LAUNCH
+    return hipGetLastError();
+  }
+  if (q4k_xs_ok(M, K, N)) {  // one workgroup of 8 waves per compute unit
+    hipLaunchKernelGGL((q4k_mfma_xs_kernel<8>), dim3(std::max(1, std::min(nb, num_cus()))), dim3(512), 0, s,
+                       x, M, k, blocks, n, y);
+    return hipGetLastError();
+  }
   int MR, KC;
   if (!q4k_mfma_config(M, K, N, &MR, &KC)) return hipErrorInvalidValue;
-  const int k = (int)K, n = (int)N;
   const bool chunked = KC < k;
   const size_t lds = mfma_stream_lds_bytes(MR, 8, KC, chunked);
   const int grid = std::max(1, std::min((n + 15) / 16, num_cus()));

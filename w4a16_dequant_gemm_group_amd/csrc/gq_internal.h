@@ -128,7 +128,7 @@ hipError_t launch_w4a16_gemv_mfma_stream(const uint16_t* x, int M, int64_t K, co
                                          const uint16_t* scales, const uint16_t* zeros, int64_t N,
                                          int G, int symmetric, uint16_t* y, hipStream_t s,
                                          bool xf16 = false);
-// Small-batch GEMV on the matrix cores with x held in registers (5 <= M <=
+// Small-batch GEMV on the matrix cores with x held in registers (4 <= M <=
 // 16, K of 512 .. 4096), no scratch.
 bool gemv_xreg_supported(int M, int64_t K, int64_t N, int G);
 hipError_t launch_w4a16_gemv_xreg(const uint16_t* x, int M, int64_t K, const uint8_t* qweight,
