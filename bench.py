@@ -60,7 +60,8 @@ SMALL_BATCH_KERNELS = {
     1: "gemv_stream_kernel (dot products, one activation row)",
     2: "gemv_stream_kernel (dot products, 2 activation rows in LDS)",
     3: "gemv_stream_kernel (dot products, 3 activation rows in LDS)",
-    4: "gemv_stream_kernel (dot products, 4 activation rows in LDS)",
+    4: "gemv_mfma_xreg_kernel (matrix cores, x in registers) on qkv/o/gate_up; "
+       "gemv_stream_kernel (dot products, 4 activation rows in LDS) on down",
     5: "gemv_mfma_xreg_kernel (matrix cores, x in registers) on qkv/o/gate_up; "
        "gemv_mfma_xs_kernel (matrix cores, x streamed per item) on down; no scratch",
 }
