@@ -228,8 +228,9 @@ def main():
             _, xb = synth.prefill_case(nm)
             qw, s, z = W[nm]
             B.gq_w4a16_gemm(to_dev(xb), qw, s, z, G, False)
-        # one small-batch GEMV per projection and row count: M = 2, 3, 4 run the
-        # multi-row streaming kernel, M = 8 and 16 the matrix-core kernels
+        # one small-batch GEMV per projection and row count: M = 2, 3 (and 4 on
+        # down) run the multi-row streaming kernel, M = 4, 8 and 16 the
+        # matrix-core kernels
         for m in (2, 3, 4, 8, 16):
             for nm, n, k in shapes:
                 qw, s, z = W[nm]
