@@ -396,3 +396,17 @@ def test_many_row_block_groups(M, N, K, sym, G):
     x, _ = synth.activations(M, K, seed=N)
     rows = np.r_[0:64, 16 * 8 * 256:16 * 8 * 256 + 64, N - 67:N]
     _run(x, qw, s, z, G, sym, f"[{N},{K}] M={M} sym={sym} G={G} (two row-block groups)", rows=rows)
+
+
+@pytest.mark.parametrize("M", [5, 8, 16])
+@pytest.mark.parametrize("N,K,sym,G", [(203, 1536, True, 32), (203, 3072, False, 128),
+                                       (77, 2560, False, 512), (9001, 3072, True, 32)])
+def test_lds_staged_k_between_register_sizes(M, N, K, sym, G):
+    # K at most 4096 that is a multiple of 512 but not a power-of-two multiple:
+    # the matrix-core kernel with x staged in LDS per workgroup (at M = 16 and
+    # 9001 rows, two teams of 8 waves share one stage)
+    assert B.gq_w4a16_gemv_workspace_size(M, K, N, G, sym) == 0
+    w, x = synth.small(N, K, M, seed=N + K + M + G)
+    qw, s, z = _oracle_weights(w, G, sym)
+    rows = None if N < 1000 else np.r_[0:64, N // 2:N // 2 + 64, N - 67:N]
+    _run(x, qw, s, z, G, sym, f"[{N},{K}] M={M} sym={sym} G={G} (x staged in LDS)", rows=rows)

@@ -1688,17 +1688,17 @@ hipError_t launch_w4a16_gemv_mfma(const uint16_t* x, int M, int64_t K, const uin
   return hipGetLastError();
 }
 
-// The super-block matrix-core GEMV: 8 staged rows (M <= 8) or 16, one
-// workgroup of 8 waves per compute unit, K in 512-wide items; x staged whole
-// while it fits, else in chunks of 8192 (8 rows) or 4096 (16 rows) columns.  False if K is not a multiple of
-// 512 or a byte offset would not fit 32 bits.
+// The super-block matrix-core GEMV with x staged in LDS: 8 staged rows (M <=
+// 8) or 16, one workgroup of 8 waves per compute unit, K in 512-wide items, x
+// staged whole (K up to 4096; longer K streams x per block instead, see
+// q4k_xs_ok).  False if K is not a multiple of 512 or a byte offset would not
+// fit 32 bits.
 static bool q4k_mfma_config(int M, int64_t K, int64_t N, int* MR, int* KC) {
-  if (M < 5 || M > 16 || K % kMSItem != 0 || K > ((int64_t)1 << 24)) return false;
+  if (M < 5 || M > 16 || K % kMSItem != 0 || K > 4096) return false;
   if (N * (K / 256) * 144 >= ((int64_t)1 << 31) || (int64_t)M * K * 2 >= ((int64_t)1 << 31)) return false;
   *MR = M <= 8 ? 8 : 16;
-  const int kcmax = *MR == 8 ? 8192 : 4096;
-  *KC = (int)std::min<int64_t>(kcmax, (K + 4095) / 4096 * 4096);
-  return mfma_stream_lds_bytes(*MR, 8, *KC, *KC < K) <= 156 * 1024;
+  *KC = 4096;  // a multiple of 8 waves x 512 columns; items at or past K load zeros
+  return mfma_stream_lds_bytes(*MR, 8, *KC, false) <= 156 * 1024;
 }
 
 // x in registers: K of 512 .. 4096 (one 512-wide column range per wave); x
@@ -1741,24 +1741,14 @@ hipError_t launch_q4k_gemv_mfma_stream(const uint16_t* x, int M, int64_t K, cons
   }
   int MR, KC;
   if (!q4k_mfma_config(M, K, N, &MR, &KC)) return hipErrorInvalidValue;
-  const bool chunked = KC < k;
-  const size_t lds = mfma_stream_lds_bytes(MR, 8, KC, chunked);
+  const size_t lds = mfma_stream_lds_bytes(MR, 8, KC, false);
   const int grid = std::max(1, std::min((n + 15) / 16, num_cus()));
-  if (MR == 8) {
-    if (chunked)
-      hipLaunchKernelGGL((q4k_mfma_stream_kernel<8, true>), dim3(grid), dim3(512), lds, s, x, M, k, blocks,
-                         n, y, KC);
-    else
-      hipLaunchKernelGGL((q4k_mfma_stream_kernel<8, false>), dim3(grid), dim3(512), lds, s, x, M, k,
-                         blocks, n, y, KC);
-  } else {
-    if (chunked)
-      hipLaunchKernelGGL((q4k_mfma_stream_kernel<16, true>), dim3(grid), dim3(512), lds, s, x, M, k,
-                         blocks, n, y, KC);
-    else
-      hipLaunchKernelGGL((q4k_mfma_stream_kernel<16, false>), dim3(grid), dim3(512), lds, s, x, M, k,
-                         blocks, n, y, KC);
-  }
+  if (MR == 8)
+    hipLaunchKernelGGL((q4k_mfma_stream_kernel<8, false>), dim3(grid), dim3(512), lds, s, x, M, k, blocks,
+                       n, y, KC);
+  else
+    hipLaunchKernelGGL((q4k_mfma_stream_kernel<16, false>), dim3(grid), dim3(512), lds, s, x, M, k, blocks,
+                       n, y, KC);
   return hipGetLastError();
 }
 
