@@ -581,6 +581,48 @@ gemv_mfma_stream_kernel(
 
 constexpr int kXrGroup = 8;  // row blocks per group (the waves meet once per group)
 
+// The activation operands of a register-x wave, xa[L][c] = x[n][k0 + 128 L +
+// 32 c + 8 g .. + 8) for lane (n, g) (rows >= M zero), loaded with whole-wave
+// contiguous 16-byte loads (lane l takes x[r][k0 + 8 l .. + 8) of row r: 1 KiB
+// per instruction, M instructions) and moved into operand order through the
+// wave's own 8 KiB of LDS, eight rows at a time (16-byte units XOR-swizzled by
+// row, so the writes and the operand reads are free of bank conflicts).  The
+// region is private to the wave: no barrier.  Loading the operands directly
+// took 16 instructions per wave of sixteen 64-byte pieces each.
+__device__ __forceinline__ void xreg_load_x(rsrc_t rx, int M, int K, int k0, int lane, uint4* region,
+                                            uint4 (&xa)[4][4]) {
+  const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int L = 0; L < 4; ++L)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) xa[L][c] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (8 * h >= M) break;
+    uint4 v[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int row = 8 * h + r;
+      const uint32_t off = row < M ? ((uint32_t)row * (uint32_t)K + (uint32_t)(k0 + 8 * lane)) * 2u : kOob;
+      const auto t = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+      v[r] = make_uint4(t[0], t[1], t[2], t[3]);
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) region[r * 64 + (lane ^ r)] = v[r];
+    // other lanes' writes: ordered within the wavefront
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if ((n >> 3) == h) {
+      const int rr = n & 7;
+#pragma unroll
+      for (int L = 0; L < 4; ++L)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) xa[L][c] = region[rr * 64 + ((16 * L + 4 * c + g) ^ rr)];
+    }
+  }
+}
+
 // Small-batch GEMV with the activations in registers (5 <= M <= 16, K = 512 NW
 // for NW = 1..8 waves): the product, operands and MFMAs of
 // gemv_mfma_stream_kernel, but wave w always covers the same 512 columns
@@ -626,14 +668,9 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_mfma_xreg_kernel(
   // for the slowest one's loads.)
   const rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
   uint4 xa[4][4];  // [step L][chunk c]: x[n][k0 + 128 L + 32 c + 8 g .. + 8), permuted
-#pragma unroll
-  for (int L = 0; L < 4; ++L)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t off = n < M ? ((uint32_t)n * (uint32_t)K + (uint32_t)(k0 + 128 * L + 32 * c + 8 * g)) * 2u : kOob;
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
-      xa[L][c] = make_uint4(v[0], v[1], v[2], v[3]);
-    }
+  // the second set of tile slots is first written after the first group's
+  // barrier, when every wave holds its operands
+  xreg_load_x(rx, M, K, k0, lane, (uint4*)(red + kXrGroup * NW * 256) + w * 512, xa);
   MsBuf<GQ, SYM> buf[3];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
@@ -1315,16 +1352,10 @@ __global__ __launch_bounds__(NW * 64, 2) void q4k_mfma_xreg_kernel(
       B.h[b] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   };
-  // x first (loads retire in order), then the weight prefetch
+  // x first (loads retire in order), then the weight prefetch; the second
+  // set of tile slots holds no tile before the first group's barrier
   uint4 xa[4][4];  // [step L][chunk c]: x[n][k0 + 128 L + 32 c + 8 g .. + 8)
-#pragma unroll
-  for (int L = 0; L < 4; ++L)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t off = n < M ? ((uint32_t)n * (uint32_t)K + (uint32_t)(k0 + 128 * L + 32 * c + 8 * g)) * 2u : kOob;
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
-      xa[L][c] = make_uint4(v[0], v[1], v[2], v[3]);
-    }
+  xreg_load_x(rx, M, K, k0, lane, (uint4*)(red + kXrGroup * NW * 256) + w * 512, xa);
   QkBuf buf[3];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
