@@ -786,27 +786,70 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_mfma_xreg_kernel(
 // Small-batch GEMV for long K (5 <= M <= 16, K a multiple of 256 beyond the
 // register-resident kernel's range): the operands, MFMAs and fp32 zero-point
 // MFMA of gemv_mfma_xreg_kernel, but x is too long to stay in registers, so
-// each 256-wide item brings its own activation operands: lane (n, g) loads
-// x[n][k0 + 128 L + 32 c + 8 g .. + 8) for its two steps L and four chunks c
-// (rows >= M read zero) together with the item's weights, two items ahead,
-// and permutes and sums them when the item is multiplied.  Every compute unit
-// reads all of x once per row block from L2 (no staging in LDS, no barrier
-// per chunk, no scratch).  Wave w takes items w, w + NW, ... of each row
-// block (items at or past K load zeros); the tiles meet in LDS once per group
-// of row blocks as in the register-resident kernel.
-template <int GQ, bool SYM>
+// each 256-wide item brings its own activation rows, loaded with the item's
+// weights two items ahead as whole-wave contiguous pieces (two rows of 512
+// bytes per load; 8 or 16 rows, MR, a compile-time count) and moved into
+// operand order through the wave's own LDS region when the item is
+// multiplied (rows >= M read zero).  Every compute unit reads all of x once per
+// row block from L2 (no staging shared by the waves, no scratch).  Wave w
+// takes items w, w + NW, ... of each row block (items at or past K load
+// zeros); the tiles meet in LDS once per group of four row blocks (the LDS
+// also holds the waves' x regions).
+template <int GQ, bool SYM, int MR>
 struct XsBuf {
   static constexpr int kHalves = GQ >= 3 ? 1 : (8 >> GQ);  // scale halves per item and lane
   static constexpr int kWords = (kHalves + 1) / 2;
-  uint4 w[2];  // sub-chunk g of each 128-wide step
-  uint4 x[8];  // [step][chunk]: activation operands (natural order)
+  uint4 w[2];       // sub-chunk g of each 128-wide step
+  uint4 x[MR / 2];  // the item's activation rows, two per load (xs_load_x)
   uint32_t s[kWords], z[SYM ? 1 : kWords];
 };
 
 constexpr int kXsItem = 256;  // k per item
+constexpr int kXsGroup = 4;   // row blocks per group of the streamed-x kernels (LDS: tiles + x)
 
-template <int GQ, bool SYM>
-__device__ __forceinline__ void xs_load(XsBuf<GQ, SYM>& B, int rb, int k0, int n, int g, int M, int N,
+// The activation rows of a 256-wide item, loaded whole-wave contiguous: v[j]
+// of lane l is x[2 j + l / 32][k0 + 8 (l % 32) .. + 8) (rows >= M and items at
+// or past K read zero): MR / 2 loads of two 512-byte row pieces each.
+template <int MR>
+__device__ __forceinline__ void xs_load_x(rsrc_t rx, int M, int K, int k0, bool kin, int lane,
+                                          uint4 (&v)[MR / 2]) {
+#pragma unroll
+  for (int j = 0; j < MR / 2; ++j) {
+    const int row = 2 * j + (lane >> 5);
+    const uint32_t off = row < M && kin ? ((uint32_t)row * (uint32_t)K + (uint32_t)(k0 + 8 * (lane & 31))) * 2u : kOob;
+    const auto t = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+    v[j] = make_uint4(t[0], t[1], t[2], t[3]);
+  }
+}
+
+// Those rows in operand order through the wave's own LDS region (16-byte
+// units XOR-swizzled by row: no bank conflicts): A[4 L + c] of lane (n, g) is
+// x[n][k0 + 128 L + 32 c + 8 g .. + 8) in natural order, zero for n >= MR.
+template <int MR>
+__device__ __forceinline__ void xs_operands(const uint4 (&v)[MR / 2], int lane, uint4* region,
+                                            uint4 (&A)[8]) {
+#pragma unroll
+  for (int j = 0; j < MR / 2; ++j) {
+    const int row = 2 * j + (lane >> 5), u = lane & 31;
+    region[row * 32 + (u ^ (row & 7))] = v[j];
+  }
+  // other lanes' writes: ordered within the wavefront
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) A[q] = make_uint4(0, 0, 0, 0);
+  if (MR == 16 || n < MR) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) A[q] = region[n * 32 + ((4 * q + g) ^ (n & 7))];
+  }
+  // the next item's writes to the region must follow these reads (same wave)
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int GQ, bool SYM, int MR>
+__device__ __forceinline__ void xs_load(XsBuf<GQ, SYM, MR>& B, int rb, int k0, int n, int g, int M, int N,
                                         int K, int G, rsrc_t rx, rsrc_t rw, rsrc_t rs, rsrc_t rz) {
   const int row = rb * 16 + n;
   const bool kin = k0 < K;
@@ -817,12 +860,7 @@ __device__ __forceinline__ void xs_load(XsBuf<GQ, SYM>& B, int rb, int k0, int n
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, wo + 64u * L, 0, 2);
     B.w[L] = make_uint4(v[0], v[1], v[2], v[3]);
   }
-  const uint32_t xo = (n < M && kin) ? ((uint32_t)n * (uint32_t)K + (uint32_t)(k0 + 8 * g)) * 2u : kOob;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {  // step j / 4, chunk j % 4
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 64u * j, 0, 0);
-    B.x[j] = make_uint4(v[0], v[1], v[2], v[3]);
-  }
+  xs_load_x<MR>(rx, M, K, k0, kin, (int)(threadIdx.x & 63), B.x);
   const uint32_t so = rin ? ((uint32_t)row * (uint32_t)(K / G) + (uint32_t)(k0 / G)) * 2u : kOob;
   auto ld = [&](rsrc_t r, uint32_t* d) {
     if constexpr (GQ == 0) {
@@ -841,13 +879,14 @@ __device__ __forceinline__ void xs_load(XsBuf<GQ, SYM>& B, int rb, int k0, int n
   if (!SYM) ld(rz, B.z);
 }
 
-template <int NW, int GQ, bool SYM, bool XF16>
+template <int NW, int GQ, bool SYM, bool XF16, int MR>
 __global__ __launch_bounds__(NW * 64, 2) void gemv_mfma_xs_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int N, int G,
     uint16_t* __restrict__ y) {
   constexpr int CPG = GQ >= 2 ? 4 : (1 << GQ);  // 32-chunks per correction segment
-  __shared__ float red[2 * kXrGroup * NW * 256];  // [slot][wave][lane][4] partial tiles
+  __shared__ float red[2 * kXsGroup * NW * 256];  // [slot][wave][lane][4] partial tiles
+  __shared__ uint4 xlds[NW][MR * 32];            // each wave's item rows in operand order
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int NB = (N + 15) / 16;
@@ -862,10 +901,10 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_mfma_xs_kernel(
   auto item_rb = [&](int i) { return (int)blockIdx.x + (i / IPW) * (int)gridDim.x; };
   auto item_k0 = [&](int i) { return ((i % IPW) * NW + w) * kXsItem; };
 
-  XsBuf<GQ, SYM> buf[3];
+  XsBuf<GQ, SYM, MR> buf[3];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    if (j < items) xs_load<GQ, SYM>(buf[j], item_rb(j), item_k0(j), n, g, M, N, K, G, rx, rw, rs, rz);
+    if (j < items) xs_load<GQ, SYM, MR>(buf[j], item_rb(j), item_k0(j), n, g, M, N, K, G, rx, rw, rs, rz);
 
   const uint32_t magic = XF16 ? 0x64006400u : 0x43004300u;  // 1024 + q or 128 + q
   constexpr float kOff = XF16 ? 1024.f : 128.f;
@@ -890,7 +929,9 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_mfma_xs_kernel(
 
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   f32x4_t accz = {0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const XsBuf<GQ, SYM>& B, int i) {
+  auto compute = [&](const XsBuf<GQ, SYM, MR>& B, int i) {
+    uint4 X[8];
+    xs_operands<MR>(B.x, lane, xlds[w], X);
 #pragma unroll
     for (int L = 0; L < 2; ++L) {
       // the step's activation operands and chunk sums (row n, chunk g)
@@ -898,7 +939,7 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_mfma_xs_kernel(
       uint32_t p[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint4 v = B.x[4 * L + c];
+        const uint4 v = X[4 * L + c];
         float s = dot2x<XF16>(v.x, 0.f);
         s = dot2x<XF16>(v.y, s);
         s = dot2x<XF16>(v.z, s);
@@ -941,18 +982,18 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_mfma_xs_kernel(
     // the wave's part of the row block is done: its tile waits in the row
     // block's slot until the group's barrier
     const int r = i / IPW;  // the workgroup's row block index
-    const int grp = r / kXrGroup;
-    *(float4*)&red[((grp & 1) * kXrGroup + r % kXrGroup) * NW * 256 + (w * 64 + lane) * 4] =
+    const int grp = r / kXsGroup;
+    *(float4*)&red[((grp & 1) * kXsGroup + r % kXsGroup) * NW * 256 + (w * 64 + lane) * 4] =
         make_float4(acc[0] + accz[0], acc[1] + accz[1], acc[2] + accz[2], acc[3] + accz[3]);
     acc[0] = acc[1] = acc[2] = acc[3] = 0.f;
     accz = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (r % kXrGroup != kXrGroup - 1 && r != nrb - 1) return;
+    if (r % kXsGroup != kXsGroup - 1 && r != nrb - 1) return;
     __syncthreads();
-    const int r0 = grp * kXrGroup, nr = r - r0 + 1;
+    const int r0 = grp * kXsGroup, nr = r - r0 + 1;
     for (int t = threadIdx.x; t < nr * 16 * M; t += NW * 64) {
       const int j = t / (16 * M), q = t - j * (16 * M);
       const int m = q >> 4, nn = q & 15;
-      const float* rd = red + ((grp & 1) * kXrGroup + j) * NW * 256;
+      const float* rd = red + ((grp & 1) * kXsGroup + j) * NW * 256;
       const int src = (nn + 16 * (m >> 2)) * 4 + (m & 3);
       float v = 0.f;
 #pragma unroll
@@ -969,7 +1010,7 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_mfma_xs_kernel(
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
       if (i + 2 < items)
-        xs_load<GQ, SYM>(buf[(j + 2) % 3], item_rb(i + 2), item_k0(i + 2), n, g, M, N, K, G, rx, rw, rs, rz);
+        xs_load<GQ, SYM, MR>(buf[(j + 2) % 3], item_rb(i + 2), item_k0(i + 2), n, g, M, N, K, G, rx, rw, rs, rz);
       __builtin_amdgcn_sched_barrier(0);
       compute(buf[j], i);
       ++i;
@@ -1299,21 +1340,21 @@ __device__ __forceinline__ float qk_operands(const uint4* v, uint4 (&A)[4]) {
 // row block's slot; at the end of a group of kXrGroup row blocks (or of the
 // workgroup's last) the waves meet and add each row block's tiles in wave
 // order
-template <int NW>
+template <int NW, int GRP>
 __device__ __forceinline__ void qk_tile_done(float* red, int r, int nrb, int w, int lane, int M, int N,
                                              float (&acc)[4], f32x4_t& accz, uint16_t* __restrict__ y) {
-  const int grp = r / kXrGroup;
-  *(float4*)&red[((grp & 1) * kXrGroup + r % kXrGroup) * NW * 256 + (w * 64 + lane) * 4] =
+  const int grp = r / GRP;
+  *(float4*)&red[((grp & 1) * GRP + r % GRP) * NW * 256 + (w * 64 + lane) * 4] =
       make_float4(acc[0] + accz[0], acc[1] + accz[1], acc[2] + accz[2], acc[3] + accz[3]);
   acc[0] = acc[1] = acc[2] = acc[3] = 0.f;
   accz = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (r % kXrGroup != kXrGroup - 1 && r != nrb - 1) return;
+  if (r % GRP != GRP - 1 && r != nrb - 1) return;
   __syncthreads();
-  const int r0 = grp * kXrGroup, nr = r - r0 + 1;
+  const int r0 = grp * GRP, nr = r - r0 + 1;
   for (int t = threadIdx.x; t < nr * 16 * M; t += NW * 64) {
     const int j = t / (16 * M), q = t - j * (16 * M);
     const int m = q >> 4, nn = q & 15;
-    const float* rd = red + ((grp & 1) * kXrGroup + j) * NW * 256;
+    const float* rd = red + ((grp & 1) * GRP + j) * NW * 256;
     const int src = (nn + 16 * (m >> 2)) * 4 + (m & 3);
     float v = 0.f;
 #pragma unroll
@@ -1374,7 +1415,7 @@ __global__ __launch_bounds__(NW * 64, 2) void q4k_mfma_xreg_kernel(
     qk_step<1>(B.w[1], xa[1], sxa[1], B.h[0], q, acc, accz);
     qk_step<0>(B.w[2], xa[2], sxa[2], B.h[1], q, acc, accz);
     qk_step<1>(B.w[3], xa[3], sxa[3], B.h[1], q, acc, accz);
-    qk_tile_done<NW>(red, i, items, w, lane, M, N, acc, accz, y);
+    qk_tile_done<NW, kXrGroup>(red, i, items, w, lane, M, N, acc, accz, y);
   };
   const int rounds = items / 3, rest = items % 3;
   int i = 0;
@@ -1393,15 +1434,17 @@ __global__ __launch_bounds__(NW * 64, 2) void q4k_mfma_xreg_kernel(
 
 // one 256-wide item of q4k_mfma_xs_kernel: sub-block g of both steps, the
 // block header, the activation operands of both steps
+template <int MR>
 struct QxBuf {
-  uint4 w[2], h, x[8];
+  uint4 w[2], h, x[MR / 2];
 };
 
-template <int NW>
+template <int NW, int MR>
 __global__ __launch_bounds__(NW * 64, 2) void q4k_mfma_xs_kernel(
     const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ blocks, int N,
     uint16_t* __restrict__ y) {
-  __shared__ float red[2 * kXrGroup * NW * 256];
+  __shared__ float red[2 * kXsGroup * NW * 256];
+  __shared__ uint4 xlds[NW][MR * 32];  // each wave's item rows in operand order
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int NB = (N + 15) / 16;
@@ -1414,7 +1457,7 @@ __global__ __launch_bounds__(NW * 64, 2) void q4k_mfma_xs_kernel(
   const int items = nrb * IPW;
   auto item_rb = [&](int i) { return (int)blockIdx.x + (i / IPW) * (int)gridDim.x; };
   auto item_blk = [&](int i) { return (i % IPW) * NW + w; };
-  auto load = [&](QxBuf& B, int i) {
+  auto load = [&](QxBuf<MR>& B, int i) {
     const int row = item_rb(i) * 16 + n, blk = item_blk(i);
     const bool kin = blk < NI;
     const uint32_t base = row < N && kin ? (uint32_t)row * row_bytes + (uint32_t)blk * 144u : kOob;
@@ -1425,27 +1468,23 @@ __global__ __launch_bounds__(NW * 64, 2) void q4k_mfma_xs_kernel(
     }
     const auto hv = __builtin_amdgcn_raw_buffer_load_b128(rb, base, 0, 0);
     B.h = make_uint4(hv[0], hv[1], hv[2], hv[3]);
-    const uint32_t xo = n < M && kin ? ((uint32_t)n * (uint32_t)K + (uint32_t)(blk * 256 + 8 * g)) * 2u : kOob;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {  // step j / 4, chunk j % 4
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 64u * j, 0, 0);
-      B.x[j] = make_uint4(v[0], v[1], v[2], v[3]);
-    }
+    xs_load_x<MR>(rx, M, K, blk * 256, kin, lane, B.x);
   };
-  QxBuf buf[3];
+  QxBuf<MR> buf[3];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
     if (j < items) load(buf[j], j);
   const QkSel q = qk_sel(g);
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   f32x4_t accz = {0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const QxBuf& B, int i) {
-    uint4 A[4];
-    float sx = qk_operands(&B.x[0], A);
+  auto compute = [&](const QxBuf<MR>& B, int i) {
+    uint4 X[8], A[4];
+    xs_operands<MR>(B.x, lane, xlds[w], X);
+    float sx = qk_operands(&X[0], A);
     qk_step<0>(B.w[0], A, sx, B.h, q, acc, accz);
-    sx = qk_operands(&B.x[4], A);
+    sx = qk_operands(&X[4], A);
     qk_step<1>(B.w[1], A, sx, B.h, q, acc, accz);
-    if (i % IPW == IPW - 1) qk_tile_done<NW>(red, i / IPW, nrb, w, lane, M, N, acc, accz, y);
+    if (i % IPW == IPW - 1) qk_tile_done<NW, kXsGroup>(red, i / IPW, nrb, w, lane, M, N, acc, accz, y);
   };
   const int rounds = items / 3, rest = items % 3;
   int i = 0;
@@ -1535,15 +1574,20 @@ hipError_t xreg_nw(const uint16_t* x, int M, int K, const uint8_t* qw, const uin
   }
 }
 
-// One workgroup of 8 waves per compute unit (its tiles take 128 KiB of LDS).
+// One workgroup of 8 waves per compute unit (its tile slots and x rows take
+// 64 + 32 or 64 KiB of LDS); 8 activation rows per item when M <= 8.
 template <bool SYM, bool XF16>
 hipError_t launch_xs(const uint16_t* x, int M, int K, const uint8_t* qw, const uint16_t* sc,
                      const uint16_t* zr, int N, int G, uint16_t* y, hipStream_t s) {
   const int nb = (N + 15) / 16;
   const int grid = std::max(1, std::min(nb, num_cus()));
-#define GQ_XS_LAUNCH(GQ_)                                                                     \
-  hipLaunchKernelGGL((gemv_mfma_xs_kernel<8, GQ_, SYM, XF16>), dim3(grid), dim3(512), 0, s, x, M, \
-                     K, qw, sc, zr, N, G, y)
+#define GQ_XS_LAUNCH(GQ_)                                                                            \
+  if (M <= 8)                                                                                          \
+    hipLaunchKernelGGL((gemv_mfma_xs_kernel<8, GQ_, SYM, XF16, 8>), dim3(grid), dim3(512), 0, s, x, M, K, \
+                       qw, sc, zr, N, G, y);                                                           \
+  else                                                                                                 \
+    hipLaunchKernelGGL((gemv_mfma_xs_kernel<8, GQ_, SYM, XF16, 16>), dim3(grid), dim3(512), 0, s, x, M, K, \
+                       qw, sc, zr, N, G, y)
   switch (G) {
     case 32: GQ_XS_LAUNCH(0); break;
     case 64: GQ_XS_LAUNCH(1); break;
@@ -1766,8 +1810,11 @@ hipError_t launch_q4k_gemv_mfma_stream(const uint16_t* x, int M, int64_t K, cons
     return hipGetLastError();
   }
   if (q4k_xs_ok(M, K, N)) {  // one workgroup of 8 waves per compute unit
-    hipLaunchKernelGGL((q4k_mfma_xs_kernel<8>), dim3(std::max(1, std::min(nb, num_cus()))), dim3(512), 0, s,
-                       x, M, k, blocks, n, y);
+    const dim3 grid(std::max(1, std::min(nb, num_cus())));
+    if (M <= 8)
+      hipLaunchKernelGGL((q4k_mfma_xs_kernel<8, 8>), grid, dim3(512), 0, s, x, M, k, blocks, n, y);
+    else
+      hipLaunchKernelGGL((q4k_mfma_xs_kernel<8, 16>), grid, dim3(512), 0, s, x, M, k, blocks, n, y);
     return hipGetLastError();
   }
   int MR, KC;
