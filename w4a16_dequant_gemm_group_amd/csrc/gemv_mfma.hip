@@ -584,11 +584,13 @@ constexpr int kXrGroup = 8;  // row blocks per group (the waves meet once per gr
 // The activation operands of a register-x wave, xa[L][c] = x[n][k0 + 128 L +
 // 32 c + 8 g .. + 8) for lane (n, g) (rows >= M zero), loaded with whole-wave
 // contiguous 16-byte loads (lane l takes x[r][k0 + 8 l .. + 8) of row r: 1 KiB
-// per instruction, M instructions) and moved into operand order through the
-// wave's own 8 KiB of LDS, eight rows at a time (16-byte units XOR-swizzled by
-// row, so the writes and the operand reads are free of bank conflicts).  The
-// region is private to the wave: no barrier.  Loading the operands directly
-// took 16 instructions per wave of sixteen 64-byte pieces each.
+// per instruction, all rows issued at once) and moved into operand order
+// through the wave's own 8 KiB of LDS, eight rows at a time (16-byte units
+// XOR-swizzled by row, so the writes and the operand reads are free of bank
+// conflicts).  The region is private to the wave: no barrier.  Loading the
+// operands directly took 16 instructions per wave of sixteen 64-byte pieces
+// each; loading the second eight rows only after the first eight had passed
+// through the region cost a second memory round trip at M > 8.
 __device__ __forceinline__ void xreg_load_x(rsrc_t rx, int M, int K, int k0, int lane, uint4* region,
                                             uint4 (&xa)[4][4]) {
   const int n = lane & 15, g = lane >> 4;
@@ -596,19 +598,25 @@ __device__ __forceinline__ void xreg_load_x(rsrc_t rx, int M, int K, int k0, int
   for (int L = 0; L < 4; ++L)
 #pragma unroll
     for (int c = 0; c < 4; ++c) xa[L][c] = make_uint4(0, 0, 0, 0);
+  uint4 v[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    if (r == 8 && M <= 8) break;
+    const uint32_t off = r < M ? ((uint32_t)r * (uint32_t)K + (uint32_t)(k0 + 8 * lane)) * 2u : kOob;
+    const auto t = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+    v[r] = make_uint4(t[0], t[1], t[2], t[3]);
+  }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     if (8 * h >= M) break;
-    uint4 v[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int row = 8 * h + r;
-      const uint32_t off = row < M ? ((uint32_t)row * (uint32_t)K + (uint32_t)(k0 + 8 * lane)) * 2u : kOob;
-      const auto t = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
-      v[r] = make_uint4(t[0], t[1], t[2], t[3]);
+    if (h == 1) {
+      // every lane's reads of the first half are done before it is overwritten
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 #pragma unroll
-    for (int r = 0; r < 8; ++r) region[r * 64 + (lane ^ r)] = v[r];
+    for (int r = 0; r < 8; ++r) region[r * 64 + (lane ^ r)] = v[8 * h + r];
     // other lanes' writes: ordered within the wavefront
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
