@@ -29,6 +29,7 @@
 // the slices in slice order (so the result does not depend on scheduling) and
 // rounds once to bf16 (fp16 for fp16 activations), nearest-even.
 #include <algorithm>
+#include <type_traits>
 #include <utility>
 
 #include "gq_internal.h"
@@ -680,13 +681,11 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_mfma_xreg_kernel(
   // barrier, when every wave holds its operands
   xreg_load_x(rx, M, K, k0, lane, (uint4*)(red + kXrGroup * NW * 256) + w * 512, xa);
   MsBuf<GQ, SYM> buf[3];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    if (j < items) ms_load<GQ, SYM>(buf[j], item_rb(j), k0, n, g, N, K, G, rw, rs, rz);
   // chunk sums of row n: lane (n, g) holds 8 of each chunk's 32 values (a
   // partial sum p_c per chunk c); the 4 x 4 transpose across the lane rows
   // gives lane (n, g) the four partials of chunk g, whose sum it keeps
   float sxa[4];
+  auto x_sums = [&]() {
 #pragma unroll
   for (int L = 0; L < 4; ++L) {
     uint32_t p[4];
@@ -704,6 +703,7 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_mfma_xreg_kernel(
     sxa[L] = (__builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1])) +
              (__builtin_bit_cast(float, p[2]) + __builtin_bit_cast(float, p[3]));
   }
+  };
 
   const uint32_t magic = XF16 ? 0x64006400u : 0x43004300u;  // 1024 + q or 128 + q
   constexpr float kOff = XF16 ? 1024.f : 128.f;
@@ -776,19 +776,34 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_mfma_xreg_kernel(
     }
   };
 
-  const int rounds = items / 3, rest = items % 3;
-  int i = 0;
-  for (int r = 0; r < rounds; ++r) {
+  // With two or more row blocks every prefetch is issued, also past the last
+  // row block (those read zeros), so the compiler's waits before each item
+  // count exactly the items in flight; a prefetch that may be skipped would
+  // make it wait for every outstanding load.  With one row block the second
+  // prefetch is skipped (an extra load that only costs).
+  auto run = [&](auto all_tag) {
+    constexpr bool kAll = decltype(all_tag)::value;
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      if (i + 2 < items) ms_load<GQ, SYM>(buf[(j + 2) % 3], item_rb(i + 2), k0, n, g, N, K, G, rw, rs, rz);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(buf[j], i);
-      ++i;
+    for (int j = 0; j < 2; ++j)
+      if (kAll || j < items) ms_load<GQ, SYM>(buf[j], item_rb(j), k0, n, g, N, K, G, rw, rs, rz);
+    x_sums();
+    const int rounds = items / 3, rest = items % 3;
+    int i = 0;
+    for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        if (kAll || i + 2 < items)
+          ms_load<GQ, SYM>(buf[(j + 2) % 3], item_rb(i + 2), k0, n, g, N, K, G, rw, rs, rz);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(buf[j], i);
+        ++i;
+      }
     }
-  }
-  if (rest > 0) compute(buf[0], i++);
-  if (rest > 1) compute(buf[1], i++);
+    if (rest > 0) compute(buf[0], i++);
+    if (rest > 1) compute(buf[1], i++);
+  };
+  if (items >= 2) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 // Small-batch GEMV for long K (5 <= M <= 16, K a multiple of 256 beyond the
@@ -860,7 +875,7 @@ template <int GQ, bool SYM, int MR>
 __device__ __forceinline__ void xs_load(XsBuf<GQ, SYM, MR>& B, int rb, int k0, int n, int g, int M, int N,
                                         int K, int G, rsrc_t rx, rsrc_t rw, rsrc_t rs, rsrc_t rz) {
   const int row = rb * 16 + n;
-  const bool kin = k0 < K;
+  const bool kin = k0 < K && rb * 16 < N;  // else an item past K or past the last row block: zeros
   const bool rin = row < N && kin;
   const uint32_t wo = rin ? (uint32_t)row * (uint32_t)(K / 2) + (uint32_t)(k0 + 32 * g) / 2 : kOob;
 #pragma unroll
@@ -909,10 +924,16 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_mfma_xs_kernel(
   auto item_rb = [&](int i) { return (int)blockIdx.x + (i / IPW) * (int)gridDim.x; };
   auto item_k0 = [&](int i) { return ((i % IPW) * NW + w) * kXsItem; };
 
+  // At 8 rows every prefetch is issued, also past the last item (those read
+  // zeros), so the compiler's waits before each item count exactly the two
+  // items in flight (a prefetch that may be skipped makes it wait for every
+  // outstanding load); at 16 rows that measured slower and the loads past the
+  // end are skipped.
   XsBuf<GQ, SYM, MR> buf[3];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    if (j < items) xs_load<GQ, SYM, MR>(buf[j], item_rb(j), item_k0(j), n, g, M, N, K, G, rx, rw, rs, rz);
+    if (MR == 8 || j < items)
+      xs_load<GQ, SYM, MR>(buf[j], item_rb(j), item_k0(j), n, g, M, N, K, G, rx, rw, rs, rz);
 
   const uint32_t magic = XF16 ? 0x64006400u : 0x43004300u;  // 1024 + q or 128 + q
   constexpr float kOff = XF16 ? 1024.f : 128.f;
@@ -1017,7 +1038,7 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_mfma_xs_kernel(
   for (int rr = 0; rr < rounds; ++rr) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      if (i + 2 < items)
+      if (MR == 8 || i + 2 < items)
         xs_load<GQ, SYM, MR>(buf[(j + 2) % 3], item_rb(i + 2), item_k0(i + 2), n, g, M, N, K, G, rx, rw, rs, rz);
       __builtin_amdgcn_sched_barrier(0);
       compute(buf[j], i);
@@ -1406,15 +1427,14 @@ __global__ __launch_bounds__(NW * 64, 2) void q4k_mfma_xreg_kernel(
   uint4 xa[4][4];  // [step L][chunk c]: x[n][k0 + 128 L + 32 c + 8 g .. + 8)
   xreg_load_x(rx, M, K, k0, lane, (uint4*)(red + kXrGroup * NW * 256) + w * 512, xa);
   QkBuf buf[3];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    if (j < items) load(buf[j], item_rb(j));
   float sxa[4];
+  auto x_sums = [&]() {
 #pragma unroll
-  for (int L = 0; L < 4; ++L) {
-    const uint4 v[4] = {xa[L][0], xa[L][1], xa[L][2], xa[L][3]};
-    sxa[L] = qk_operands(v, xa[L]);
-  }
+    for (int L = 0; L < 4; ++L) {
+      const uint4 v[4] = {xa[L][0], xa[L][1], xa[L][2], xa[L][3]};
+      sxa[L] = qk_operands(v, xa[L]);
+    }
+  };
   const QkSel q = qk_sel(g);
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   f32x4_t accz = {0.f, 0.f, 0.f, 0.f};
@@ -1425,19 +1445,30 @@ __global__ __launch_bounds__(NW * 64, 2) void q4k_mfma_xreg_kernel(
     qk_step<1>(B.w[3], xa[3], sxa[3], B.h[1], q, acc, accz);
     qk_tile_done<NW, kXrGroup>(red, i, items, w, lane, M, N, acc, accz, y);
   };
-  const int rounds = items / 3, rest = items % 3;
-  int i = 0;
-  for (int r = 0; r < rounds; ++r) {
+  // every prefetch issued with two or more row blocks (exact waits), the
+  // second skipped with one, as in gemv_mfma_xreg_kernel
+  auto run = [&](auto all_tag) {
+    constexpr bool kAll = decltype(all_tag)::value;
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      if (i + 2 < items) load(buf[(j + 2) % 3], item_rb(i + 2));
-      __builtin_amdgcn_sched_barrier(0);
-      compute(buf[j], i);
-      ++i;
+    for (int j = 0; j < 2; ++j)
+      if (kAll || j < items) load(buf[j], item_rb(j));
+    x_sums();
+    const int rounds = items / 3, rest = items % 3;
+    int i = 0;
+    for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        if (kAll || i + 2 < items) load(buf[(j + 2) % 3], item_rb(i + 2));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(buf[j], i);
+        ++i;
+      }
     }
-  }
-  if (rest > 0) compute(buf[0], i++);
-  if (rest > 1) compute(buf[1], i++);
+    if (rest > 0) compute(buf[0], i++);
+    if (rest > 1) compute(buf[1], i++);
+  };
+  if (items >= 2) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 // one 256-wide item of q4k_mfma_xs_kernel: sub-block g of both steps, the
@@ -1467,7 +1498,7 @@ __global__ __launch_bounds__(NW * 64, 2) void q4k_mfma_xs_kernel(
   auto item_blk = [&](int i) { return (i % IPW) * NW + w; };
   auto load = [&](QxBuf<MR>& B, int i) {
     const int row = item_rb(i) * 16 + n, blk = item_blk(i);
-    const bool kin = blk < NI;
+    const bool kin = blk < NI && item_rb(i) * 16 < N;  // else past K or past the last row block: zeros
     const uint32_t base = row < N && kin ? (uint32_t)row * row_bytes + (uint32_t)blk * 144u : kOob;
 #pragma unroll
     for (int L = 0; L < 2; ++L) {
@@ -1479,9 +1510,10 @@ __global__ __launch_bounds__(NW * 64, 2) void q4k_mfma_xs_kernel(
     xs_load_x<MR>(rx, M, K, blk * 256, kin, lane, B.x);
   };
   QxBuf<MR> buf[3];
+  // prefetches as in gemv_mfma_xs_kernel: all issued at 8 rows (exact waits)
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    if (j < items) load(buf[j], j);
+    if (MR == 8 || j < items) load(buf[j], j);
   const QkSel q = qk_sel(g);
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   f32x4_t accz = {0.f, 0.f, 0.f, 0.f};
@@ -1499,7 +1531,7 @@ __global__ __launch_bounds__(NW * 64, 2) void q4k_mfma_xs_kernel(
   for (int r = 0; r < rounds; ++r) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      if (i + 2 < items) load(buf[(j + 2) % 3], i + 2);
+      if (MR == 8 || i + 2 < items) load(buf[(j + 2) % 3], i + 2);
       __builtin_amdgcn_sched_barrier(0);
       compute(buf[j], i);
       ++i;
