@@ -470,10 +470,14 @@ gemv_mfma_stream_kernel(
   // does not wait for the weights (loads retire in order)
   uint4 xv0[kUX];
   stage_load(0, 0, xv0);
+  // every prefetch is issued, also past the last item (row blocks >= NB read
+  // zeros), so the compiler's waits before each item count exactly the items
+  // in flight; a prefetch that may be skipped would make it wait for every
+  // outstanding load
   MsBuf<GQ, SYM> buf[3];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    if (j < items) ms_load<GQ, SYM>(buf[j], item_rb(j), item_k0(j), n, g, N, K, G, rw, rs, rz);
+    ms_load<GQ, SYM>(buf[j], item_rb(j), item_k0(j), n, g, N, K, G, rw, rs, rz);
   stage_store(0, xv0);
   stage(0, kUX * NT);
   if (SXW == MR) {
@@ -569,8 +573,7 @@ gemv_mfma_stream_kernel(
   for (int r = 0; r < rounds; ++r) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      if (i + 2 < items)
-        ms_load<GQ, SYM>(buf[(j + 2) % 3], item_rb(i + 2), item_k0(i + 2), n, g, N, K, G, rw, rs, rz);
+      ms_load<GQ, SYM>(buf[(j + 2) % 3], item_rb(i + 2), item_k0(i + 2), n, g, N, K, G, rw, rs, rz);
       __builtin_amdgcn_sched_barrier(0);
       compute(buf[j], i);
       ++i;
@@ -1167,10 +1170,10 @@ __global__ __launch_bounds__(512, 1) void q4k_mfma_stream_kernel(
 
   uint4 xv0[kUX];
   stage_load(0, 0, xv0);
-  QkBuf buf[3];
+  QkBuf buf[3];  // every prefetch issued (exact waits), as in gemv_mfma_stream_kernel
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    if (j < items) load(buf[j], item_rb(j), item_k0(j));
+    load(buf[j], item_rb(j), item_k0(j));
   stage_store(0, xv0);
   stage(0, kUX * NT);
   if (SXW == MR) {
@@ -1275,7 +1278,7 @@ __global__ __launch_bounds__(512, 1) void q4k_mfma_stream_kernel(
   for (int r = 0; r < rounds; ++r) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      if (i + 2 < items) load(buf[(j + 2) % 3], item_rb(i + 2), item_k0(i + 2));
+      load(buf[(j + 2) % 3], item_rb(i + 2), item_k0(i + 2));
       __builtin_amdgcn_sched_barrier(0);
       compute(buf[j], i);
       ++i;
