@@ -398,6 +398,25 @@ def test_many_row_block_groups(M, N, K, sym, G):
     _run(x, qw, s, z, G, sym, f"[{N},{K}] M={M} sym={sym} G={G} (two row-block groups)", rows=rows)
 
 
+@pytest.mark.parametrize("M,N,K,sym,G", [(5, 6139, 4096, True, 32), (8, 6139, 4096, False, 128),
+                                         (16, 6139, 4096, True, 32), (8, 12285, 4096, True, 32),
+                                         (16, 12285, 4096, False, 64), (8, 6139, 4352, True, 32),
+                                         (8, 12285, 4352, False, 128), (12, 6139, 4352, True, 32)])
+def test_prefetch_paths_by_row_blocks_per_workgroup(M, N, K, sym, G):
+    # 384 row blocks at K = 4096 on 256 workgroups (register-x kernel): half
+    # of them take two (every prefetch issued), half one (the second prefetch
+    # skipped); 768: three each, the loop's prefetches running past the last
+    # row block; the last row block ragged.  At K = 4352 the streamed-x
+    # kernel with one to three row blocks per workgroup, 8 rows (every
+    # prefetch issued, also past the last item) and 16 rows (guarded).  Rows
+    # at the start, around the second row block of the first workgroups, in
+    # the middle and at the end.
+    w, x = synth.small(N, K, M, seed=N + K + M)
+    qw, s, z = _oracle_weights(w, G, sym)
+    rows = np.r_[0:48, 4096 - 16:4096 + 48, N // 2:N // 2 + 32, N - 43:N]
+    _run(x, qw, s, z, G, sym, f"[{N},{K}] M={M} sym={sym} G={G} (prefetch paths)", rows=rows)
+
+
 @pytest.mark.parametrize("M", [5, 8, 16])
 @pytest.mark.parametrize("N,K,sym,G", [(203, 1536, True, 32), (203, 3072, False, 128),
                                        (77, 2560, False, 512), (9001, 3072, True, 32)])
