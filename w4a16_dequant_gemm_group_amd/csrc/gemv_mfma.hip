@@ -331,19 +331,37 @@ struct MsBuf {
   uint32_t s[kWords], z[SYM ? 1 : kWords];
 };
 
-template <int GQ, bool SYM>
+// LINES: load j brings rows 8 (j % 2) .. + 8 of the row block, 128 whole bytes
+// (a cache line of each) per row: lane (n, g) the 16 bytes at 128 (j / 2) +
+// 64 (n / 8) + 16 g of row 8 (j % 2) + n % 8, so step 2 (j / 2) + n / 8 of that
+// row; ms_rows_to_steps then swaps the pieces between lanes n and n ^ 8.
+// Otherwise load L brings step L of row n (64 bytes of each of 16 rows).
+template <int GQ, bool SYM, bool LINES = false>
 __device__ __forceinline__ void ms_load(MsBuf<GQ, SYM>& B, int rb, int k0, int n, int g, int N, int K,
                                         int G, rsrc_t rw, rsrc_t rs, rsrc_t rz) {
   const int row = rb * 16 + n;
   const bool rin = row < N && k0 < K;  // k0 >= K: an item past a partial last chunk
   const uint32_t rbytes = (uint32_t)K / 2;
-  const uint32_t wo = rin ? (uint32_t)row * rbytes + (uint32_t)(k0 + 32 * g) / 2 : kOob;
+  if constexpr (LINES) {
 #pragma unroll
-  for (int L = 0; L < 4; ++L) {
-    // the step in the lane offset (kOob + 192 is still out of range); a
-    // lane-dependent scalar offset would need a waterfall loop per load
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, wo + 64u * L, 0, 2);
-    B.w[L] = make_uint4(v[0], v[1], v[2], v[3]);
+    for (int j = 0; j < 4; ++j) {
+      const int r = rb * 16 + (n & 7) + 8 * (j & 1);
+      const uint32_t o = r < N && k0 < K
+                             ? (uint32_t)r * rbytes + (uint32_t)k0 / 2 +
+                                   (uint32_t)(128 * (j >> 1) + 64 * (n >> 3) + 16 * g)
+                             : kOob;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, o, 0, 2);
+      B.w[j] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  } else {
+    const uint32_t wo = rin ? (uint32_t)row * rbytes + (uint32_t)(k0 + 32 * g) / 2 : kOob;
+#pragma unroll
+    for (int L = 0; L < 4; ++L) {
+      // the step in the lane offset (kOob + 192 is still out of range); a
+      // lane-dependent scalar offset would need a waterfall loop per load
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, wo + 64u * L, 0, 2);
+      B.w[L] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
   }
   const uint32_t so = rin ? ((uint32_t)row * (uint32_t)(K / G) + (uint32_t)(k0 / G)) * 2u : kOob;
   auto ld = [&](rsrc_t r, uint32_t* d) {
@@ -585,6 +603,27 @@ gemv_mfma_stream_kernel(
 
 constexpr int kXrGroup = 8;  // row blocks per group (the waves meet once per group)
 
+// Lane n of a 16-lane row exchanges with lane n ^ 8 (row_ror:8).
+__device__ __forceinline__ uint32_t ror8(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint4 ror8(const uint4& v) {
+  return make_uint4(ror8(v.x), ror8(v.y), ror8(v.z), ror8(v.w));
+}
+
+// The pieces of a LINES load (ms_load) in step order: W[L] = step L of row n.
+// Lanes n < 8 hold steps 0 and 2 of row n and steps 0 and 2 of row n + 8;
+// lanes n >= 8 steps 1 and 3 of row n - 8 and of row n.
+__device__ __forceinline__ void ms_rows_to_steps(const uint4 (&w)[4], int n, uint4 (&W)[4]) {
+  const bool lo = n < 8;
+  const uint4 a = ror8(lo ? w[1] : w[0]);
+  const uint4 b = ror8(lo ? w[3] : w[2]);
+  W[0] = lo ? w[0] : a;
+  W[1] = lo ? a : w[1];
+  W[2] = lo ? w[2] : b;
+  W[3] = lo ? b : w[3];
+}
+
 // The activation operands of a register-x wave, xa[L][c] = x[n][k0 + 128 L +
 // 32 c + 8 g .. + 8) for lane (n, g) (rows >= M zero), loaded with whole-wave
 // contiguous 16-byte loads (lane l takes x[r][k0 + 8 l .. + 8) of row r: 1 KiB
@@ -723,9 +762,11 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_mfma_xreg_kernel(
   auto compute = [&](const MsBuf<GQ, SYM>& B, int i) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     f32x4_t accz = {0.f, 0.f, 0.f, 0.f};
+    uint4 W[4];
+    ms_rows_to_steps(B.w, n, W);
 #pragma unroll
     for (int L = 0; L < 4; ++L) {
-      uint32_t e0 = B.w[L].x, e1 = B.w[L].y, e2 = B.w[L].z, e3 = B.w[L].w;
+      uint32_t e0 = W[L].x, e1 = W[L].y, e2 = W[L].z, e3 = W[L].w;
       transpose4(e0, e1, e2, e3);
       const uint32_t ev[4] = {e0, e1, e2, e3};
       f32x4_t Dq[4 / CPG];
@@ -788,7 +829,7 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_mfma_xreg_kernel(
     constexpr bool kAll = decltype(all_tag)::value;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      if (kAll || j < items) ms_load<GQ, SYM>(buf[j], item_rb(j), k0, n, g, N, K, G, rw, rs, rz);
+      if (kAll || j < items) ms_load<GQ, SYM, true>(buf[j], item_rb(j), k0, n, g, N, K, G, rw, rs, rz);
     x_sums();
     const int rounds = items / 3, rest = items % 3;
     int i = 0;
@@ -796,7 +837,7 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_mfma_xreg_kernel(
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
         if (kAll || i + 2 < items)
-          ms_load<GQ, SYM>(buf[(j + 2) % 3], item_rb(i + 2), k0, n, g, N, K, G, rw, rs, rz);
+          ms_load<GQ, SYM, true>(buf[(j + 2) % 3], item_rb(i + 2), k0, n, g, N, K, G, rw, rs, rz);
         __builtin_amdgcn_sched_barrier(0);
         compute(buf[j], i);
         ++i;
