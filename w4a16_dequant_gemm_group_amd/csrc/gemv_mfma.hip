@@ -1451,14 +1451,20 @@ __global__ __launch_bounds__(NW * 64, 2) void q4k_mfma_xreg_kernel(
   const rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
   const int items = (int)blockIdx.x < NB ? (NB - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
   auto item_rb = [&](int i) { return (int)blockIdx.x + i * (int)gridDim.x; };
+  // nibbles as in ms_load's LINES form: load j brings the 128 nibble bytes of
+  // block j / 2 of rows 8 (j % 2) .. + 8 (two cache lines per row at most,
+  // against up to two per 64 bytes with a row's 4 lanes per load), the
+  // headers of row n as they are
   auto load = [&](QkBuf& B, int rbk) {
     const int row = rbk * 16 + n;
     const uint32_t base = row < N ? (uint32_t)row * row_bytes + (uint32_t)(k0 / 256) * 144u : kOob;
 #pragma unroll
-    for (int L = 0; L < 4; ++L) {
+    for (int j = 0; j < 4; ++j) {
+      const int r = rbk * 16 + (n & 7) + 8 * (j & 1);
+      const uint32_t bj = r < N ? (uint32_t)r * row_bytes + (uint32_t)(k0 / 256) * 144u : kOob;
       const auto v = __builtin_amdgcn_raw_buffer_load_b128(
-          rb, base + (uint32_t)((L >> 1) * 144 + 16 + 16 * ((L & 1) * 4 + g)), 0, 2);
-      B.w[L] = make_uint4(v[0], v[1], v[2], v[3]);
+          rb, bj + (uint32_t)((j >> 1) * 144 + 16 + 64 * (n >> 3) + 16 * g), 0, 2);
+      B.w[j] = make_uint4(v[0], v[1], v[2], v[3]);
     }
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -1483,10 +1489,12 @@ __global__ __launch_bounds__(NW * 64, 2) void q4k_mfma_xreg_kernel(
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   f32x4_t accz = {0.f, 0.f, 0.f, 0.f};
   auto compute = [&](const QkBuf& B, int i) {
-    qk_step<0>(B.w[0], xa[0], sxa[0], B.h[0], q, acc, accz);
-    qk_step<1>(B.w[1], xa[1], sxa[1], B.h[0], q, acc, accz);
-    qk_step<0>(B.w[2], xa[2], sxa[2], B.h[1], q, acc, accz);
-    qk_step<1>(B.w[3], xa[3], sxa[3], B.h[1], q, acc, accz);
+    uint4 W[4];
+    ms_rows_to_steps(B.w, n, W);
+    qk_step<0>(W[0], xa[0], sxa[0], B.h[0], q, acc, accz);
+    qk_step<1>(W[1], xa[1], sxa[1], B.h[0], q, acc, accz);
+    qk_step<0>(W[2], xa[2], sxa[2], B.h[1], q, acc, accz);
+    qk_step<1>(W[3], xa[3], sxa[3], B.h[1], q, acc, accz);
     qk_tile_done<NW, kXrGroup>(red, i, items, w, lane, M, N, acc, accz, y);
   };
   // every prefetch issued with two or more row blocks (exact waits), the
