@@ -614,6 +614,13 @@ __device__ __forceinline__ uint4 ror8(const uint4& v) {
 // The pieces of a LINES load (ms_load) in step order: W[L] = step L of row n.
 // Lanes n < 8 hold steps 0 and 2 of row n and steps 0 and 2 of row n + 8;
 // lanes n >= 8 steps 1 and 3 of row n - 8 and of row n.
+__device__ __forceinline__ void ms_rows_to_steps2(const uint4 (&w)[2], int n, uint4 (&W)[2]) {
+  // the same for two steps: load j brings rows 8 j .. + 8, step n / 8
+  const bool lo = n < 8;
+  const uint4 a = ror8(lo ? w[1] : w[0]);
+  W[0] = lo ? w[0] : a;
+  W[1] = lo ? a : w[1];
+}
 __device__ __forceinline__ void ms_rows_to_steps(const uint4 (&w)[4], int n, uint4 (&W)[4]) {
   const bool lo = n < 8;
   const uint4 a = ror8(lo ? w[1] : w[0]);
@@ -921,11 +928,17 @@ __device__ __forceinline__ void xs_load(XsBuf<GQ, SYM, MR>& B, int rb, int k0, i
   const int row = rb * 16 + n;
   const bool kin = k0 < K && rb * 16 < N;  // else an item past K or past the last row block: zeros
   const bool rin = row < N && kin;
-  const uint32_t wo = rin ? (uint32_t)row * (uint32_t)(K / 2) + (uint32_t)(k0 + 32 * g) / 2 : kOob;
+  // load j: the item's 128 bytes of rows 8 j .. + 8 (whole lines; lane (n, g)
+  // the 16 bytes at 64 (n / 8) + 16 g, step n / 8), reordered by
+  // ms_rows_to_steps2
 #pragma unroll
-  for (int L = 0; L < 2; ++L) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, wo + 64u * L, 0, 2);
-    B.w[L] = make_uint4(v[0], v[1], v[2], v[3]);
+  for (int j = 0; j < 2; ++j) {
+    const int r = rb * 16 + (n & 7) + 8 * j;
+    const uint32_t o = r < N && kin ? (uint32_t)r * (uint32_t)(K / 2) + (uint32_t)k0 / 2 +
+                                          (uint32_t)(64 * (n >> 3) + 16 * g)
+                                    : kOob;
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, o, 0, 2);
+    B.w[j] = make_uint4(v[0], v[1], v[2], v[3]);
   }
   xs_load_x<MR>(rx, M, K, k0, kin, (int)(threadIdx.x & 63), B.x);
   const uint32_t so = rin ? ((uint32_t)row * (uint32_t)(K / G) + (uint32_t)(k0 / G)) * 2u : kOob;
@@ -1003,8 +1016,9 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_mfma_xs_kernel(
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   f32x4_t accz = {0.f, 0.f, 0.f, 0.f};
   auto compute = [&](const XsBuf<GQ, SYM, MR>& B, int i) {
-    uint4 X[8];
+    uint4 X[8], W[2];
     xs_operands<MR>(B.x, lane, xlds[w], X);
+    ms_rows_to_steps2(B.w, n, W);
 #pragma unroll
     for (int L = 0; L < 2; ++L) {
       // the step's activation operands and chunk sums (row n, chunk g)
@@ -1023,7 +1037,7 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_mfma_xs_kernel(
       transpose4(p[0], p[1], p[2], p[3]);
       const float sx = (__builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1])) +
                        (__builtin_bit_cast(float, p[2]) + __builtin_bit_cast(float, p[3]));
-      uint32_t e0 = B.w[L].x, e1 = B.w[L].y, e2 = B.w[L].z, e3 = B.w[L].w;
+      uint32_t e0 = W[L].x, e1 = W[L].y, e2 = W[L].z, e3 = W[L].w;
       transpose4(e0, e1, e2, e3);
       const uint32_t ev[4] = {e0, e1, e2, e3};
       f32x4_t Dq[4 / CPG];
@@ -1552,10 +1566,14 @@ __global__ __launch_bounds__(NW * 64, 2) void q4k_mfma_xs_kernel(
     const int row = item_rb(i) * 16 + n, blk = item_blk(i);
     const bool kin = blk < NI && item_rb(i) * 16 < N;  // else past K or past the last row block: zeros
     const uint32_t base = row < N && kin ? (uint32_t)row * row_bytes + (uint32_t)blk * 144u : kOob;
+    // load j: the block's 128 nibble bytes of rows 8 j .. + 8 (ms_rows_to_steps2)
 #pragma unroll
-    for (int L = 0; L < 2; ++L) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rb, base + (uint32_t)(16 + 16 * (L * 4 + g)), 0, 2);
-      B.w[L] = make_uint4(v[0], v[1], v[2], v[3]);
+    for (int j = 0; j < 2; ++j) {
+      const int r = item_rb(i) * 16 + (n & 7) + 8 * j;
+      const uint32_t bj = r < N && kin ? (uint32_t)r * row_bytes + (uint32_t)blk * 144u : kOob;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+          rb, bj + (uint32_t)(16 + 64 * (n >> 3) + 16 * g), 0, 2);
+      B.w[j] = make_uint4(v[0], v[1], v[2], v[3]);
     }
     const auto hv = __builtin_amdgcn_raw_buffer_load_b128(rb, base, 0, 0);
     B.h = make_uint4(hv[0], hv[1], hv[2], hv[3]);
@@ -1570,12 +1588,13 @@ __global__ __launch_bounds__(NW * 64, 2) void q4k_mfma_xs_kernel(
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   f32x4_t accz = {0.f, 0.f, 0.f, 0.f};
   auto compute = [&](const QxBuf<MR>& B, int i) {
-    uint4 X[8], A[4];
+    uint4 X[8], A[4], W[2];
     xs_operands<MR>(B.x, lane, xlds[w], X);
+    ms_rows_to_steps2(B.w, n, W);
     float sx = qk_operands(&X[0], A);
-    qk_step<0>(B.w[0], A, sx, B.h, q, acc, accz);
+    qk_step<0>(W[0], A, sx, B.h, q, acc, accz);
     sx = qk_operands(&X[4], A);
-    qk_step<1>(B.w[1], A, sx, B.h, q, acc, accz);
+    qk_step<1>(W[1], A, sx, B.h, q, acc, accz);
     if (i % IPW == IPW - 1) qk_tile_done<NW, kXsGroup>(red, i / IPW, nrb, w, lane, M, N, acc, accz, y);
   };
   const int rounds = items / 3, rest = items % 3;
